@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for the scaled-dot-product-attention forward.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import this package; the product path never does.  It shares no code with
+the HIP library and does not import it.
+
+The arithmetic lives in oracle.c (plain fp64 loops, one output row at a time); this module
+only marshals torch CPU tensors (or numpy arrays) into pointers and strides.
+
+What is computed, per "Profiling in PyTorch (part 3): attention" (naive causal attention
+section: the five primitive steps and the default scale 1/sqrt(head_dim); SDPA math
+backend section: the safe softmax that keeps fully masked rows free of NaN):
+
+    out[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:].k[b,h,j,:] over visible j) v[b,h,j,:]
+    lse[b,h,i]   = log sum_{visible j} exp(scale * q.k)         (natural log)
+
+with visible j = (not causal or j <= i) and (no mask or mask[b,h,i,j] != 0); a row with
+no visible key returns zeros and lse = -inf.  A rank-3 [N,L,D] input is read as the
+rank-4 input [1,N,L,D], following the PyTorch 2.14 note on rank-3 SDPA inputs (a folded
+or missing batch dimension is the same computation).
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# ORACLE_LIB points the wrapper at another build of oracle.c (the mutation test uses it to
+# check that the pins reject deliberately broken copies).
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float64: 2}
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_sdpa_fwd.restype = ctypes.c_int
+        lib.oracle_sdpa_fwd.argtypes = [
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64,
+            ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
+            ctypes.c_void_p, i64p,
+            ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64, dp, dp, ctypes.c_int]
+        lib.oracle_default_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    """OpenMP threads the oracle uses when nthreads <= 0."""
+    return int(_load().oracle_default_threads())
+
+
+def _as_tensor(x):
+    if isinstance(x, np.ndarray):
+        return torch.from_numpy(x)
+    return x
+
+
+def _strides4(t):
+    """(b, h, row, d) element strides of a rank-3 or rank-4 tensor (rank 3 -> B = 1)."""
+    s = t.stride()
+    return (0,) + tuple(s) if t.dim() == 3 else tuple(s)
+
+
+def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, nthreads=0):
+    """Evaluate the plain definition in fp64.
+
+    q: [N,Lq,D] or [B,H,Lq,D]; k, v: same rank with Lk rows; CPU tensors (or numpy) of one
+    dtype among float32 / bfloat16 / float64, any strides.  mask: optional bool or uint8
+    tensor broadcastable to [B,H,Lq,Lk] (rank 4) or [N,Lq,Lk] (rank 3); nonzero = visible.
+    rows: optional int64 flat row ids (b*H + h)*Lq + i.
+
+    Returns (out, lse) as float64 numpy arrays: shaped like q and q.shape[:-1] when rows is
+    None, else [len(rows), D] and [len(rows)].
+    """
+    q, k, v = _as_tensor(q), _as_tensor(k), _as_tensor(v)
+    for t in (q, k, v):
+        if t.device.type != "cpu":
+            raise ValueError("the oracle reads host memory; move tensors to the CPU first")
+    if not (q.dim() == k.dim() == v.dim() and q.dim() in (3, 4)):
+        raise ValueError("q, k, v must all be rank 3 or all rank 4")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float64")
+    rank = q.dim()
+    if rank == 3:
+        B, H, Lq, D = 1, q.shape[0], q.shape[1], q.shape[2]
+        Lk = k.shape[1]
+    else:
+        B, H, Lq, D = q.shape
+        Lk = k.shape[2]
+    if tuple(k.shape) != tuple(q.shape[:-2]) + (Lk, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must have q's leading dims, the same length Lk and head dim")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+
+    mptr, ms_arr, mask_t = None, None, None
+    if mask is not None:
+        mask_t = _as_tensor(mask)
+        full = tuple(q.shape[:-1]) + (Lk,)
+        mask_t = mask_t.expand(full)
+        if mask_t.dtype == torch.bool:
+            mask_t = mask_t.view(torch.uint8)
+        if mask_t.dtype != torch.uint8:
+            raise ValueError("mask must be bool or uint8")
+        ms = _strides4(mask_t)
+        ms_arr = (ctypes.c_int64 * 4)(*ms)
+        mptr = ctypes.c_void_p(mask_t.data_ptr())
+
+    if rows is None:
+        n = B * H * Lq
+        rows_arr, rows_ptr = None, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows_arr.shape[0]
+        rows_ptr = rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+    out = np.zeros((n, D), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    qs = (ctypes.c_int64 * 4)(*_strides4(q))
+    ks = (ctypes.c_int64 * 4)(*_strides4(k))
+    vs = (ctypes.c_int64 * 4)(*_strides4(v))
+    lib = _load()
+    st = lib.oracle_sdpa_fwd(
+        _DTYPE_CODE[q.dtype], B, H, Lq, Lk, D,
+        ctypes.c_void_p(q.data_ptr()), qs, ctypes.c_void_p(k.data_ptr()), ks,
+        ctypes.c_void_p(v.data_ptr()), vs, mptr, ms_arr,
+        1 if is_causal else 0, float(scale), rows_ptr, n,
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))
+    if st != 0:
+        raise RuntimeError(f"oracle_sdpa_fwd failed with status {st}")
+    if rows is None:
+        out = out.reshape(tuple(q.shape))
+        lse = lse.reshape(tuple(q.shape[:-1]))
+    return out, lse

@@ -1,0 +1,180 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU definition of scaled-dot-product attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file; only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+ * do.  It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (one row at a time, no tiling, no online softmax):
+ *   "Profiling in PyTorch (part 3): attention" -- the naive causal attention section lists
+ *   the five steps  scores = q.k^T ; scores *= scale ; masked positions -> -inf ;
+ *   attn = softmax(scores, dim=-1) ; out = attn.v  and fixes the default scale to
+ *   1/sqrt(head_dim).  The SDPA math-backend section of the same article adds the
+ *   `_safe_softmax` rule: a row whose every position is masked must not produce NaN;
+ *   this oracle returns a zero row for it and an LSE of -inf.
+ *   The log-sum-exp of each row (natural log, in the scaled-score domain) is returned
+ *   next to the output, as the FlashInfer DSA article's fused forward returns `lse`.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - mask polarity: a nonzero mask byte means "this key may be attended"; zero masks it.
+ *   - causal alignment: top-left, key j is allowed for query i iff j <= i.
+ *   - causal together with a mask: a key must pass both.
+ *   - rank-3 [N,L,D] input is the rank-4 input with B=1, H=N (handled by the caller
+ *     through strides; this file only sees (b,h,i,d) strides).
+ *
+ * Precision: every input element is decoded exactly to double (bf16 by a 16-bit shift
+ * into the high half of an IEEE single, fp32 by conversion), all arithmetic is double,
+ * dot products sum over d in ascending order, the softmax is the textbook two-pass form
+ * (max, then exp and sum), and the probabilities are normalised before the product
+ * with V, exactly in the order the five steps give.
+ *
+ * Parity pins: see tests/test_oracle_*.py (brute force, closed forms, invariants,
+ * hand-derived golden cases, the library's fp64 math-backend SDPA).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+
+/* Exact decode of one element of a q/k/v tensor to double. */
+static double load_elem(const void* base, int dtype, int64_t off) {
+  if (dtype == ORACLE_F64) return ((const double*)base)[off];
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[off];
+  /* bf16: the 16 stored bits are the high half of an IEEE-754 binary32. */
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[off] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Is key j visible to query i of head (b,h)? (causal triangle and/or boolean mask) */
+static int allowed(int is_causal, const uint8_t* mask, const int64_t* ms, int64_t b,
+                   int64_t h, int64_t i, int64_t j) {
+  if (is_causal && j > i) return 0;
+  if (mask && mask[b * ms[0] + h * ms[1] + i * ms[2] + j * ms[3]] == 0) return 0;
+  return 1;
+}
+
+/*
+ * One output row: query i of head (b,h).  `s` and `p` are scratch of length Lk.
+ * Writes D doubles to out_row and one double to *lse_out.
+ */
+static void one_row(int dtype, int64_t Lk, int64_t D, const void* q, const int64_t* qs,
+                    const void* k, const int64_t* ks, const void* v, const int64_t* vs,
+                    const uint8_t* mask, const int64_t* ms, int is_causal, double scale,
+                    int64_t b, int64_t h, int64_t i, double* s, double* p, double* out_row,
+                    double* lse_out) {
+  const int64_t qrow = b * qs[0] + h * qs[1] + i * qs[2];
+  int any = 0;
+  double m = -INFINITY;
+  /* steps 1-3: scores of the visible keys, scaled after the dot product */
+  for (int64_t j = 0; j < Lk; ++j) {
+    if (!allowed(is_causal, mask, ms, b, h, i, j)) {
+      s[j] = -INFINITY;
+      continue;
+    }
+    const int64_t krow = b * ks[0] + h * ks[1] + j * ks[2];
+    double dot = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+      dot += load_elem(q, dtype, qrow + d * qs[3]) * load_elem(k, dtype, krow + d * ks[3]);
+    s[j] = scale * dot;
+    if (!any || s[j] > m) m = s[j];
+    any = 1;
+  }
+  if (!any) { /* every key masked: the safe softmax yields an all-zero row */
+    for (int64_t d = 0; d < D; ++d) out_row[d] = 0.0;
+    *lse_out = -INFINITY;
+    return;
+  }
+  /* step 4: softmax over the visible keys, two passes (max above, exp+sum here) */
+  double l = 0.0;
+  for (int64_t j = 0; j < Lk; ++j) {
+    p[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
+    l += p[j];
+  }
+  for (int64_t j = 0; j < Lk; ++j) p[j] /= l;
+  /* step 5: out = attn . v */
+  for (int64_t d = 0; d < D; ++d) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < Lk; ++j)
+      acc += p[j] * load_elem(v, dtype, b * vs[0] + h * vs[1] + j * vs[2] + d * vs[3]);
+    out_row[d] = acc;
+  }
+  *lse_out = m + log(l);
+}
+
+/*
+ * oracle_sdpa_fwd -- the whole forward, or a chosen subset of its rows.
+ *
+ *   dtype        ORACLE_F32 / ORACLE_BF16 (raw 16-bit patterns) / ORACLE_F64, shared by q,k,v
+ *   B,H,Lq,Lk,D  sizes; q is [B,H,Lq,D], k and v are [B,H,Lk,D] through the strides below
+ *   qs,ks,vs     four element strides each, in (b, h, row, d) order; any value allowed
+ *   mask, ms     optional byte mask addressed as mask[b*ms0 + h*ms1 + i*ms2 + j*ms3]
+ *                (0 = masked); strides may be 0 to broadcast; NULL = no mask
+ *   is_causal    nonzero: also hide keys j > i
+ *   scale        multiplies q.k after the dot product
+ *   rows, nrows  flat row ids r = (b*H + h)*Lq + i to evaluate; rows == NULL evaluates
+ *                all B*H*Lq rows in that order (then nrows is ignored)
+ *   out          [n, D] doubles, row-major, one row per evaluated row
+ *   lse          [n] doubles (natural log), -inf for rows with no visible key
+ *   nthreads     OpenMP threads (<= 0: the runtime's default)
+ *
+ * Returns 0 on success, 1 on a bad argument, 2 if scratch memory could not be allocated.
+ */
+int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                    const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                    const void* v, const int64_t* vs, const uint8_t* mask, const int64_t* ms,
+                    int is_causal, double scale, const int64_t* rows, int64_t nrows,
+                    double* out, double* lse, int nthreads) {
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return 1;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || D < 0) return 1;
+  if (!out || !lse || !qs || !ks || !vs || (mask && !ms)) return 1;
+  const int64_t n = rows ? nrows : B * H * Lq;
+  if (n < 0) return 1;
+  if (rows) {
+    for (int64_t r = 0; r < n; ++r)
+      if (rows[r] < 0 || rows[r] >= B * H * Lq) return 1;
+  }
+  int status = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
+    if (!s || !p) {
+#pragma omp atomic write
+      status = 2;
+    }
+    /* every thread reaches the work-sharing loop; one without scratch only reports */
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t r = 0; r < n; ++r) {
+      if (!s || !p) continue;
+      const int64_t flat = rows ? rows[r] : r;
+      const int64_t i = flat % Lq;
+      const int64_t bh = flat / Lq;
+      one_row(dtype, Lk, D, q, qs, k, ks, v, vs, mask, ms, is_causal, scale, bh / H, bh % H, i,
+              s, p, out + r * D, lse + r);
+    }
+    free(s);
+    free(p);
+  }
+  return status;
+}
+
+/* Threads the OpenMP runtime would use by default (reported next to CPU timings). */
+int oracle_default_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
