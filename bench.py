@@ -1,0 +1,222 @@
+"""Benchmark of the fused SDPA forward on one MI355X.
+
+One step = one call of the fused forward (one kernel) over the long-sequence causal
+workload: q, k, v bf16 [B=1, H=32, L=8192, D=128], entries N(0,1)*0.5, each a [B,L,H,D]
+buffer viewed as [B,H,L,D] (non-contiguous), scale 1/sqrt(128), causal.  Inputs are
+resident in HBM before the timed region.
+
+Throughput is causal-adjusted: the algorithmic work of one step is 4*D flops per visible
+(query, key) pair (2*D for q.k, 2*D for p.v), i.e. 2*B*H*D*L*(L+1) flops for a causal
+square problem; work the kernel spends on the masked half of diagonal tiles is not
+credited.  The roofline peak is MI355X's dense bf16 matrix-core rate,
+256 CU x 2.4 GHz x 4096 flop/clk = 2516.6 TFLOP/s.
+
+Prints one JSON line.  `--report PATH` also writes per-workload timings (all five
+configurations, rank-3 vs rank-4) to PATH.
+"""
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # 2516.58
+PEAK_F32_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+METRIC = "causal SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
+# FETCH_SIZE + WRITE_SIZE of the fused kernel on the default workload, from two
+# rocprofv3 --pmc passes, each scaled by the same counter on a plain copy of known size;
+# bytes per launch.  None until measured for the kernel as it is now.
+TRAFFIC_BYTES = None
+
+
+def visible_pairs(Lq, Lk, causal):
+    """(query, key) pairs of one head inside the causal triangle (all pairs otherwise)."""
+    if not causal:
+        return Lq * Lk
+    full = min(Lq, Lk)
+    return full * (full + 1) // 2 + max(0, Lq - Lk) * Lk
+
+
+def step_flops(wl):
+    """Algorithmic flops of one forward: 4*D per (query, key) pair the method evaluates.
+    A causal problem evaluates only the triangle; a boolean mask is applied to the full
+    score matrix, so a masked problem is counted dense."""
+    B, H, Lq, Lk, D = wl.shape4()
+    return 4 * D * B * H * visible_pairs(Lq, Lk, wl.is_causal)
+
+
+def time_kernel(fn, steps, warmup):
+    """Warm up, then time `steps` calls: wall clock around all of them (synchronised on
+    both sides) and HIP events around each launch on the stream the kernel runs on."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in ev]  # ms
+    return wall, per
+
+
+def cpu_baseline(wl, target_s=12.0, seed=0):
+    """The fp64 oracle on a bounded sample of rows of the same workload, on the host
+    cores; flops of the sampled rows / time, in TFLOP/s."""
+    import numpy as np
+    import oracle
+    B, H, Lq, Lk, D = wl.shape4()
+    rng = np.random.default_rng(seed)
+
+    def row_flops(rows):
+        i = rows % Lq
+        vis = np.minimum(i + 1, Lk) if wl.is_causal else np.full_like(i, Lk)
+        return int(4 * D * vis.sum())
+
+    def run(n):
+        rows = np.sort(rng.choice(B * H * Lq, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.sdpa_oracle(wl.q, wl.k, wl.v, mask=wl.mask, is_causal=wl.is_causal,
+                           scale=wl.scale, rows=rows)
+        return time.perf_counter() - t0, row_flops(rows), n
+
+    dt, fl, n = run(256)  # calibration
+    n2 = int(min(B * H * Lq, max(256, 256 * target_s / max(dt, 1e-3))))
+    dt, fl, n = run(n2)
+    threads = oracle.default_threads()
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows drawn uniformly from the {B * H * Lq} rows of the same "
+                      f"workload, fp64 oracle, {dt:.2f} s for {fl / 1e9:.2f} GFLOP of visible "
+                      f"pairs, {threads} OpenMP threads, host cpu: {cpu_model()}"}
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def to_device(wl, dev):
+    import torch
+
+    def mv(t):
+        if t is None:
+            return None
+        d = t.to(dev)
+        assert d.stride() == t.stride(), "device copy must keep the layout"
+        return d
+    return mv(wl.q), mv(wl.k), mv(wl.v), mv(wl.mask)
+
+
+def bench_workload(wl, steps, warmup):
+    import torch
+    from scaled_dot_product_11_amd import sdpa_fwd
+    q, k, v, m = to_device(wl, "cuda")
+    out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+
+    def fn():
+        sdpa_fwd(q, k, v, out, lse, mask=m, is_causal=wl.is_causal, scale=wl.scale)
+    wall, per = time_kernel(fn, steps, warmup)
+    flops = step_flops(wl)
+    return {"workload": wl.name, "flops": flops, "wall_s": wall, "steps": steps,
+            "kernel_ms_mean": statistics.fmean(per), "kernel_ms_median": statistics.median(per),
+            "kernel_ms_min": min(per), "kernel_ms_max": max(per),
+            "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--report", default=None, help="write per-workload timings here")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "no GPU visible"
+    props = torch.cuda.get_device_properties(0)
+
+    wl = W.config4()
+    r = bench_workload(wl, args.steps, args.warmup)
+    ms_per_step = r["wall_s"] / args.steps * 1e3
+    value = r["flops"] / (ms_per_step * 1e-3) / 1e12
+    achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "shape_bhld": [1, 32, 8192, 128],
+                   "layout": "[B,L,H,D] buffers viewed as [B,H,L,D]", "is_causal": True,
+                   "scale": wl.scale, "flops_per_step": r["flops"],
+                   "flop_convention": "4*D per visible (i,j) pair, causal-adjusted",
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "device": props.name, "cus": props.multi_processor_count},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": TRAFFIC_BYTES,
+                     "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
+                     "kernel_ms_median": round(r["kernel_ms_median"], 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    if args.report:
+        rows = [r]
+        for name, fn in (("c1", W.config1), ("c2", W.config2), ("c5", W.config5)):
+            rows.append(bench_workload(fn(), args.steps, args.warmup))
+        for rank in (3, 4):
+            rows.append(bench_workload(W.config3(rank=rank), args.steps, args.warmup))
+        with open(args.report, "w") as f:
+            json.dump({"peak_bf16_tflops": PEAK_BF16_TFLOPS, "device": props.name,
+                       "results": rows}, f, indent=1)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

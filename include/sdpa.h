@@ -1,0 +1,145 @@
+/*
+ * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product-attention forward.
+ *
+ * The operation ("Profiling in PyTorch (part 3): attention", naive causal attention
+ * section, five steps; SDPA section, the one-call form that takes a mask or a causal
+ * flag; math-backend section, the safe softmax):
+ *
+ *   out[b,h,i,:] = sum_j P[i,j] v[b,h,j,:],   P[i,:] = softmax over the visible keys j of
+ *                                                      scale * q[b,h,i,:].k[b,h,j,:]
+ *   lse[b,h,i]   = log sum_{visible j} exp(scale * q[b,h,i,:].k[b,h,j,:])   (natural log)
+ *
+ *   key j is visible to query i iff (!is_causal || j <= i) && (mask == NULL || mask[b,h,i,j] != 0)
+ *
+ * A query row with no visible key returns an all-zero output row and lse = -inf (the safe
+ * softmax of the math-backend section; no NaN is ever produced for finite inputs).  The
+ * causal triangle is aligned top-left (j <= i) also when Lq != Lk.
+ *
+ * Rank-3 and rank-4 inputs take the same fused kernel (the PyTorch 2.14 note on rank-3
+ * SDPA inputs): a rank-3 [N,L,D] input is computed exactly as the rank-4 input
+ * [1,N,L,D], bit for bit.
+ *
+ * The library launches exactly one kernel per sdpa_fwd call on the caller's stream,
+ * allocates nothing, frees nothing, never synchronises, and keeps no per-call state (the
+ * only global is a per-device cache of the architecture check).  Calls are thread-safe.
+ */
+#ifndef SDPA_MI355X_H_
+#define SDPA_MI355X_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v and out (all four share one). */
+enum sdpa_dtype {
+  SDPA_F32 = 0,  /* IEEE binary32; products and sums in fp32 (matrix cores, fp32 MFMA)   */
+  SDPA_BF16 = 1  /* bfloat16; bf16 products on matrix cores with fp32 accumulation, the
+                    softmax in fp32, probabilities rounded to bf16 (nearest-even) before
+                    the product with V                                                    */
+};
+
+/* Status codes.  On any nonzero status nothing was launched and nothing was written. */
+enum sdpa_status {
+  SDPA_OK = 0,
+  SDPA_ERR_NULL = 1,     /* a required pointer is NULL (strides, or q/k/v/out when read) */
+  SDPA_ERR_RANK = 2,     /* rank not 3 or 4, or rank 3 with B != 1                       */
+  SDPA_ERR_SHAPE = 3,    /* negative size, or a size/grid beyond the supported maximum   */
+  SDPA_ERR_HEAD_DIM = 4, /* D not in {64, 128}                                           */
+  SDPA_ERR_DTYPE = 5,    /* dtype not an sdpa_dtype                                      */
+  SDPA_ERR_STRIDE = 6,   /* innermost stride != 1, or a negative stride                  */
+  SDPA_ERR_ALIGN = 7,    /* q/k/v/out base or row stride not 16-byte aligned, lse not 4  */
+  SDPA_ERR_SCALE = 8,    /* scale is NaN or infinite                                     */
+  SDPA_ERR_DEVICE = 9    /* the stream's device is not gfx950, or the launch failed      */
+};
+
+/*
+ * sdpa_fwd -- fused SDPA forward with per-row LSE, one kernel on `stream`.
+ *
+ *   q, k, v, out  device pointers to elements of `dtype`.  q and out are [B,H,Lq,D]
+ *                 (rank 4) or [N,Lq,D] (rank 3); k and v are [B,H,Lk,D] / [N,Lk,D].
+ *                 Any layout whose innermost (D) stride is 1 is accepted, e.g. a
+ *                 [B,L,H,D] buffer viewed as [B,H,L,D]: there is no transpose or copy.
+ *                 Base pointers and every non-innermost stride (in bytes) must be
+ *                 multiples of 16.  out must not overlap q, k or v, nor itself.
+ *                 k and v may be NULL when Lk == 0; q and out may be NULL when
+ *                 B*H*Lq == 0.
+ *   lse           NULL, or a device pointer to B*H*Lq contiguous floats ([B,H,Lq] /
+ *                 [N,Lq]), 4-byte aligned, receiving the natural-log LSE (-inf for
+ *                 rows with no visible key).
+ *   rank          3 or 4.  Rank 3 requires B == 1 and H == N.
+ *   B,H,Lq,Lk,D   sizes; D in {64, 128}; Lq, Lk and B*H below 2^31.  B*H*Lq == 0 is a
+ *                 no-op returning SDPA_OK; Lk == 0 makes every row empty.
+ *   strides       5*rank element strides, tensor-major: q, k, v, out, mask, each in its
+ *                 own axis order ([N,L,D] / [B,H,L,D]; the mask is [N,Lq,Lk] /
+ *                 [B,H,Lq,Lk]).  The mask's entries are ignored when mask == NULL.
+ *                 Mask strides may be 0 (broadcast, e.g. one mask for all heads); the
+ *                 mask's innermost (key) stride must be 1.
+ *   scale         finite multiplier of q.k applied after the dot product (the usual
+ *                 choice is 1/sqrt(D); any finite value, including 0 or negative, is
+ *                 accepted).
+ *   is_causal     nonzero: hide keys j > i (top-left triangle); combines with a mask
+ *                 by intersection.
+ *   mask          NULL, or a device pointer to bytes, nonzero = visible, 0 = hidden.
+ *   dtype         an sdpa_dtype.
+ *   stream        a hipStream_t (NULL = the null stream of the current device).
+ *
+ * Ownership: every pointer is owned by the caller and must stay valid until the work on
+ * `stream` has completed.  Errors: validation runs on the host before any launch; a
+ * failed launch returns SDPA_ERR_DEVICE; faults during execution surface at the
+ * caller's next synchronisation.
+ */
+int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int rank,
+             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides,
+             float scale, int is_causal, const uint8_t* mask, int dtype, void* stream);
+
+/*
+ * sdpa_check -- the host-side validation of sdpa_fwd alone (same arguments, no stream).
+ * Makes no HIP call and reads no device memory (pointers are only tested for NULL and
+ * alignment), so it runs on a machine without a GPU.  Returns the status sdpa_fwd would
+ * return before launching.
+ */
+int sdpa_check(const void* q, const void* k, const void* v, const void* out, const float* lse,
+               int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+               const int64_t* strides, float scale, int is_causal, const uint8_t* mask,
+               int dtype);
+
+/* sdpa_strerror -- a static, human-readable message for a status code. */
+const char* sdpa_strerror(int status);
+
+/*
+ * Launch plan (host-only introspection of the tile scheduler).
+ *
+ * A work item is one (b*H + h, query tile) pair: block_m query rows of one head, which
+ * walk the key/value tiles of block_n keys.  With is_causal the items are issued
+ * heaviest-first (last query tile of every head first), so the long items start early
+ * and the short ones fill the tail.  Without it the items are issued query-tile-major
+ * with heads innermost, so the heads that share a broadcast mask tile run back to back.
+ */
+typedef struct sdpa_plan {
+  int64_t block_m;      /* query rows per work item                                    */
+  int64_t block_n;      /* keys per inner step                                         */
+  int64_t threads;      /* threads per workgroup (wave64)                              */
+  int64_t q_tiles;      /* ceil(Lq / block_m)                                          */
+  int64_t bh;           /* B*H                                                         */
+  int64_t items;        /* bh * q_tiles = workgroups launched                          */
+  int64_t lds_bytes;    /* LDS per workgroup                                           */
+  int64_t is_causal;    /* issue order: 1 heaviest-first, 0 tile-major                 */
+} sdpa_plan_t;
+
+/* Fill `plan` for a problem that sdpa_check accepts (pointers are not needed). Returns
+ * SDPA_ERR_NULL for plan == NULL, or the validation status of the sizes and dtype. */
+int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+              int is_causal, int dtype, sdpa_plan_t* plan);
+
+/* The work item that workgroup `block` (0 <= block < plan->items) runs: its flat head
+ * index b*H + h and its query tile.  This is the decode the kernel performs on the GPU.
+ * Returns SDPA_ERR_SHAPE for a block out of range. */
+int sdpa_plan_item(const sdpa_plan_t* plan, int64_t block, int64_t* bh, int64_t* q_tile);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H_ */

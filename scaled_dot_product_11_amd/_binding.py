@@ -1,0 +1,187 @@
+"""ctypes binding of the gfx950 SDPA library: argument marshalling only.
+
+Every step of the forward runs in the HIP library; PyTorch provides device memory and the
+current stream.  There is no fallback of any kind: if the library is missing, or the
+tensors are not on a GPU, the call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch  # must precede loading the library: it binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdpa_gfx950.so")
+
+SDPA_F32, SDPA_BF16 = 0, 1
+_DTYPES = {torch.float32: SDPA_F32, torch.bfloat16: SDPA_BF16}
+
+STATUS_NAMES = {
+    0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_RANK", 3: "SDPA_ERR_SHAPE",
+    4: "SDPA_ERR_HEAD_DIM", 5: "SDPA_ERR_DTYPE", 6: "SDPA_ERR_STRIDE", 7: "SDPA_ERR_ALIGN",
+    8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE",
+}
+
+EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
+
+
+class SdpaError(RuntimeError):
+    """A nonzero status from the library (status code in .status)."""
+
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class SdpaPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("block_m", "block_n", "threads", "q_tiles", "bh", "items", "lds_bytes",
+                 "is_causal")]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libsdpa_gfx950.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m scaled_dot_product_11_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    common = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
+              ctypes.POINTER(i64), ctypes.c_float, ctypes.c_int, vp, ctypes.c_int]
+    lib.sdpa_fwd.argtypes = common + [vp]
+    lib.sdpa_fwd.restype = ctypes.c_int
+    lib.sdpa_check.argtypes = common
+    lib.sdpa_check.restype = ctypes.c_int
+    lib.sdpa_strerror.argtypes = [ctypes.c_int]
+    lib.sdpa_strerror.restype = ctypes.c_char_p
+    lib.sdpa_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                              ctypes.POINTER(SdpaPlan)]
+    lib.sdpa_plan.restype = ctypes.c_int
+    lib.sdpa_plan_item.argtypes = [ctypes.POINTER(SdpaPlan), i64, ctypes.POINTER(i64),
+                                   ctypes.POINTER(i64)]
+    lib.sdpa_plan_item.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def sdpa_strerror(status: int) -> str:
+    return load_library().sdpa_strerror(int(status)).decode()
+
+
+def _raise_on(status):
+    if status != 0:
+        raise SdpaError(status, sdpa_strerror(status))
+
+
+def _sizes(q, k):
+    if q.dim() == 3:
+        return 1, q.shape[0], q.shape[1], k.shape[1], q.shape[2]
+    if q.dim() == 4:
+        return q.shape[0], q.shape[1], q.shape[2], k.shape[2], q.shape[3]
+    return 0, 0, 0, 0, q.shape[-1] if q.dim() else 0
+
+
+def _marshal(q, k, v, out, lse, mask, scale, is_causal):
+    rank = q.dim()
+    B, H, Lq, Lk, D = _sizes(q, k)
+    dtype = _DTYPES.get(q.dtype, -1)
+    strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride()]
+    mask_ptr, mask_keep = None, None
+    if mask is not None:
+        m = mask.expand(*q.shape[:-1], Lk)
+        if m.dtype == torch.bool:
+            m = m.view(torch.uint8)
+        if m.dtype != torch.uint8:
+            raise TypeError("mask must be a bool or uint8 tensor")
+        strides += list(m.stride())
+        mask_ptr, mask_keep = m.data_ptr(), m
+    else:
+        strides += [0] * rank
+    arr = (ctypes.c_int64 * len(strides))(*strides)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr,
+            float(scale), 1 if is_causal else 0, mask_ptr, dtype]
+    return args, mask_keep
+
+
+def _check_shapes(q, k, v, out, lse, mask):
+    if not (q.dim() == k.dim() == v.dim()):
+        raise ValueError("q, k and v must have the same rank")
+    if q.dim() in (3, 4):
+        if tuple(k.shape) != tuple(v.shape):
+            raise ValueError("k and v must have the same shape")
+        if tuple(k.shape[:-2]) != tuple(q.shape[:-2]) or k.shape[-1] != q.shape[-1]:
+            raise ValueError("k must match q in the leading dims and the head dim")
+        if out is not None and tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have q's shape")
+        if lse is not None and (tuple(lse.shape) != tuple(q.shape[:-1]) or
+                                lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor of shape q.shape[:-1]")
+    if not (q.dtype == k.dtype == v.dtype) or (out is not None and out.dtype != q.dtype):
+        raise ValueError("q, k, v and out must share one dtype")
+    for t in (q, k, v, out, lse, mask):
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("sdpa_fwd runs on the GPU only: every tensor must be on a cuda device")
+    devs = {t.device for t in (q, k, v, out, lse, mask) if t is not None}
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on the same device")
+
+
+def sdpa_fwd(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, mask=None,
+             stream=None, return_lse=True):
+    """Fused SDPA forward through the C ABI `sdpa_fwd`.
+
+    q: [N,Lq,D] or [B,H,Lq,D]; k, v: [N,Lk,D] or [B,H,Lk,D]; bf16 or fp32 cuda tensors with
+    unit innermost stride (any other strides).  mask: optional bool/uint8 tensor
+    broadcastable to q.shape[:-1] + (Lk,), True/nonzero = visible.  scale defaults to
+    1/sqrt(D).  out/lse are allocated when not given (out contiguous, lse float32
+    [..., Lq]).  Returns (out, lse) -- lse is None when return_lse is False and no lse
+    tensor was passed.  The kernel is enqueued on `stream` (default: torch's current
+    stream of q's device); nothing is synchronised.
+    """
+    _check_shapes(q, k, v, out, lse, mask)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    args, _keep = _marshal(q, k, v, out, lse, mask, scale, is_causal)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        status = load_library().sdpa_fwd(*args, handle)
+    _raise_on(status)
+    return out, lse
+
+
+def sdpa_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, rank, B, H, Lq, Lk, D, strides, scale,
+               is_causal, mask_ptr, dtype) -> int:
+    """The C ABI `sdpa_check` on raw integers (pointers as ints, strides as a list of
+    5*rank ints).  Host-only: needs no GPU.  Returns the status code."""
+    arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
+    return load_library().sdpa_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, rank, B, H, Lq, Lk, D,
+                                     arr, float(scale), int(is_causal), mask_ptr, int(dtype))
+
+
+def sdpa_plan(rank, B, H, Lq, Lk, D, is_causal, dtype) -> SdpaPlan:
+    """The C ABI `sdpa_plan`: launch plan of the tile scheduler (host-only)."""
+    plan = SdpaPlan()
+    _raise_on(load_library().sdpa_plan(rank, B, H, Lq, Lk, D, int(is_causal), int(dtype),
+                                       ctypes.byref(plan)))
+    return plan
+
+
+def sdpa_plan_item(plan: SdpaPlan, block: int):
+    """The C ABI `sdpa_plan_item`: (bh, q_tile) run by workgroup `block` (host-only)."""
+    bh, qt = ctypes.c_int64(), ctypes.c_int64()
+    _raise_on(load_library().sdpa_plan_item(ctypes.byref(plan), int(block), ctypes.byref(bh),
+                                            ctypes.byref(qt)))
+    return bh.value, qt.value

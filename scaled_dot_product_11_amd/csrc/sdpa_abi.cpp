@@ -1,0 +1,195 @@
+// sdpa_abi.cpp -- the exported C ABI: validation, the rank-3/rank-4 stride normaliser,
+// the launch plan, status strings, and the one launch per call.
+//
+// Rank handling follows the PyTorch 2.14 note on rank-3 SDPA inputs: a folded or missing
+// batch dimension is the same computation, so a rank-3 [N,L,D] problem is rewritten as
+// the rank-4 problem [1,N,L,D] (batch stride 0) before anything else happens, and both
+// ranks reach the same fused kernel with the same arguments.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/sdpa.h"
+#include "sdpa_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validate the arguments and build the canonical (b, h, row, col) problem.
+int normalise(const void* q, const void* k, const void* v, const void* out, const float* lse,
+              int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+              const int64_t* strides, float scale, int is_causal, const uint8_t* mask,
+              int dtype, sdpa::Problem* p) {
+  if (rank != 3 && rank != 4) return SDPA_ERR_RANK;
+  if (rank == 3 && B != 1) return SDPA_ERR_RANK;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return SDPA_ERR_SHAPE;
+  if (Lq > kMaxDim || Lk > kMaxDim || B > kMaxDim || H > kMaxDim) return SDPA_ERR_SHAPE;
+  if (B != 0 && H > kMaxDim / B) return SDPA_ERR_SHAPE;
+  if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+  if (!strides) return SDPA_ERR_NULL;
+  if (!isfinite(scale)) return SDPA_ERR_SCALE;
+
+  const int64_t bh = B * H;
+  const int64_t q_tiles = (Lq + sdpa::kBlockM - 1) / sdpa::kBlockM;
+  if (bh != 0 && q_tiles > kMaxDim / bh) return SDPA_ERR_SHAPE;  // grid size
+  const bool any_rows = bh * Lq != 0;
+  const bool reads_kv = any_rows && Lk != 0;
+
+  // strides: q, k, v, out, mask; each `rank` entries in its own axis order.
+  int64_t s4[5][4];
+  for (int t = 0; t < 5; ++t) {
+    const int64_t* s = strides + t * rank;
+    if (t == 4 && !mask) {
+      s4[t][0] = s4[t][1] = s4[t][2] = s4[t][3] = 0;
+      continue;
+    }
+    if (rank == 4) {
+      for (int a = 0; a < 4; ++a) s4[t][a] = s[a];
+    } else {
+      s4[t][0] = 0;
+      s4[t][1] = s[0];
+      s4[t][2] = s[1];
+      s4[t][3] = s[2];
+    }
+    for (int a = 0; a < 4; ++a)
+      if (s4[t][a] < 0) return SDPA_ERR_STRIDE;
+    if (s4[t][3] != 1) return SDPA_ERR_STRIDE;
+  }
+
+  if (any_rows && (!q || !out)) return SDPA_ERR_NULL;
+  if (reads_kv && (!k || !v)) return SDPA_ERR_NULL;
+
+  const int64_t esize = dtype == SDPA_BF16 ? 2 : 4;
+  const void* bases[4] = {q, k, v, out};
+  for (int t = 0; t < 4; ++t) {
+    const bool used = (t == 1 || t == 2) ? reads_kv : any_rows;
+    if (!used) continue;
+    if (!aligned(bases[t], 16)) return SDPA_ERR_ALIGN;
+    for (int a = 0; a < 3; ++a)
+      if ((s4[t][a] * esize) % 16 != 0) return SDPA_ERR_ALIGN;
+  }
+  if (lse && !aligned(lse, 4)) return SDPA_ERR_ALIGN;
+
+  if (p) {
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->out = const_cast<void*>(out);
+    p->lse = const_cast<float*>(lse);
+    p->mask = mask;
+    p->B = B;
+    p->H = H;
+    p->Lq = Lq;
+    p->Lk = Lk;
+    p->D = D;
+    memcpy(p->sq, s4[0], sizeof p->sq);
+    memcpy(p->sk, s4[1], sizeof p->sk);
+    memcpy(p->sv, s4[2], sizeof p->sv);
+    memcpy(p->so, s4[3], sizeof p->so);
+    memcpy(p->sm, s4[4], sizeof p->sm);
+    p->scale = scale;
+    p->causal = is_causal ? 1 : 0;
+    p->dtype = dtype;
+  }
+  return SDPA_OK;
+}
+
+// The code object holds gfx950 machine code only; refuse other devices up front.
+// Cached per device id (the only global state of the library).
+bool device_is_gfx950(hipStream_t stream) {
+  int dev = 0;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return false;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return false;
+  }
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static signed char verdict[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (verdict[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+    verdict[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return verdict[dev] == 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_check(const void* q, const void* k, const void* v, const void* out, const float* lse,
+               int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+               const int64_t* strides, float scale, int is_causal, const uint8_t* mask,
+               int dtype) {
+  return normalise(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal, mask,
+                   dtype, nullptr);
+}
+
+int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int rank,
+             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides,
+             float scale, int is_causal, const uint8_t* mask, int dtype, void* stream) {
+  sdpa::Problem p;
+  const int st = normalise(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal,
+                           mask, dtype, &p);
+  if (st != SDPA_OK) return st;
+  if (p.B * p.H * p.Lq == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
+const char* sdpa_strerror(int status) {
+  switch (status) {
+    case SDPA_OK: return "success";
+    case SDPA_ERR_NULL: return "a required pointer is NULL";
+    case SDPA_ERR_RANK: return "rank must be 3 or 4 (rank 3 requires B == 1)";
+    case SDPA_ERR_SHAPE: return "negative size, or a size beyond the supported maximum";
+    case SDPA_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
+    case SDPA_ERR_DTYPE: return "dtype must be SDPA_F32 or SDPA_BF16";
+    case SDPA_ERR_STRIDE: return "innermost strides must be 1 and no stride may be negative";
+    case SDPA_ERR_ALIGN:
+      return "q/k/v/out base pointers and outer strides must be 16-byte aligned, lse 4-byte";
+    case SDPA_ERR_SCALE: return "scale must be finite";
+    case SDPA_ERR_DEVICE: return "device is not gfx950 or the kernel launch failed";
+    default: return "unknown sdpa status";
+  }
+}
+
+int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, int is_causal,
+              int dtype, sdpa_plan_t* plan) {
+  if (!plan) return SDPA_ERR_NULL;
+  // Validate the sizes only: fake, aligned, non-NULL pointers and unit-innermost strides.
+  int64_t strides[20];
+  for (int t = 0; t < 5; ++t)
+    for (int a = 0; a < rank && a < 4; ++a) strides[t * rank + a] = (a == rank - 1) ? 1 : 0;
+  static const float dummy[4] __attribute__((aligned(16))) = {0, 0, 0, 0};
+  const int st = normalise(dummy, dummy, dummy, dummy, nullptr, rank, B, H, Lq, Lk, D, strides,
+                           1.0f, is_causal, nullptr, dtype, nullptr);
+  if (st != SDPA_OK) return st;
+  plan->block_m = sdpa::kBlockM;
+  plan->block_n = sdpa::kBlockN;
+  plan->threads = sdpa::kThreads;
+  plan->q_tiles = (Lq + sdpa::kBlockM - 1) / sdpa::kBlockM;
+  plan->bh = B * H;
+  plan->items = plan->bh * plan->q_tiles;
+  plan->lds_bytes = dtype == SDPA_BF16 ? sdpa::lds_bytes_bf16(int(D)) : sdpa::lds_bytes_f32(int(D));
+  plan->is_causal = is_causal ? 1 : 0;
+  return SDPA_OK;
+}
+
+int sdpa_plan_item(const sdpa_plan_t* plan, int64_t block, int64_t* bh, int64_t* q_tile) {
+  if (!plan || !bh || !q_tile) return SDPA_ERR_NULL;
+  if (block < 0 || block >= plan->items) return SDPA_ERR_SHAPE;
+  sdpa::decode_item(block, plan->bh, plan->q_tiles, plan->is_causal != 0, bh, q_tile);
+  return SDPA_OK;
+}
+
+}  // extern "C"

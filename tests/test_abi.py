@@ -1,0 +1,214 @@
+"""Host-only tests of the C ABI: the library loads without a GPU, exports every entry point
+declared in include/*.h, and sdpa_check / sdpa_plan behave as documented.  No kernel is
+launched here."""
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import scaled_dot_product_11_amd as sd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, RANK, SHAPE, HEAD, DTYPE, STRIDE, ALIGN, SCALE, DEVICE = range(10)
+
+
+def declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(sdpa_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    decl = declared_functions()
+    assert set(decl) >= {"sdpa_fwd", "sdpa_check", "sdpa_strerror", "sdpa_plan",
+                         "sdpa_plan_item"}
+    out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in decl if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = sd.load_library()
+    for n in decl:
+        assert hasattr(lib, n)
+
+
+def test_library_has_gfx950_code_only():
+    out = subprocess.run(["strings", sd.LIB_PATH], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+A = 0x100000  # a 16-byte aligned fake device address (never dereferenced by sdpa_check)
+
+
+def args4(B=2, H=3, Lq=100, Lk=90, D=64, dtype=sd.SDPA_BF16, mask=False, **over):
+    esz = 2 if dtype == sd.SDPA_BF16 else 4
+    q = [H * Lq * D, Lq * D, D, 1]
+    k = [H * Lk * D, Lk * D, D, 1]
+    m = [0, 0, Lk, 1] if mask else [0, 0, 0, 0]
+    a = dict(q_ptr=A, k_ptr=A + 0x10000, v_ptr=A + 0x20000, out_ptr=A + 0x30000, lse_ptr=A,
+             rank=4, B=B, H=H, Lq=Lq, Lk=Lk, D=D, strides=q + k + k + q + m, scale=0.125,
+             is_causal=1, mask_ptr=A + 0x40000 if mask else None, dtype=dtype)
+    a.update(over)
+    return a
+
+
+def check(**kw):
+    return sd.sdpa_check(**kw)
+
+
+def test_valid_rank4_and_rank3():
+    assert check(**args4()) == OK
+    assert check(**args4(mask=True)) == OK
+    assert check(**args4(dtype=sd.SDPA_F32, D=128)) == OK
+    r3 = args4(B=1)
+    s = r3["strides"]
+    r3["strides"] = s[1:4] + s[5:8] + s[9:12] + s[13:16] + s[17:20]
+    r3["rank"] = 3
+    assert check(**r3) == OK
+
+
+def test_rank_errors():
+    assert check(**args4(rank=5)) == RANK
+    assert check(**args4(rank=2)) == RANK
+    bad = args4(B=2)
+    bad["rank"] = 3
+    bad["strides"] = bad["strides"][:15]
+    assert check(**bad) == RANK
+
+
+def test_shape_errors():
+    assert check(**args4(Lq=-1)) == SHAPE
+    assert check(**args4(Lk=-5)) == SHAPE
+    assert check(**args4(B=-1)) == SHAPE
+    assert check(**args4(Lq=2 ** 31)) == SHAPE
+    assert check(**args4(B=2 ** 20, H=2 ** 12)) == SHAPE
+
+
+def test_head_dim_and_dtype_errors():
+    for D in (0, 32, 96, 256):
+        assert check(**args4(D=D)) == HEAD
+    assert check(**args4(dtype=2)) == DTYPE
+    assert check(**args4(dtype=-1)) == DTYPE
+
+
+def test_stride_errors():
+    a = args4()
+    a["strides"] = list(a["strides"])
+    a["strides"][3] = 2  # q's innermost stride
+    assert check(**a) == STRIDE
+    a = args4()
+    a["strides"] = list(a["strides"])
+    a["strides"][5] = -64  # k's head stride
+    assert check(**a) == STRIDE
+    a = args4(mask=True)
+    a["strides"] = list(a["strides"])
+    a["strides"][19] = 2  # mask's key stride
+    assert check(**a) == STRIDE
+    a = args4(mask=False)
+    a["strides"] = list(a["strides"])
+    a["strides"][19] = 7  # ignored without a mask
+    assert check(**a) == OK
+
+
+def test_alignment_errors():
+    assert check(**args4(q_ptr=A + 8)) == ALIGN
+    assert check(**args4(out_ptr=A + 2)) == ALIGN
+    assert check(**args4(lse_ptr=A + 2)) == ALIGN
+    a = args4()
+    a["strides"] = list(a["strides"])
+    a["strides"][2] = 68  # bf16 row stride of 136 bytes is not a multiple of 16
+    assert check(**a) == ALIGN
+    a = args4(dtype=sd.SDPA_F32)
+    a["strides"] = list(a["strides"])
+    a["strides"][6] = 66  # fp32 row stride of 264 bytes
+    assert check(**a) == ALIGN
+    # masks need no alignment
+    assert check(**args4(mask=True, mask_ptr=A + 3)) == OK
+
+
+def test_null_errors():
+    assert check(**args4(q_ptr=None)) == NULL
+    assert check(**args4(out_ptr=None)) == NULL
+    assert check(**args4(k_ptr=None)) == NULL
+    assert check(**args4(strides=None)) == NULL
+    assert check(**args4(lse_ptr=None)) == OK  # lse is optional
+    # k/v are not read when Lk == 0, q/out not when there are no rows
+    assert check(**args4(Lk=0, k_ptr=None, v_ptr=None)) == OK
+    assert check(**args4(Lq=0, q_ptr=None, out_ptr=None)) == OK
+
+
+def test_scale_errors():
+    for s in (float("nan"), float("inf"), float("-inf")):
+        assert check(**args4(scale=s)) == SCALE
+    for s in (0.0, -1.0, 1e30):
+        assert check(**args4(scale=s)) == OK
+
+
+def test_strerror_distinct():
+    msgs = {sd.sdpa_strerror(s) for s in range(10)}
+    assert len(msgs) == 10
+    assert "unknown" in sd.sdpa_strerror(12345)
+
+
+def test_fwd_rejects_before_any_device_call():
+    """Validation errors come back from sdpa_fwd itself, without touching a GPU."""
+    import ctypes
+    lib = sd.load_library()
+    a = args4(D=96)
+    arr = (ctypes.c_int64 * 20)(*a["strides"])
+    st = lib.sdpa_fwd(a["q_ptr"], a["k_ptr"], a["v_ptr"], a["out_ptr"], a["lse_ptr"], 4, 2, 3, 100,
+                      90, 96, arr, 0.125, 1, None, 1, None)
+    assert st == HEAD
+    # an empty problem is a no-op returning success, also without a GPU
+    st = lib.sdpa_fwd(None, None, None, None, None, 4, 2, 3, 0, 90, 64, arr, 0.125, 1, None, 1, None)
+    assert st == OK
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_plan_items_are_a_permutation(causal):
+    for (B, H, L) in [(1, 32, 8192), (4, 16, 1024), (2, 3, 200), (1, 1, 1)]:
+        plan = sd.sdpa_plan(4, B, H, L, L, 128, causal, sd.SDPA_BF16)
+        assert plan.q_tiles == (L + plan.block_m - 1) // plan.block_m
+        assert plan.items == B * H * plan.q_tiles
+        seen = set()
+        order = [sd.sdpa_plan_item(plan, i) for i in range(plan.items)]
+        for bh, qt in order:
+            assert 0 <= bh < B * H and 0 <= qt < plan.q_tiles
+            seen.add((bh, qt))
+        assert len(seen) == plan.items
+        if causal:  # heaviest first: the query tile never increases along the launch order
+            qts = [qt for _, qt in order]
+            assert all(a >= b for a, b in zip(qts, qts[1:]))
+            assert qts[0] == plan.q_tiles - 1
+        # consecutive workgroups belong to different heads; with B*H a multiple of 8,
+        # workgroup i (which lands on XCD i % 8) always serves a head of that residue
+        if B * H % 8 == 0:
+            for i, (bh, _) in enumerate(order):
+                assert bh % 8 == i % 8
+        with pytest.raises(sd.SdpaError):
+            sd.sdpa_plan_item(plan, plan.items)
+
+
+def test_plan_rejects_bad_sizes():
+    with pytest.raises(sd.SdpaError) as e:
+        sd.sdpa_plan(4, 1, 1, 16, 16, 80, 1, sd.SDPA_BF16)
+    assert e.value.status == HEAD
+    plan = sd.sdpa_plan(3, 1, 128, 2048, 2048, 128, 1, sd.SDPA_BF16)
+    plan4 = sd.sdpa_plan(4, 8, 16, 2048, 2048, 128, 1, sd.SDPA_BF16)
+    # rank 3 and rank 4 of the same problem get the same launch
+    assert [getattr(plan, f) for f, _ in sd.SdpaPlan._fields_] == \
+        [getattr(plan4, f) for f, _ in sd.SdpaPlan._fields_]
+    assert plan.lds_bytes <= 160 * 1024
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU only"):
+        sd.sdpa_fwd(q, q, q)

@@ -123,8 +123,10 @@ def config5(device="cpu"):
         m[b, 0, rows, :] = False
         empty.append(rows.sort().values)
     q, k, v, m = q.to(device), k.to(device), v.to(device), m.to(device)
-    return Workload("c5_rank4_bf16_boolmask_b2_h8_l4096_d64", q, k, v,
-                    m.expand(2, 8, 4096, 4096), False, 1 / math.sqrt(64),
+    # the [2,1,L,L] mask is handed over as is: consumers broadcast it over the heads with
+    # a zero head stride (moving an expanded view between devices would materialise it)
+    return Workload("c5_rank4_bf16_boolmask_b2_h8_l4096_d64", q, k, v, m, False,
+                    1 / math.sqrt(64),
                     "rank-4 bool-mask bf16 [2,8,4096,64], p_keep=0.1, 5% empty rows",
                     extra={"empty_rows": torch.stack(empty)})
 
