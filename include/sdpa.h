@@ -45,7 +45,7 @@ enum sdpa_status {
   SDPA_OK = 0,
   SDPA_ERR_NULL = 1,     /* a required pointer is NULL (strides, or q/k/v/out when read) */
   SDPA_ERR_RANK = 2,     /* rank not 3 or 4, or rank 3 with B != 1                       */
-  SDPA_ERR_SHAPE = 3,    /* negative size, or a size/grid beyond the supported maximum   */
+  SDPA_ERR_SHAPE = 3,    /* negative size, or a size/extent beyond the supported maximum */
   SDPA_ERR_HEAD_DIM = 4, /* D not in {64, 128}                                           */
   SDPA_ERR_DTYPE = 5,    /* dtype not an sdpa_dtype                                      */
   SDPA_ERR_STRIDE = 6,   /* innermost stride != 1, or a negative stride                  */
@@ -69,8 +69,10 @@ enum sdpa_status {
  *                 [N,Lq]), 4-byte aligned, receiving the natural-log LSE (-inf for
  *                 rows with no visible key).
  *   rank          3 or 4.  Rank 3 requires B == 1 and H == N.
- *   B,H,Lq,Lk,D   sizes; D in {64, 128}; Lq, Lk and B*H below 2^31.  B*H*Lq == 0 is a
- *                 no-op returning SDPA_OK; Lk == 0 makes every row empty.
+ *   B,H,Lq,Lk,D   sizes; D in {64, 128}; Lq, Lk and B*H below 2^31; (Lk + 64) times the
+ *                 row stride of k (and of v) must stay below 2 GiB (one head's rows are
+ *                 addressed with 32-bit offsets).  B*H*Lq == 0 is a no-op returning
+ *                 SDPA_OK; Lk == 0 makes every row empty.
  *   strides       5*rank element strides, tensor-major: q, k, v, out, mask, each in its
  *                 own axis order ([N,L,D] / [B,H,L,D]; the mask is [N,Lq,Lk] /
  *                 [B,H,Lq,Lk]).  The mask's entries are ignored when mask == NULL.

@@ -74,6 +74,11 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
       if ((s4[t][a] * esize) % 16 != 0) return SDPA_ERR_ALIGN;
   }
   if (lse && !aligned(lse, 4)) return SDPA_ERR_ALIGN;
+  // K and V rows are addressed with 32-bit byte offsets from the head's base: the rows of
+  // one head plus one tile of overrun must span less than 2 GiB.
+  if (reads_kv)
+    for (int t = 1; t <= 2; ++t)
+      if (s4[t][2] > kMaxDim / esize / (Lk + sdpa::kBlockN)) return SDPA_ERR_SHAPE;
 
   if (p) {
     p->q = q;
@@ -151,7 +156,9 @@ const char* sdpa_strerror(int status) {
     case SDPA_OK: return "success";
     case SDPA_ERR_NULL: return "a required pointer is NULL";
     case SDPA_ERR_RANK: return "rank must be 3 or 4 (rank 3 requires B == 1)";
-    case SDPA_ERR_SHAPE: return "negative size, or a size beyond the supported maximum";
+    case SDPA_ERR_SHAPE:
+      return "negative size, a size beyond the supported maximum, or one head's k/v rows "
+             "spanning 2 GiB or more";
     case SDPA_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
     case SDPA_ERR_DTYPE: return "dtype must be SDPA_F32 or SDPA_BF16";
     case SDPA_ERR_STRIDE: return "innermost strides must be 1 and no stride may be negative";

@@ -68,6 +68,14 @@ __device__ inline float pair_sum(float x) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for all vector-memory loads only:
+// vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle, no stride;
+// reads past num_records return zero.
+constexpr int kBufferFlags = 0x00020000;
+
 // Row permutation of a 32-key K sub-tile in LDS: swapping bits 2 and 3 of the row index
 // makes the score accumulator hold, in half h of the lanes, keys 8h..8h+7 in registers
 // 0..7 and keys 16+8h..16+8h+7 in registers 8..15, i.e. runs of 8 consecutive keys --
@@ -75,27 +83,45 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // involution, so the same map is used to store and to interpret.
 __device__ inline int perm5(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// XOR swizzle of the 16-byte chunks of a transposed V row (row = head-dim index d,
-// 8 chunks of 8 keys) so that both the transposing stores and the operand loads of
-// the second product spread over all LDS banks.
-__device__ inline int vswz(int d) { return (d ^ (d >> 3)) & 7; }
-
 // ---------------------------------------------------------------------------------------
 // bf16 kernel: bf16 MFMA 32x32x16 for both products, fp32 accumulation and softmax.
+//
+// LDS per workgroup: two K stages and two V stages, each a plain row-major copy of 64
+// keys x D (rows padded: K by 16 bytes, V by 32 bytes, so that the operand reads below
+// hit distinct banks).  Rows of a 32-key K sub-tile are stored with bits 2 and 3 of
+// the row index swapped (perm5), so that the score accumulator of half h of the lanes
+// holds keys 8h..8h+7 (registers 0..7) and 16+8h..16+8h+7 (registers 8..15) -- runs of
+// 8 consecutive keys, exactly the operand layout P^T needs in the second product.
+// The V^T operand is read with the gfx950 transposing LDS read (ds_read_b64_tr_b16):
+// within each group of 16 lanes, lane i receives element i mod 4 of the 8-byte pieces
+// addressed by lanes 4e + i/4 (e = 0..3); addressing V[key0 + e][d0 + 4q] from lane
+// 4e + q therefore hands lane i the column d0 + i of four consecutive keys.
 // ---------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// The running max used as the exponent reference may lag the true row max by up to this
+// many base-2 units before O and l are rescaled: p = 2^(x - m_ref) then stays <= 256,
+// exact in fp32 accumulation and in bf16 (8 significand bits at every magnitude), and
+// the final O / l is unchanged because both carry the same reference.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ inline s16x4 ds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+template <int D, bool CAUSAL, bool MASK, bool POS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16(Args a) {
-  constexpr int DG = D / 8;                             // 16-byte groups per row
-  constexpr int KCH = kBlockN * DG / kThreads;          // K chunks per thread per tile
-  constexpr int VUNITS = (kBlockN / 4) * DG;            // (4 keys x 8 cols) V units per tile
-  constexpr int KROW = D + 8;                           // K row pitch in LDS (elements)
-  constexpr int K_ELEMS = kBlockN * KROW;
-  constexpr int V_ELEMS = D * kBlockN;                  // transposed V: D rows of 64 keys
-  constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static_assert(KCH * kThreads == kBlockN * DG, "K tile must split evenly over threads");
-  static_assert(VUNITS <= kThreads, "one V unit per thread at most");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  constexpr int DG = D / 8;                      // 16-byte chunks per row
+  constexpr int CH = kBlockN * DG / kThreads;    // chunks per thread per K (or V) tile
+  constexpr int ROWS_PER_PASS = kThreads / DG;   // tile rows covered by one chunk pass
+  constexpr int KP = 2 * D + 16;                 // K row pitch in LDS (bytes)
+  constexpr int VP = 2 * D + 32;                 // V row pitch in LDS (bytes)
+  constexpr int KT = kBlockN * KP;               // bytes of one K stage
+  constexpr int VT = kBlockN * VP;               // bytes of one V stage
+  static_assert(CH * kThreads == kBlockN * DG, "tile must split evenly over threads");
+  __shared__ __attribute__((aligned(16))) char lds[2 * KT + 2 * VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,8 +133,8 @@ void fwd_bf16(Args a) {
   decode_item(blockIdx.x, a.bh_count, a.q_tiles, CAUSAL, &bh, &qt);
   const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.sq[0] + h * a.sq[1];
-  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.sk[0] + h * a.sk[1];
-  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + b * a.sv[0] + h * a.sv[1];
+  const char* kb = static_cast<const char*>(a.k) + 2 * (b * a.sk[0] + h * a.sk[1]);
+  const char* vb = static_cast<const char*>(a.v) + 2 * (b * a.sv[0] + h * a.sv[1]);
   uint16_t* ob = static_cast<uint16_t*>(a.out) + b * a.so[0] + h * a.so[1];
   const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
 
@@ -118,8 +144,8 @@ void fwd_bf16(Args a) {
   const bool q_ok = qi < a.Lq;
   const bool wave_live = qw < a.Lq;
 
-  // Q^T operand fragments, held in registers for the whole key walk:
-  // chunk c covers head dims 16c..16c+15, half hf supplies dims 16c+8hf..16c+8hf+7.
+  // Q^T operand fragments, held for the whole key walk: chunk c covers head dims
+  // 16c..16c+15, half hf supplies dims 16c+8hf..16c+8hf+7.
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
@@ -127,79 +153,80 @@ void fwd_bf16(Args a) {
     if (q_ok) w = ld16(qb + int64_t(qi) * a.sq[2] + 16 * c + 8 * hf);
     qf[c] = __builtin_bit_cast(bf16x8, w);
   }
+  // Retire the Q loads here, on every path: left in flight, they would make the
+  // memory-counter wait in the key loop cover the K/V prefetch as well.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // Keys that can be visible to some stored row of this workgroup.
   int kend = a.Lk;
   if (CAUSAL) kend = min(kend, min(q0 + kBlockM, a.Lq));
   const int ntiles = (kend + kBlockN - 1) / kBlockN;
 
-  // ---- global -> register staging of one K/V tile ----
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-  const int v_kg = tid % 16;  // V unit: keys 4*v_kg..+3 of the tile
-  const int v_dg = tid / 16;  //         head dims 8*v_dg..+7
-  auto load_tile = [&](int t) {
-    const int k0 = t * kBlockN;
+  // ---- global -> register -> LDS staging of K and V tiles (buffer loads: rows past
+  // the end of the head read as zero) ----
+  const int k_rowb = int(a.sk[2]) * 2, v_rowb = int(a.sv[2]) * 2;  // row strides, bytes
+  const int k_ext = a.Lk > 0 ? (a.Lk - 1) * k_rowb + 2 * D : 0;
+  const int v_ext = a.Lk > 0 ? (a.Lk - 1) * v_rowb + 2 * D : 0;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, k_ext, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, v_ext, kBufferFlags);
+  const int ld_row = tid / DG, ld_col = tid % DG;  // this thread's first chunk
+  const int k_goff = ld_row * k_rowb + ld_col * 16;
+  const int v_goff = ld_row * v_rowb + ld_col * 16;
+  const int k_soff = ((ld_row & ~31) | perm5(ld_row & 31)) * KP + ld_col * 16;
+  const int v_soff = ld_row * VP + ld_col * 16;
+  u32x4 kreg[CH], vreg[CH];
+  auto load_k = [&](int t) {
 #pragma unroll
-    for (int p = 0; p < KCH; ++p) {
-      const int c = tid + p * kThreads;
-      const int row = c / DG, col = (c % DG) * 8;
-      const int key = k0 + row;
-      kreg[p] = key < a.Lk ? ld16(kb + int64_t(key) * a.sk[2] + col) : u32x4{0, 0, 0, 0};
-    }
-    if (tid < VUNITS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * v_kg + r;
-        vreg[r] = key < a.Lk ? ld16(vb + int64_t(key) * a.sv[2] + 8 * v_dg) : u32x4{0, 0, 0, 0};
-      }
-    }
+    for (int p = 0; p < CH; ++p)
+      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_goff + p * ROWS_PER_PASS * k_rowb,
+                                                       t * kBlockN * k_rowb, 0);
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = lds + buf * STAGE;
-    uint16_t* vt = ks + K_ELEMS;
+  auto load_v = [&](int t) {
 #pragma unroll
-    for (int p = 0; p < KCH; ++p) {
-      const int c = tid + p * kThreads;
-      const int row = c / DG, col = (c % DG) * 8;
-      const int prow = (row & ~31) | perm5(row & 31);
-      *reinterpret_cast<u32x4*>(ks + prow * KROW + col) = kreg[p];
-    }
-    if (tid < VUNITS) {
-      // 4 keys x 8 dims -> 8 rows (dims) of 4 consecutive keys each.
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t r0 = vreg[0][e2], r1 = vreg[1][e2], r2 = vreg[2][e2], r3 = vreg[3][e2];
-        const int d_lo = 8 * v_dg + 2 * e2;
-        const u32x2 lo = {(r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16)};
-        const u32x2 hi = {(r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u)};
-        const int lc = v_kg >> 1, half = v_kg & 1;
-        *reinterpret_cast<u32x2*>(vt + d_lo * kBlockN + ((lc ^ vswz(d_lo)) * 8) + half * 4) = lo;
-        *reinterpret_cast<u32x2*>(vt + (d_lo + 1) * kBlockN + ((lc ^ vswz(d_lo + 1)) * 8) +
-                                  half * 4) = hi;
-      }
-    }
+    for (int p = 0; p < CH; ++p)
+      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_goff + p * ROWS_PER_PASS * v_rowb,
+                                                       t * kBlockN * v_rowb, 0);
   };
+  auto store_k = [&](int s) {
+#pragma unroll
+    for (int p = 0; p < CH; ++p)
+      *reinterpret_cast<u32x4*>(lds + s * KT + k_soff + p * ROWS_PER_PASS * KP) = kreg[p];
+  };
+  auto store_v = [&](int s) {
+#pragma unroll
+    for (int p = 0; p < CH; ++p)
+      *reinterpret_cast<u32x4*>(lds + 2 * KT + s * VT + v_soff + p * ROWS_PER_PASS * VP) = vreg[p];
+  };
+
+  // Per-lane operand addresses (stage and tile offsets are immediates).
+  const int kfrag = li * KP + hf * 16;
+  const int g16 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+  const int vfrag = (8 * (g16 >> 1) + e4) * VP + (16 * (g16 & 1) + 4 * q4) * 2;
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY;  // running max of the base-2 scores of this row
-  float l_run = 0.f;        // running sum over this lane's key half, relative to m_run
+  float m_ref = -INFINITY;  // exponent reference (base-2 units), may lag the row max
+  float l_run = 0.f;        // sum of 2^(x - m_ref) over this lane's key half
+  const float c2 = POS ? a.scale_log2 : 1.f;
 
   if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
   }
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const uint16_t* ks = lds + buf * STAGE;
-    const uint16_t* vt = ks + K_ELEMS;
+    const int stg = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      load_k(t + 1);
+      load_v(t + 1);
+    }
     const int k0 = t * kBlockN;
     // Wave-uniform: does any key of this tile reach any row of this wave?
     const bool tile_live = wave_live && (!CAUSAL || k0 <= qw + 31);
@@ -223,29 +250,31 @@ void fwd_bf16(Args a) {
         }
       }
 
-      // S^T = K . Q^T for the two 32-key sub-tiles.
+      // S^T = K . Q^T for the two 32-key sub-tiles (all fragment reads of a sub-tile
+      // are issued before its products).
+      const char* kfp = lds + stg * KT + kfrag;
       f32x16 s[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        bf16x8 kf[D / 16];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          kf[c] = __builtin_bit_cast(bf16x8, ld16(kfp + kt * 32 * KP + c * 32));
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-        const bool sub_live = !CAUSAL || (k0 + 32 * kt <= qw + 31);
-        if (sub_live) {
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) {
-            const bf16x8 kf = __builtin_bit_cast(
-                bf16x8, ld16(ks + (32 * kt + li) * KROW + 16 * c + 8 * hf));
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kt], 0, 0, 0);
-          }
-        }
+        for (int c = 0; c < D / 16; ++c)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], s[kt], 0, 0, 0);
       }
 
-      // Scale into base-2 units and hide invisible keys.
-      float x[2][16];
+      // Scores in the comparison domain: raw q.k when the scale is positive (the scale
+      // is folded into the exponent), else scale * q.k.  Invisible keys -> -inf.
+      if (!POS) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[kt][r] = s[kt][r] * a.scale_log2;
+          for (int r = 0; r < 16; ++r) s[kt][r] *= a.scale_log2;
+      }
       const bool edge = (CAUSAL && k0 + kBlockN - 1 > qw) || (k0 + kBlockN > a.Lk);
       if (edge || MASK) {
 #pragma unroll
@@ -256,57 +285,66 @@ void fwd_bf16(Args a) {
             bool hide = key >= a.Lk;
             if (CAUSAL) hide = hide || key > qi;
             if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
-            if (hide) x[kt][r] = -INFINITY;
+            if (hide) s[kt][r] = -INFINITY;
           }
       }
 
-      // Online softmax: new running max over both key halves, rescale, exponentiate.
+      // Online softmax with a lagging reference: rescale O and l only when some row of
+      // the wave sees its max grow by more than kRescaleSlack.
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kt][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+      mx = pair_max(mx) * c2;  // base-2 units
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_ref == -INFINITY ? 0.f : exp2_fast(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(x[kt][r] - m_use);
-          x[kt][r] = p;
+          const float p = exp2_fast(__builtin_fmaf(s[kt][r], c2, -mu));
+          s[kt][r] = p;
           psum += p;
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      l_run += psum;
 
       // P^T operand: chunk c holds keys 16c + 8hf .. 16c + 8hf + 7 of this lane's row.
       bf16x8 pf[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) pf[c][u] = static_cast<__bf16>(x[c >> 1][8 * (c & 1) + u]);
+        for (int u = 0; u < 8; ++u) pf[c][u] = static_cast<__bf16>(s[c >> 1][8 * (c & 1) + u]);
 
-      // O^T += V^T . P^T
+      // O^T += V^T . P^T ; the V^T operand of key chunk c comes from two transposing
+      // reads (keys 16c + 8hf + 0..3 and + 4..7, head dims 32dt + li).
+      const char* vfp = lds + 2 * KT + stg * VT + vfrag;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int d = 32 * dt + li;
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8, ld16(vt + d * kBlockN + (((2 * c + hf) ^ vswz(d)) * 8)));
+          const s16x4 lo = ds_read_tr(vfp + (16 * c) * VP + 64 * dt);
+          const s16x4 hi = ds_read_tr(vfp + (16 * c + 4) * VP + 64 * dt);
+          const s16x4 both[2] = {lo, hi};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[dt], 0, 0, 0);
         }
-      }
     }
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    if (more) {
+      store_k(stg ^ 1);
+      store_v(stg ^ 1);
+    }
     __syncthreads();
   }
 
@@ -332,7 +370,7 @@ void fwd_bf16(Args a) {
       }
     if (a.lse && hf == 0)
       a.lse[bh * a.Lq + qi] =
-          l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+          l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -527,8 +565,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32(Args a) {
 template <int D, bool CAUSAL, bool MASK>
 hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Args*>(&a)};
-  const void* fn = dtype == 1 ? reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK>)
-                              : reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK>);
+  const void* fn;
+  if (dtype == 1)
+    fn = a.scale_log2 > 0.f ? reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, true>)
+                            : reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, false>);
+  else
+    fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK>);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
 }
 

@@ -88,6 +88,13 @@ def test_shape_errors():
     assert check(**args4(B=-1)) == SHAPE
     assert check(**args4(Lq=2 ** 31)) == SHAPE
     assert check(**args4(B=2 ** 20, H=2 ** 12)) == SHAPE
+    # one head's K rows (plus a tile) must span less than 2 GiB
+    big = args4(Lk=2 ** 20, D=128)
+    big["strides"] = list(big["strides"])
+    big["strides"][6] = 1024  # k row stride: 2^20 rows * 2 KiB = 2 GiB
+    assert check(**big) == SHAPE
+    big["strides"][6] = 512
+    assert check(**big) == OK
 
 
 def test_head_dim_and_dtype_errors():
