@@ -30,10 +30,20 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # 2516.58
 PEAK_F32_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
-# FETCH_SIZE + WRITE_SIZE of the fused kernel on the default workload, from two
-# rocprofv3 --pmc passes, each scaled by the same counter on a plain copy of known size;
-# bytes per launch.  None until measured for the kernel as it is now.
-TRAFFIC_BYTES = None
+# HBM bytes per launch of the fused kernel on the default workload: FETCH_SIZE and
+# WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
+# for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
+# kernel source they were taken on (sha256 prefix below); reported as null otherwise.
+TRAFFIC_BYTES = 549138 * 1024
+TRAFFIC_KERNEL_SHA256 = "185175e18b4da2d4"
+KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
+
+
+def measured_traffic():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        current = hashlib.sha256(f.read()).hexdigest()
+    return TRAFFIC_BYTES if current.startswith(TRAFFIC_KERNEL_SHA256) else None
 
 
 def visible_pairs(Lq, Lk, causal):
@@ -150,7 +160,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--report", default=None, help="write per-workload timings here")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="also run one plain device copy of this many MiB (counter scaling)")
+                    help="also run one elementwise kernel reading and writing this many MiB "
+                         "(scale reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -189,7 +200,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": TRAFFIC_BYTES,
+                     "traffic": measured_traffic(),
                      "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
                      "kernel_ms_median": round(r["kernel_ms_median"], 4)},
         "cpu_baseline": None,
@@ -198,11 +209,13 @@ def main():
         line["cpu_baseline"] = cpu_baseline(wl)
 
     if args.copy_calibration_mib:
+        # one elementwise kernel that reads N bytes and writes N bytes: the HBM counters
+        # read for it give their scale factor against known traffic
         n = args.copy_calibration_mib * 2 ** 20 // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     if args.report:

@@ -35,7 +35,8 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
 
   const int64_t bh = B * H;
-  const int64_t q_tiles = (Lq + sdpa::kBlockM - 1) / sdpa::kBlockM;
+  const int64_t bm = sdpa::block_m(dtype);
+  const int64_t q_tiles = (Lq + bm - 1) / bm;
   if (bh != 0 && q_tiles > kMaxDim / bh) return SDPA_ERR_SHAPE;  // grid size
   const bool any_rows = bh * Lq != 0;
   const bool reads_kv = any_rows && Lk != 0;
@@ -78,7 +79,7 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
   // one head plus one tile of overrun must span less than 2 GiB.
   if (reads_kv)
     for (int t = 1; t <= 2; ++t)
-      if (s4[t][2] > kMaxDim / esize / (Lk + sdpa::kBlockN)) return SDPA_ERR_SHAPE;
+      if (s4[t][2] > kMaxDim / esize / (Lk + sdpa::block_n(dtype))) return SDPA_ERR_SHAPE;
 
   if (p) {
     p->q = q;
@@ -181,10 +182,10 @@ int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
   const int st = normalise(dummy, dummy, dummy, dummy, nullptr, rank, B, H, Lq, Lk, D, strides,
                            1.0f, is_causal, nullptr, dtype, nullptr);
   if (st != SDPA_OK) return st;
-  plan->block_m = sdpa::kBlockM;
-  plan->block_n = sdpa::kBlockN;
-  plan->threads = sdpa::kThreads;
-  plan->q_tiles = (Lq + sdpa::kBlockM - 1) / sdpa::kBlockM;
+  plan->block_m = sdpa::block_m(dtype);
+  plan->block_n = sdpa::block_n(dtype);
+  plan->threads = sdpa::block_threads(dtype);
+  plan->q_tiles = (Lq + plan->block_m - 1) / plan->block_m;
   plan->bh = B * H;
   plan->items = plan->bh * plan->q_tiles;
   plan->lds_bytes = dtype == SDPA_BF16 ? sdpa::lds_bytes_bf16(int(D)) : sdpa::lds_bytes_f32(int(D));

@@ -72,6 +72,10 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // vmcnt = 0, expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 // Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle, no stride;
 // reads past num_records return zero.
 constexpr int kBufferFlags = 0x00020000;
@@ -86,16 +90,30 @@ __device__ inline int perm5(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 
 // ---------------------------------------------------------------------------------------
 // bf16 kernel: bf16 MFMA 32x32x16 for both products, fp32 accumulation and softmax.
 //
+// A workgroup is 8 waves owning 256 query rows of one (b, h), 32 rows per wave; each
+// SIMD hosts two of its waves, one from each of two groups.  Per key tile t of 64 keys,
+// a wave's work splits into a matrix phase M(t) = { O += V(t-1) P(t-1); S(t) = K(t) Q^T }
+// and a vector phase V(t) = { softmax of S(t) -> P(t) }, and the two groups run them
+// out of step, separated by workgroup barriers:
+//     phase A of step t:  group 0 runs M(t),   group 1 runs V(t-1)
+//     phase B of step t:  group 0 runs V(t),   group 1 runs M(t)
+// so on every SIMD one wave feeds the matrix cores while the other feeds the vector
+// ALU.  The groups take alternating 32-row slices, so under a causal mask their numbers
+// of live key tiles differ by at most one.
+//
 // LDS per workgroup: two K stages and two V stages, each a plain row-major copy of 64
-// keys x D (rows padded: K by 16 bytes, V by 32 bytes, so that the operand reads below
-// hit distinct banks).  Rows of a 32-key K sub-tile are stored with bits 2 and 3 of
-// the row index swapped (perm5), so that the score accumulator of half h of the lanes
-// holds keys 8h..8h+7 (registers 0..7) and 16+8h..16+8h+7 (registers 8..15) -- runs of
-// 8 consecutive keys, exactly the operand layout P^T needs in the second product.
-// The V^T operand is read with the gfx950 transposing LDS read (ds_read_b64_tr_b16):
-// within each group of 16 lanes, lane i receives element i mod 4 of the 8-byte pieces
-// addressed by lanes 4e + i/4 (e = 0..3); addressing V[key0 + e][d0 + 4q] from lane
-// 4e + q therefore hands lane i the column d0 + i of four consecutive keys.
+// keys x D.  Rows are padded so that the operand reads below hit distinct banks of the
+// 64-bank LDS: K by 16 bytes (the 16 rows a b128 read touches start 4 banks apart), V by
+// 64 bytes (the four rows of a transposing read start 16 or 48 banks apart, so the two
+// 16-lane groups reading 32 bytes each from them never share a bank).  Rows of a 32-key
+// K sub-tile are stored with bits 2 and 3 of the row index swapped (perm5), so that the
+// score accumulator of half h of the lanes holds keys 8h..8h+7 (registers 0..7) and
+// 16+8h..16+8h+7 (registers 8..15) -- runs of 8 consecutive keys, exactly the operand
+// layout P^T needs in the second product.  The V^T operand is read with the gfx950
+// transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i
+// receives element i mod 4 of the 8-byte pieces addressed by lanes 4e + i/4 (e = 0..3);
+// addressing V[key0 + e][d0 + 4q] from lane 4e + q therefore hands lane i the column
+// d0 + i of four consecutive keys.
 // ---------------------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -111,21 +129,27 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
 }
 
 template <int D, bool CAUSAL, bool MASK, bool POS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreadsBf16) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16(Args a) {
-  constexpr int DG = D / 8;                      // 16-byte chunks per row
-  constexpr int CH = kBlockN * DG / kThreads;    // chunks per thread per K (or V) tile
-  constexpr int ROWS_PER_PASS = kThreads / DG;   // tile rows covered by one chunk pass
-  constexpr int KP = 2 * D + 16;                 // K row pitch in LDS (bytes)
-  constexpr int VP = 2 * D + 32;                 // V row pitch in LDS (bytes)
-  constexpr int KT = kBlockN * KP;               // bytes of one K stage
-  constexpr int VT = kBlockN * VP;               // bytes of one V stage
-  static_assert(CH * kThreads == kBlockN * DG, "tile must split evenly over threads");
+  constexpr int BN = kBlockNBf16;
+  constexpr int NT = kThreadsBf16;
+  constexpr int DG = D / 8;                // 16-byte chunks per row
+  constexpr int CH = BN * DG / NT;         // chunks per thread per K (or V) tile
+  constexpr int ROWS = NT / DG;            // tile rows covered by one chunk pass
+  constexpr int KPRE = MASK ? 2 : 4;     // K fragments read ahead of each matrix phase
+  constexpr int KP = k_pitch_bf16(D);      // K row pitch in LDS (bytes)
+  constexpr int VP = v_pitch_bf16(D);      // V row pitch in LDS (bytes)
+  constexpr int KT = BN * KP;              // bytes of one K stage
+  constexpr int VT = BN * VP;              // bytes of one V stage
+  static_assert(CH * NT == BN * DG, "tile must split evenly over the workgroup");
+  static_assert(2 * KT + 2 * VT == lds_bytes_bf16(D), "plan and kernel disagree on LDS");
   __shared__ __attribute__((aligned(16))) char lds[2 * KT + 2 * VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = tid >> 6;        // 0..7; SIMD = wave % 4
+  const int grp = wave >> 2;        // phase group
+  const int slice = 2 * (wave & 3) + grp;  // 32-row slice of the workgroup's rows
   const int li = lane & 31;
   const int hf = lane >> 5;
 
@@ -138,9 +162,9 @@ void fwd_bf16(Args a) {
   uint16_t* ob = static_cast<uint16_t*>(a.out) + b * a.so[0] + h * a.so[1];
   const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
 
-  const int q0 = int(qt) * kBlockM;
-  const int qw = q0 + wave * 32;  // first query row of this wave
-  const int qi = qw + li;         // this lane's query row
+  const int q0 = int(qt) * kBlockMBf16;
+  const int qw = q0 + 32 * slice;  // first query row of this wave
+  const int qi = qw + li;          // this lane's query row
   const bool q_ok = qi < a.Lq;
   const bool wave_live = qw < a.Lq;
 
@@ -157,13 +181,17 @@ void fwd_bf16(Args a) {
   // memory-counter wait in the key loop cover the K/V prefetch as well.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // Keys that can be visible to some stored row of this workgroup.
+  // Key tiles the workgroup stages (keys that can be visible to some stored row), and
+  // the tiles this wave computes on (with a causal mask: tiles 0 .. (qw + 31) / 64).
   int kend = a.Lk;
-  if (CAUSAL) kend = min(kend, min(q0 + kBlockM, a.Lq));
-  const int ntiles = (kend + kBlockN - 1) / kBlockN;
+  if (CAUSAL) kend = min(kend, min(q0 + kBlockMBf16, a.Lq));
+  const int ntiles = (kend + BN - 1) / BN;
+  const int wtiles = !wave_live ? 0 : CAUSAL ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
 
   // ---- global -> register -> LDS staging of K and V tiles (buffer loads: rows past
-  // the end of the head read as zero) ----
+  // the end of the head read as zero).  All 512 threads stage: the loads of K(t+1) and
+  // V(t) are issued at the start of step t, K(t+1) is written to LDS at the end of phase
+  // A and V(t) at the end of phase B, so each phase carries half of the store traffic. ----
   const int k_rowb = int(a.sk[2]) * 2, v_rowb = int(a.sv[2]) * 2;  // row strides, bytes
   const int k_ext = a.Lk > 0 ? (a.Lk - 1) * k_rowb + 2 * D : 0;
   const int v_ext = a.Lk > 0 ? (a.Lk - 1) * v_rowb + 2 * D : 0;
@@ -178,30 +206,31 @@ void fwd_bf16(Args a) {
   auto load_k = [&](int t) {
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_goff + p * ROWS_PER_PASS * k_rowb,
-                                                       t * kBlockN * k_rowb, 0);
+      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_goff + p * ROWS * k_rowb,
+                                                       t * BN * k_rowb, 0);
   };
   auto load_v = [&](int t) {
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_goff + p * ROWS_PER_PASS * v_rowb,
-                                                       t * kBlockN * v_rowb, 0);
+      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_goff + p * ROWS * v_rowb,
+                                                       t * BN * v_rowb, 0);
   };
-  auto store_k = [&](int s) {
+  auto store_k = [&](int st) {
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      *reinterpret_cast<u32x4*>(lds + s * KT + k_soff + p * ROWS_PER_PASS * KP) = kreg[p];
+      *reinterpret_cast<u32x4*>(lds + st * KT + k_soff + p * ROWS * KP) = kreg[p];
   };
-  auto store_v = [&](int s) {
+  auto store_v = [&](int st) {
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      *reinterpret_cast<u32x4*>(lds + 2 * KT + s * VT + v_soff + p * ROWS_PER_PASS * VP) = vreg[p];
+      *reinterpret_cast<u32x4*>(lds + 2 * KT + st * VT + v_soff + p * ROWS * VP) = vreg[p];
   };
 
   // Per-lane operand addresses (stage and tile offsets are immediates).
   const int kfrag = li * KP + hf * 16;
   const int g16 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
   const int vfrag = (8 * (g16 >> 1) + e4) * VP + (16 * (g16 & 1) + 4 * q4) * 2;
+  const float c2 = POS ? a.scale_log2 : 1.f;
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -210,28 +239,95 @@ void fwd_bf16(Args a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m_ref = -INFINITY;  // exponent reference (base-2 units), may lag the row max
   float l_run = 0.f;        // sum of 2^(x - m_ref) over this lane's key half
-  const float c2 = POS ? a.scale_log2 : 1.f;
+  f32x16 s[2];              // scores of tile t; sub-tile kt, register r = key
+                            // 32kt + 16(r/8) + 8hf + r%8
+  bf16x8 pf[4];             // P^T operand of tile t: chunk c = keys 16c + 8hf .. +7
+  bf16x8 kpre[KPRE];        // first K fragments of the next S, read ahead in the vector phase
 
-  if (ntiles > 0) {
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-  }
-  __syncthreads();
+  // The first KPRE K fragments of tile t's S, read at the end of the vector phase that
+  // precedes M(t) (K(t) is staged by then), so M(t) starts on the matrix cores at once.
+  auto prefetch_k = [&](int t) {
+    if (t >= wtiles) return;
+    const char* kfp = lds + (t & 1) * KT + kfrag;
+#pragma unroll
+    for (int c = 0; c < KPRE; ++c) kpre[c] = __builtin_bit_cast(bf16x8, ld16(kfp + c * 32));
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int stg = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      load_k(t + 1);
-      load_v(t + 1);
+  // Matrix phase M(t): S^T(t) = K(t) Q^T, then O^T += V^T(t-1) P^T(t-1).  It runs at
+  // raised wave priority: the wave of the other group on this SIMD issues a dense
+  // stream of independent vector instructions, and without priority it would take every
+  // issue slot and hold the matrix products back.
+  auto mphase = [&](int t) {
+    __builtin_amdgcn_s_setprio(1);
+    if (t < wtiles) {
+      const char* kfp = lds + (t & 1) * KT + kfrag;
+      bf16x8 kf[2][D / 16];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          kf[kt][c] = (kt == 0 && c < KPRE)
+                          ? kpre[c]
+                          : __builtin_bit_cast(bf16x8, ld16(kfp + kt * 32 * KP + c * 32));
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][c], qf[c], s[kt], 0, 0, 0);
+      }
+      // The rest of the first sub-tile's reads, then its products interleaved with the
+      // second sub-tile's reads, then the second sub-tile's products.
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, D / 16 - KPRE, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, D / 16, 0);
     }
-    const int k0 = t * kBlockN;
-    // Wave-uniform: does any key of this tile reach any row of this wave?
-    const bool tile_live = wave_live && (!CAUSAL || k0 <= qw + 31);
+    if (t >= 1 && t - 1 < wtiles) {
+      // the V^T operand of key chunk c comes from two transposing reads (keys
+      // 16c + 8hf + 0..3 and + 4..7, head dims 32dt + li)
+      const char* vfp = lds + 2 * KT + ((t - 1) & 1) * VT + vfrag;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const s16x4 lo = ds_read_tr(vfp + (16 * c) * VP + 64 * dt);
+          const s16x4 hi = ds_read_tr(vfp + (16 * c + 4) * VP + 64 * dt);
+          const s16x4 both[2] = {lo, hi};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[dt], 0, 0, 0);
+        }
+      // Keep LDS reads ahead of the products: the first 8 reads, then one product per
+      // two reads, then the remaining products.
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * (D / 32) * 4 / 2 - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-    if (tile_live) {
+  // Vector phase V(t): the online softmax of S(t) into P(t).
+  auto vphase = [&](int t) {
+    if (t < 0 || t >= wtiles) return;
+    const int k0 = t * BN;
+    // Scores in the comparison domain: raw q.k when the scale is positive (the scale is
+    // folded into the exponent), else scale * q.k.  Invisible keys -> -inf.
+    if (!POS) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] *= a.scale_log2;
+    }
+    const bool edge = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > a.Lk);
+    if (edge || MASK) {
       // Mask bytes of this lane's keys: runs of 8 at k0 + 32kt + 16g + 8hf.
       uint64_t mbits[4] = {~0ull, ~0ull, ~0ull, ~0ull};
       if (MASK && q_ok) {
@@ -249,102 +345,79 @@ void fwd_bf16(Args a) {
           }
         }
       }
-
-      // S^T = K . Q^T for the two 32-key sub-tiles (all fragment reads of a sub-tile
-      // are issued before its products).
-      const char* kfp = lds + stg * KT + kfrag;
-      f32x16 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        bf16x8 kf[D / 16];
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-          kf[c] = __builtin_bit_cast(bf16x8, ld16(kfp + kt * 32 * KP + c * 32));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c], qf[c], s[kt], 0, 0, 0);
-      }
-
-      // Scores in the comparison domain: raw q.k when the scale is positive (the scale
-      // is folded into the exponent), else scale * q.k.  Invisible keys -> -inf.
-      if (!POS) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kt][r] *= a.scale_log2;
-      }
-      const bool edge = (CAUSAL && k0 + kBlockN - 1 > qw) || (k0 + kBlockN > a.Lk);
-      if (edge || MASK) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
-            bool hide = key >= a.Lk;
-            if (CAUSAL) hide = hide || key > qi;
-            if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
-            if (hide) s[kt][r] = -INFINITY;
-          }
-      }
-
-      // Online softmax with a lagging reference: rescale O and l only when some row of
-      // the wave sees its max grow by more than kRescaleSlack.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
-      mx = pair_max(mx) * c2;  // base-2 units
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = m_ref == -INFINITY ? 0.f : exp2_fast(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-      float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(__builtin_fmaf(s[kt][r], c2, -mu));
-          s[kt][r] = p;
-          psum += p;
+          const int key = k0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
+          bool hide = key >= a.Lk;
+          if (CAUSAL) hide = hide || key > qi;
+          if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
+          if (hide) s[kt][r] = -INFINITY;
         }
-      l_run += psum;
-
-      // P^T operand: chunk c holds keys 16c + 8hf .. 16c + 8hf + 7 of this lane's row.
-      bf16x8 pf[4];
+    }
+    // Online softmax with a lagging reference: rescale O and l only when some row of the
+    // wave sees its max grow by more than kRescaleSlack.
+    float mx = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) pf[c][u] = static_cast<__bf16>(s[c >> 1][8 * (c & 1) + u]);
-
-      // O^T += V^T . P^T ; the V^T operand of key chunk c comes from two transposing
-      // reads (keys 16c + 8hf + 0..3 and + 4..7, head dims 32dt + li).
-      const char* vfp = lds + 2 * KT + stg * VT + vfrag;
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+    mx = pair_max(mx) * c2;  // base-2 units
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_ref == -INFINITY ? 0.f : exp2_fast(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const s16x4 lo = ds_read_tr(vfp + (16 * c) * VP + 64 * dt);
-          const s16x4 hi = ds_read_tr(vfp + (16 * c + 4) * VP + 64 * dt);
-          const s16x4 both[2] = {lo, hi};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[dt], 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
+    const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(__builtin_fmaf(s[kt][r], c2, -mu));
+        psum += p;
+        pf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(p);
+      }
+    l_run += psum;
+  };
 
-    if (more) {
-      store_k(stg ^ 1);
-      store_v(stg ^ 1);
+  // ---- two-phase pipeline over key tiles ----
+  // Step t:  phase A: group 0 runs M(t); group 1 runs V(t-1) and reads ahead for its M(t);
+  //                   then every thread writes K(t+1) to LDS
+  //          phase B: group 0 runs V(t) and reads ahead for M(t+1); group 1 runs M(t);
+  //                   then every thread writes V(t) to LDS
+  // M(t) reads K(t) (stage t&1) and V(t-1) (stage (t-1)&1); K(t+1) and V(t) go to the
+  // other stages, whose previous tiles step t-1 finished with.
+  if (ntiles > 0) {
+    load_k(0);
+    store_k(0);
+  }
+  __syncthreads();
+  if (grp == 0) prefetch_k(0);
+  for (int t = 0; t <= ntiles; ++t) {
+    if (t + 1 < ntiles) load_k(t + 1);
+    if (t < ntiles) load_v(t);
+    if (grp == 0) {
+      mphase(t);
+    } else {
+      vphase(t - 1);
+      prefetch_k(t);
     }
+    if (t + 1 < ntiles) store_k((t + 1) & 1);
+    __syncthreads();
+    if (grp == 0) {
+      vphase(t);
+      prefetch_k(t + 1);
+    } else {
+      mphase(t);
+    }
+    if (t < ntiles) store_v(t & 1);
     __syncthreads();
   }
 
@@ -379,14 +452,14 @@ void fwd_bf16(Args a) {
 // products; same decomposition as the bf16 kernel, probabilities stay fp32.
 // ---------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreads) void fwd_f32(Args a) {
+__global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   constexpr int DG = D / 4;                             // 16-byte groups per row
-  constexpr int CH = kBlockN * DG / kThreads;           // chunks per thread per tile
+  constexpr int CH = kBlockNF32 * DG / kThreadsF32;           // chunks per thread per tile
   constexpr int KROW = D + 1;                           // odd pitch: conflict-free column reads
-  constexpr int K_ELEMS = kBlockN * KROW;
-  constexpr int V_ELEMS = kBlockN * D;
+  constexpr int K_ELEMS = kBlockNF32 * KROW;
+  constexpr int V_ELEMS = kBlockNF32 * D;
   constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static_assert(CH * kThreads == kBlockN * DG, "tile must split evenly over threads");
+  static_assert(CH * kThreadsF32 == kBlockNF32 * DG, "tile must split evenly over threads");
   __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -404,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32(Args a) {
   float* ob = static_cast<float*>(a.out) + b * a.so[0] + h * a.so[1];
   const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
 
-  const int q0 = int(qt) * kBlockM;
+  const int q0 = int(qt) * kBlockMF32;
   const int qw = q0 + wave * 32;
   const int qi = qw + li;
   const bool q_ok = qi < a.Lq;
@@ -416,15 +489,15 @@ __global__ __launch_bounds__(kThreads) void fwd_f32(Args a) {
   for (int c = 0; c < D / 2; ++c) qf[c] = q_ok ? qb[int64_t(qi) * a.sq[2] + 2 * c + hf] : 0.f;
 
   int kend = a.Lk;
-  if (CAUSAL) kend = min(kend, min(q0 + kBlockM, a.Lq));
-  const int ntiles = (kend + kBlockN - 1) / kBlockN;
+  if (CAUSAL) kend = min(kend, min(q0 + kBlockMF32, a.Lq));
+  const int ntiles = (kend + kBlockNF32 - 1) / kBlockNF32;
 
   u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int t) {
-    const int k0 = t * kBlockN;
+    const int k0 = t * kBlockNF32;
 #pragma unroll
     for (int p = 0; p < CH; ++p) {
-      const int c = tid + p * kThreads;
+      const int c = tid + p * kThreadsF32;
       const int row = c / DG, col = (c % DG) * 4;
       const int key = k0 + row;
       const bool ok = key < a.Lk;
@@ -437,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32(Args a) {
     float* vs = ks + K_ELEMS;
 #pragma unroll
     for (int p = 0; p < CH; ++p) {
-      const int c = tid + p * kThreads;
+      const int c = tid + p * kThreadsF32;
       const int row = c / DG, col = (c % DG) * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ks[row * KROW + col + e] = __uint_as_float(kreg[p][e]);
@@ -464,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32(Args a) {
     if (t + 1 < ntiles) load_tile(t + 1);
     const float* ks = lds + buf * STAGE;
     const float* vs = ks + K_ELEMS;
-    const int k0 = t * kBlockN;
+    const int k0 = t * kBlockNF32;
     const bool tile_live = wave_live && (!CAUSAL || k0 <= qw + 31);
 
     if (tile_live) {
@@ -485,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32(Args a) {
       }
 
       float x[2][16];
-      const bool edge = (CAUSAL && k0 + kBlockN - 1 > qw) || (k0 + kBlockN > a.Lk);
+      const bool edge = (CAUSAL && k0 + kBlockNF32 - 1 > qw) || (k0 + kBlockNF32 > a.Lk);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -571,7 +644,7 @@ hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
                             : reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, false>);
   else
     fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK>);
-  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(block_threads(dtype)), args, 0, stream);
 }
 
 template <int D>
@@ -601,7 +674,7 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.H = int32_t(p.H);
   a.Lq = int32_t(p.Lq);
   a.Lk = int32_t(p.Lk);
-  a.q_tiles = int32_t((p.Lq + kBlockM - 1) / kBlockM);
+  a.q_tiles = int32_t((p.Lq + block_m(p.dtype) - 1) / block_m(p.dtype));
   a.bh_count = int32_t(p.B * p.H);
   a.scale_log2 = p.scale * kLog2e;
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&

@@ -7,12 +7,20 @@
 
 namespace sdpa {
 
-// Tile shape of the bf16 and fp32 kernels: 4 waves of 64 lanes, each wave owning 32
-// query rows, so a workgroup owns 128 query rows and steps through 64 keys at a time.
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBlockM = 32 * kWaves;
-constexpr int kBlockN = 64;
+// Tile shapes.  bf16 kernel: a workgroup is 8 waves of 64 lanes, each wave owns 32 query
+// rows (256 per workgroup), keys advance 64 at a time; the waves form two groups that
+// alternate between matrix and vector phases.  fp32 kernel: 4 waves, 32 rows each (128
+// per workgroup), 64 keys at a time.
+constexpr int kThreadsBf16 = 512;
+constexpr int kBlockMBf16 = 256;
+constexpr int kBlockNBf16 = 64;
+constexpr int kThreadsF32 = 256;
+constexpr int kBlockMF32 = 128;
+constexpr int kBlockNF32 = 64;
+// dtype: 1 = bf16, 0 = fp32 (the values of sdpa_dtype)
+constexpr int block_m(int dtype) { return dtype == 1 ? kBlockMBf16 : kBlockMF32; }
+constexpr int block_n(int dtype) { return dtype == 1 ? kBlockNBf16 : kBlockNF32; }
+constexpr int block_threads(int dtype) { return dtype == 1 ? kThreadsBf16 : kThreadsF32; }
 
 // Rank-3 [N,L,D] and rank-4 [B,H,L,D] inputs both become this (b, h, row, col) view;
 // every stride is in elements of the tensor's own type.
@@ -42,12 +50,15 @@ __host__ __device__ inline void decode_item(int64_t block, int64_t bh_count, int
   *q_tile = causal ? (q_tiles - 1 - rank) : rank;
 }
 
-// LDS bytes per workgroup of each kernel (two stages of K and V tiles).
+// LDS row pitches (bytes) of the bf16 kernel's K and V tiles, and LDS bytes per
+// workgroup of each kernel (two stages of K and two of V).
+constexpr int k_pitch_bf16(int D) { return 2 * D + 16; }
+constexpr int v_pitch_bf16(int D) { return 2 * D + 64; }
 constexpr int64_t lds_bytes_bf16(int D) {
-  return 2 * (int64_t(kBlockN) * (D + 8) * 2 + int64_t(D) * kBlockN * 2);
+  return 2 * int64_t(kBlockNBf16) * (k_pitch_bf16(D) + v_pitch_bf16(D));
 }
 constexpr int64_t lds_bytes_f32(int D) {
-  return 2 * (int64_t(kBlockN) * (D + 1) * 4 + int64_t(kBlockN) * D * 4);
+  return 2 * (int64_t(kBlockNF32) * (D + 1) * 4 + int64_t(kBlockNF32) * D * 4);
 }
 
 // Launches the kernel matching p.dtype / p.D / p.causal / mask on `stream`.
