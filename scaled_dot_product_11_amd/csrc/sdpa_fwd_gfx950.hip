@@ -11,17 +11,18 @@
 // backend's safe softmax).
 //
 // Work decomposition (bf16 and fp32 kernels alike):
-//   * a workgroup is 4 waves of 64 lanes and owns 128 query rows of one (b, h);
-//   * each wave owns 32 query rows; lane l serves query row (l % 32) and half h = l / 32
-//     of every key tile, so all per-row softmax state (running max m, running sum l,
-//     rescale factor) is a per-lane scalar;
+//   * a workgroup owns a tile of query rows of one (b, h): 256 rows in 8 waves (bf16) or
+//     128 rows in 4 waves (fp32); each wave owns 32 query rows;
+//   * lane l serves query row (l % 32) and half h = l / 32 of every key tile, so all
+//     per-row softmax state (running max, running sum, rescale factor) is a per-lane
+//     scalar;
 //   * the scores are computed transposed, S^T = K . Q^T, on 32x32 MFMA tiles: the
 //     accumulator of a 32x32 tile gives each lane 16 keys of its own query row;
 //   * the output is accumulated transposed, O^T += V^T . P^T, so P^T comes straight from
-//     the score registers (rounded to bf16) and each lane again owns its query's column;
-//   * K and V tiles of 64 keys are double-buffered through LDS: the global loads of tile
-//     t+1 are issued before the matrix work on tile t and written to the other LDS stage
-//     after it, with one barrier per tile.
+//     the score registers and each lane again owns its query's column;
+//   * K and V tiles of 64 keys are double-buffered through LDS: the global loads of the
+//     next tiles are issued before the matrix work on the current ones and written to
+//     the other LDS stage after it.
 #include <math.h>
 
 #include "sdpa_internal.h"
@@ -117,6 +118,8 @@ __device__ inline int perm5(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 
 // ---------------------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // The running max used as the exponent reference may lag the true row max by up to this
 // many base-2 units before O and l are rescaled: p = 2^(x - m_ref) then stays <= 256,
@@ -188,10 +191,16 @@ void fwd_bf16(Args a) {
   const int ntiles = (kend + BN - 1) / BN;
   const int wtiles = !wave_live ? 0 : CAUSAL ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
 
-  // ---- global -> register -> LDS staging of K and V tiles (buffer loads: rows past
-  // the end of the head read as zero).  All 512 threads stage: the loads of K(t+1) and
-  // V(t) are issued at the start of step t, K(t+1) is written to LDS at the end of phase
-  // A and V(t) at the end of phase B, so each phase carries half of the store traffic. ----
+  // ---- global -> register -> LDS staging of K and V tiles.  All 512 threads stage: the
+  // loads of K(t+1) and V(t) are issued at the start of step t, K(t+1) is written to LDS
+  // at the end of phase A and V(t) at the end of phase B, so each phase carries half of
+  // the store traffic.  The loads are buffer loads whose whole byte offset (tile, row and
+  // column) is in the per-lane offset, which the hardware checks against the buffer's
+  // extent: rows past the end of the head read as zero, and tiles past the staged range
+  // are given an offset beyond the extent, so they read zeros without touching memory.
+  // Loads and stores are therefore unconditional, and the memory-counter waits before
+  // the stores are exact.  Offsets stay below 2^31: the caller guarantees that
+  // (Lk + 64) rows of K and of V span less than 2 GiB. ----
   const int k_rowb = int(a.sk[2]) * 2, v_rowb = int(a.sv[2]) * 2;  // row strides, bytes
   const int k_ext = a.Lk > 0 ? (a.Lk - 1) * k_rowb + 2 * D : 0;
   const int v_ext = a.Lk > 0 ? (a.Lk - 1) * v_rowb + 2 * D : 0;
@@ -204,16 +213,16 @@ void fwd_bf16(Args a) {
   const int v_soff = ld_row * VP + ld_col * 16;
   u32x4 kreg[CH], vreg[CH];
   auto load_k = [&](int t) {
+    const int base = k_goff + (t < ntiles ? t * BN * k_rowb : k_ext);
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_goff + p * ROWS * k_rowb,
-                                                       t * BN * k_rowb, 0);
+      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + p * ROWS * k_rowb, 0, 0);
   };
   auto load_v = [&](int t) {
+    const int base = v_goff + (t < ntiles ? t * BN * v_rowb : v_ext);
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_goff + p * ROWS * v_rowb,
-                                                       t * BN * v_rowb, 0);
+      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, base + p * ROWS * v_rowb, 0, 0);
   };
   auto store_k = [&](int st) {
 #pragma unroll
@@ -357,12 +366,12 @@ void fwd_bf16(Args a) {
         }
     }
     // Online softmax with a lagging reference: rescale O and l only when some row of the
-    // wave sees its max grow by more than kRescaleSlack.
-    float mx = -INFINITY;
+    // wave sees its max grow by more than kRescaleSlack.  The lane's 32 scores are
+    // reduced by a chain of 3-input maxima (v_max3_f32).
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kt][r], s[kt][r + 1]));
+    for (int i = 2; i < 32; i += 2)
+      mx = fmaxf(fmaxf(mx, s[i >> 4][i & 15]), s[i >> 4][(i + 1) & 15]);
     mx = pair_max(mx) * c2;  // base-2 units
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
       const float m_new = fmaxf(m_ref, mx);
@@ -375,16 +384,23 @@ void fwd_bf16(Args a) {
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-    float psum = 0.f;
+    // p = 2^(x - mu), rounded to bf16 two at a time into the P^T operand.  The row sum
+    // adds the fp32 values (the lse needs them unrounded) in two independent chains.
+    float ps[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int c = 0; c < 4; ++c) {
+      u32x4 w;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(__builtin_fmaf(s[kt][r], c2, -mu));
-        psum += p;
-        pf[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(p);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * (c & 1) + 2 * e;
+        const f32x2 pp = {exp2_fast(__builtin_fmaf(s[c >> 1][r], c2, -mu)),
+                          exp2_fast(__builtin_fmaf(s[c >> 1][r + 1], c2, -mu))};
+        ps[c & 1] = c < 2 && e == 0 ? pp[0] + pp[1] : ps[c & 1] + pp[0] + pp[1];
+        w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
       }
-    l_run += psum;
+      pf[c] = __builtin_bit_cast(bf16x8, w);
+    }
+    l_run += ps[0] + ps[1];
   };
 
   // ---- two-phase pipeline over key tiles ----
@@ -394,22 +410,20 @@ void fwd_bf16(Args a) {
   //                   then every thread writes V(t) to LDS
   // M(t) reads K(t) (stage t&1) and V(t-1) (stage (t-1)&1); K(t+1) and V(t) go to the
   // other stages, whose previous tiles step t-1 finished with.
-  if (ntiles > 0) {
-    load_k(0);
-    store_k(0);
-  }
+  load_k(0);
+  store_k(0);
   __syncthreads();
   if (grp == 0) prefetch_k(0);
   for (int t = 0; t <= ntiles; ++t) {
-    if (t + 1 < ntiles) load_k(t + 1);
-    if (t < ntiles) load_v(t);
+    load_k(t + 1);
+    load_v(t);
     if (grp == 0) {
       mphase(t);
     } else {
       vphase(t - 1);
       prefetch_k(t);
     }
-    if (t + 1 < ntiles) store_k((t + 1) & 1);
+    store_k((t + 1) & 1);
     __syncthreads();
     if (grp == 0) {
       vphase(t);
@@ -417,7 +431,7 @@ void fwd_bf16(Args a) {
     } else {
       mphase(t);
     }
-    if (t < ntiles) store_v(t & 1);
+    store_v(t & 1);
     __syncthreads();
   }
 
