@@ -34,8 +34,8 @@ METRIC = "causal SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=12
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
 # kernel source they were taken on (sha256 prefix below); reported as null otherwise.
-TRAFFIC_BYTES = 549138 * 1024
-TRAFFIC_KERNEL_SHA256 = "185175e18b4da2d4"
+TRAFFIC_BYTES = 484244 * 1024
+TRAFFIC_KERNEL_SHA256 = "e61d876b7a1cce9d"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 
 
