@@ -51,6 +51,13 @@ def _load():
             ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
             ctypes.c_void_p, i64p,
             ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64, dp, dp, ctypes.c_int]
+        lib.oracle_sdpa_bwd.restype = ctypes.c_int
+        lib.oracle_sdpa_bwd.argtypes = [
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64,
+            ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
+            ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
+            ctypes.c_int, ctypes.c_double, dp, dp, dp, ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -71,6 +78,68 @@ def _strides4(t):
     """(b, h, row, d) element strides of a rank-3 or rank-4 tensor (rank 3 -> B = 1)."""
     s = t.stride()
     return (0,) + tuple(s) if t.dim() == 3 else tuple(s)
+
+
+def _check_qkv(q, k, v):
+    for t in (q, k, v):
+        if t.device.type != "cpu":
+            raise ValueError("the oracle reads host memory; move tensors to the CPU first")
+    if not (q.dim() == k.dim() == v.dim() and q.dim() in (3, 4)):
+        raise ValueError("q, k, v must all be rank 3 or all rank 4")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float64")
+    if q.dim() == 3:
+        B, H, Lq, D = 1, q.shape[0], q.shape[1], q.shape[2]
+        Lk = k.shape[1]
+    else:
+        B, H, Lq, D = q.shape
+        Lk = k.shape[2]
+    if tuple(k.shape) != tuple(q.shape[:-2]) + (Lk, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must have q's leading dims, the same length Lk and head dim")
+    return B, H, Lq, Lk, D
+
+
+def _mask_args(mask, q, Lk):
+    """(pointer, strides array, keep-alive tensor) of a bool/uint8 mask expanded to q's rows."""
+    if mask is None:
+        return None, None, None
+    mask_t = _as_tensor(mask).expand(tuple(q.shape[:-1]) + (Lk,))
+    if mask_t.dtype == torch.bool:
+        mask_t = mask_t.view(torch.uint8)
+    if mask_t.dtype != torch.uint8:
+        raise ValueError("mask must be bool or uint8")
+    return ctypes.c_void_p(mask_t.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(mask_t)), mask_t
+
+
+def sdpa_bwd_oracle(q, k, v, dout, *, mask=None, is_causal=False, scale=None, nthreads=0):
+    """Gradients (dq, dk, dv) of out = sdpa(q, k, v) for the upstream gradient dout, in fp64.
+
+    Same tensor conventions as sdpa_oracle; dout has q's shape and dtype.  Returns float64
+    numpy arrays shaped like q, k and v.  Fully masked query rows contribute nothing.
+    """
+    q, k, v, dout = _as_tensor(q), _as_tensor(k), _as_tensor(v), _as_tensor(dout)
+    B, H, Lq, Lk, D = _check_qkv(q, k, v)
+    if tuple(dout.shape) != tuple(q.shape) or dout.dtype != q.dtype or dout.device.type != "cpu":
+        raise ValueError("dout must be a CPU tensor with q's shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    mptr, ms_arr, _keep = _mask_args(mask, q, Lk)
+    dq = np.zeros((B * H * Lq, D), dtype=np.float64)
+    dk = np.zeros((B * H * Lk, D), dtype=np.float64)
+    dv = np.zeros((B * H * Lk, D), dtype=np.float64)
+    st = _load().oracle_sdpa_bwd(
+        _DTYPE_CODE[q.dtype], B, H, Lq, Lk, D,
+        ctypes.c_void_p(q.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(q)),
+        ctypes.c_void_p(k.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(k)),
+        ctypes.c_void_p(v.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(v)),
+        ctypes.c_void_p(dout.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(dout)),
+        mptr, ms_arr, 1 if is_causal else 0, float(scale),
+        dq.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        dk.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        dv.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))
+    if st != 0:
+        raise RuntimeError(f"oracle_sdpa_bwd failed with status {st}")
+    return dq.reshape(tuple(q.shape)), dk.reshape(tuple(k.shape)), dv.reshape(tuple(v.shape))
 
 
 def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, nthreads=0):

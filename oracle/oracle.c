@@ -28,8 +28,14 @@
  * (max, then exp and sum), and the probabilities are normalised before the product
  * with V, exactly in the order the five steps give.
  *
+ * The backward (oracle_sdpa_bwd) is the derivative of the same function, written out with
+ * the chain rule through the five steps: none of the pages defines a backward, but its
+ * result is fixed by the forward; it is the step after the forward that the exported LSE
+ * exists for (the FlashInfer DSA article's fused forward returns `lse` for its backward).
+ *
  * Parity pins: see tests/test_oracle_*.py (brute force, closed forms, invariants,
- * hand-derived golden cases, the library's fp64 math-backend SDPA).
+ * hand-derived golden cases, the library's fp64 math-backend SDPA; for the backward,
+ * central finite differences of the forward oracle and the library's fp64 autograd).
  */
 #include <math.h>
 #include <stdint.h>
@@ -166,6 +172,119 @@ int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
     }
     free(s);
     free(p);
+  }
+  return status;
+}
+
+/*
+ * oracle_sdpa_bwd -- gradients of out = sdpa(q, k, v) for a given upstream gradient dout,
+ * one head at a time, whole [Lq, Lk] matrices in fp64:
+ *
+ *   S   = scale * q.k^T, hidden positions -inf       (the forward's steps 1-3)
+ *   P   = row softmax of S; a row with every key hidden is all zero (safe softmax)
+ *   dV  = P^T dout                                   (through step 5, out = P v)
+ *   dP  = dout v^T
+ *   dS  = P * (dP - rowsum(P * dP))                  (through step 4, the softmax Jacobian)
+ *   dQ  = scale * dS k                               (through steps 1-2)
+ *   dK  = scale * dS^T q
+ *
+ *   dtype, B..D, q/k/v and their strides, mask, is_causal, scale: as in oracle_sdpa_fwd
+ *   dout, dos    upstream gradient [B,H,Lq,D] of q's dtype, four element strides
+ *   dq           [B,H,Lq,D] doubles, row-major;  dk, dv: [B,H,Lk,D] doubles, row-major
+ *   nthreads     OpenMP threads over heads (<= 0: the runtime's default)
+ *
+ * Returns 0 on success, 1 on a bad argument, 2 if scratch memory could not be allocated.
+ */
+int oracle_sdpa_bwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                    const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                    const void* v, const int64_t* vs, const void* dout, const int64_t* dos,
+                    const uint8_t* mask, const int64_t* ms, int is_causal, double scale,
+                    double* dq, double* dk, double* dv, int nthreads) {
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return 1;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || D < 0) return 1;
+  if (!dq || !dk || !dv || !qs || !ks || !vs || !dos || (mask && !ms)) return 1;
+  int status = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const size_t mat = (size_t)(Lq > 0 ? Lq : 1) * (size_t)(Lk > 0 ? Lk : 1);
+#pragma omp parallel
+  {
+    double* P = (double*)malloc(sizeof(double) * mat);
+    double* dS = (double*)malloc(sizeof(double) * mat);
+    if (!P || !dS) {
+#pragma omp atomic write
+      status = 2;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+      if (!P || !dS) continue;
+      const int64_t b = bh / H, h = bh % H;
+      const int64_t qb = b * qs[0] + h * qs[1], kb = b * ks[0] + h * ks[1];
+      const int64_t vb = b * vs[0] + h * vs[1], ob = b * dos[0] + h * dos[1];
+      /* P: the forward's softmax, row by row */
+      for (int64_t i = 0; i < Lq; ++i) {
+        double* pr = P + i * Lk;
+        double m = -INFINITY;
+        int any = 0;
+        for (int64_t j = 0; j < Lk; ++j) {
+          if (!allowed(is_causal, mask, ms, b, h, i, j)) {
+            pr[j] = -INFINITY;
+            continue;
+          }
+          double dot = 0.0;
+          for (int64_t d = 0; d < D; ++d)
+            dot += load_elem(q, dtype, qb + i * qs[2] + d * qs[3]) *
+                   load_elem(k, dtype, kb + j * ks[2] + d * ks[3]);
+          pr[j] = scale * dot;
+          if (!any || pr[j] > m) m = pr[j];
+          any = 1;
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < Lk; ++j) {
+          pr[j] = (!any || pr[j] == -INFINITY) ? 0.0 : exp(pr[j] - m);
+          l += pr[j];
+        }
+        for (int64_t j = 0; j < Lk; ++j) pr[j] = any ? pr[j] / l : 0.0;
+      }
+      /* dP = dout v^T, then dS = P (dP - rowsum(P dP)) */
+      for (int64_t i = 0; i < Lq; ++i) {
+        double rowsum = 0.0;
+        for (int64_t j = 0; j < Lk; ++j) {
+          double dot = 0.0;
+          for (int64_t d = 0; d < D; ++d)
+            dot += load_elem(dout, dtype, ob + i * dos[2] + d * dos[3]) *
+                   load_elem(v, dtype, vb + j * vs[2] + d * vs[3]);
+          dS[i * Lk + j] = dot;
+          rowsum += P[i * Lk + j] * dot;
+        }
+        for (int64_t j = 0; j < Lk; ++j)
+          dS[i * Lk + j] = P[i * Lk + j] * (dS[i * Lk + j] - rowsum);
+      }
+      /* dV = P^T dout, dK = scale dS^T q */
+      for (int64_t j = 0; j < Lk; ++j)
+        for (int64_t d = 0; d < D; ++d) {
+          double av = 0.0, ak = 0.0;
+          for (int64_t i = 0; i < Lq; ++i) {
+            av += P[i * Lk + j] * load_elem(dout, dtype, ob + i * dos[2] + d * dos[3]);
+            ak += dS[i * Lk + j] * load_elem(q, dtype, qb + i * qs[2] + d * qs[3]);
+          }
+          dv[(bh * Lk + j) * D + d] = av;
+          dk[(bh * Lk + j) * D + d] = scale * ak;
+        }
+      /* dQ = scale dS k */
+      for (int64_t i = 0; i < Lq; ++i)
+        for (int64_t d = 0; d < D; ++d) {
+          double a = 0.0;
+          for (int64_t j = 0; j < Lk; ++j)
+            a += dS[i * Lk + j] * load_elem(k, dtype, kb + j * ks[2] + d * ks[3]);
+          dq[(bh * Lq + i) * D + d] = scale * a;
+        }
+    }
+    free(P);
+    free(dS);
   }
   return status;
 }

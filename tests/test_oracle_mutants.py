@@ -1,5 +1,6 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU) and check that the pins
-in test_oracle_pins.py reject every one of them.  The shipped oracle is never modified."""
+reject every one of them: forward mistakes by test_oracle_pins.py, backward mistakes by
+test_oracle_bwd_pins.py.  The shipped oracle is never modified."""
 import os
 import subprocess
 import sys
@@ -26,10 +27,37 @@ MUTANTS = {
     "bf16_decode_shift": ("<< 16", "<< 15"),
 }
 
+# backward: (anchor, replacement) in oracle_sdpa_bwd
+BWD_MUTANTS = {
+    "bwd_rowsum_sign": ("P[i * Lk + j] * (dS[i * Lk + j] - rowsum)",
+                        "P[i * Lk + j] * (dS[i * Lk + j] + rowsum)"),
+    "bwd_rowsum_dropped": ("P[i * Lk + j] * (dS[i * Lk + j] - rowsum)",
+                           "P[i * Lk + j] * dS[i * Lk + j]"),
+    "bwd_rowsum_without_p": ("rowsum += P[i * Lk + j] * dot;", "rowsum += dot;"),
+    "bwd_dk_scale_dropped": ("dk[(bh * Lk + j) * D + d] = scale * ak;",
+                             "dk[(bh * Lk + j) * D + d] = ak;"),
+    "bwd_dq_scale_dropped": ("dq[(bh * Lq + i) * D + d] = scale * a;",
+                             "dq[(bh * Lq + i) * D + d] = a;"),
+    "bwd_dk_from_dout": ("ak += dS[i * Lk + j] * load_elem(q, dtype, qb + i * qs[2] + d * qs[3]);",
+                         "ak += dS[i * Lk + j] * load_elem(dout, dtype, ob + i * dos[2] + d * dos[3]);"),
+    "bwd_dv_uses_ds": ("av += P[i * Lk + j] *", "av += dS[i * Lk + j] *"),
+    "bwd_dp_uses_k": ("load_elem(v, dtype, vb + j * vs[2] + d * vs[3]);",
+                      "load_elem(k, dtype, kb + j * ks[2] + d * ks[3]);"),
+    "bwd_dq_uses_v": ("a += dS[i * Lk + j] * load_elem(k, dtype, kb + j * ks[2] + d * ks[3]);",
+                      "a += dS[i * Lk + j] * load_elem(v, dtype, vb + j * vs[2] + d * vs[3]);"),
+    "bwd_p_unnormalised": ("pr[j] = any ? pr[j] / l : 0.0;", "pr[j] = any ? pr[j] : 0.0;"),
+    "bwd_empty_row_not_zeroed": ("pr[j] = any ? pr[j] / l : 0.0;", "pr[j] = pr[j] / l;"),
+    "bwd_dout_row_stride": ("ob + i * dos[2] + d * dos[3]) *", "ob + i * dos[3] + d * dos[3]) *"),
+}
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+
+ALL = {**{n: (o, r, "test_oracle_pins.py") for n, (o, r) in MUTANTS.items()},
+       **{n: (o, r, "test_oracle_bwd_pins.py") for n, (o, r) in BWD_MUTANTS.items()}}
+
+
+@pytest.mark.parametrize("name", sorted(ALL))
 def test_pins_reject_mutant(name, tmp_path):
-    old, new = MUTANTS[name]
+    old, new, pins = ALL[name]
     src = open(SRC).read()
     assert old in src, f"mutation anchor for {name} no longer matches oracle.c"
     mutant_c = tmp_path / "oracle_mutant.c"
@@ -39,6 +67,6 @@ def test_pins_reject_mutant(name, tmp_path):
                     str(mutant_c), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"pins accepted the mutant {name}:\n{r.stdout[-2000:]}"
