@@ -1,5 +1,6 @@
 /*
- * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product-attention forward.
+ * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product attention: the forward
+ * (sdpa_fwd) and its gradients (sdpa_bwd).
  *
  * The operation ("Profiling in PyTorch (part 3): attention", naive causal attention
  * section, five steps; SDPA section, the one-call form that takes a mask or a causal
@@ -109,6 +110,62 @@ int sdpa_check(const void* q, const void* k, const void* v, const void* out, con
 
 /* sdpa_strerror -- a static, human-readable message for a status code. */
 const char* sdpa_strerror(int status);
+
+/*
+ * sdpa_bwd -- gradients dq, dk, dv of sdpa_fwd for an upstream gradient dout, bf16 only.
+ *
+ * The derivative of the forward above by the chain rule through its steps (the pages
+ * define no backward; the forward's exported lse is what it reuses, as the fused
+ * forward of "Optimizing DeepSeek Sparse Attention with FlashInfer" returns its lse):
+ *
+ *   P[i,j]  = exp(scale * q_i.k_j - lse[i]) for visible (i,j), else 0  (all 0 if lse = -inf)
+ *   dv[j,:] = sum_i P[i,j] dout[i,:]
+ *   dP[i,j] = dout[i,:].v[j,:],   delta[i] = sum_d dout[i,d] out[i,d]  (= sum_j P[i,j] dP[i,j])
+ *   dS[i,j] = P[i,j] (dP[i,j] - delta[i])
+ *   dq[i,:] = scale * sum_j dS[i,j] k[j,:],   dk[j,:] = scale * sum_i dS[i,j] q[i,:]
+ *
+ * P and dS are rounded to bf16 (nearest-even) before their products; every product
+ * accumulates in fp32, and dq, dk, dv are rounded to bf16 once at the end.  Deterministic:
+ * no atomics, every output element is written by exactly one lane.  A query row with no
+ * visible key gets dq = 0 and contributes nothing to dk, dv; a key seen by no query gets
+ * dk = dv = 0.
+ *
+ *   q, k, v, out, dout, dq, dk, dv
+ *                 device pointers to bf16.  q, out, dout, dq are [B,H,Lq,D] / [N,Lq,D];
+ *                 k, v, dk, dv are [B,H,Lk,D] / [N,Lk,D]; any layout with unit innermost
+ *                 stride.  Bases and non-innermost strides (in bytes) multiples of 16.
+ *                 dq, dk, dv must not overlap each other or any input.  q/out/dout/dq
+ *                 may be NULL when B*H*Lq == 0, k/v/dk/dv when B*H*Lk == 0.
+ *   lse           device pointer to the B*H*Lq contiguous floats sdpa_fwd wrote for this
+ *                 same problem (natural log, -inf for empty rows); required when
+ *                 B*H*Lq > 0.
+ *   delta         device pointer to B*H*Lq contiguous floats of caller-owned scratch,
+ *                 4-byte aligned; receives delta[i] above (fp32).  Required when
+ *                 B*H*Lq > 0.
+ *   rank, B..D    as in sdpa_fwd (D in {64, 128}); additionally (Lq + 64) times the row
+ *                 stride of q (and of dout) must stay below 2 GiB.
+ *   strides       9*rank element strides, tensor-major: q, k, v, out, dout, dq, dk, dv,
+ *                 mask, each in its own axis order as in sdpa_fwd.
+ *   scale, is_causal, mask
+ *                 exactly as passed to sdpa_fwd.
+ *   dtype         SDPA_BF16 (anything else: SDPA_ERR_DTYPE).
+ *   stream        a hipStream_t (NULL = the null stream of the current device).
+ *
+ * Launches two kernels on `stream` (dq and delta first, then dk and dv); allocates,
+ * frees and synchronises nothing.  Ownership and errors as for sdpa_fwd.
+ */
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta, int rank, int64_t B,
+             int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+             int is_causal, const uint8_t* mask, int dtype, void* stream);
+
+/* sdpa_bwd_check -- the host-side validation of sdpa_bwd alone (no stream, no HIP call,
+ * no device read).  Returns the status sdpa_bwd would return before launching. */
+int sdpa_bwd_check(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, const void* dq, const void* dk,
+                   const void* dv, const float* delta, int rank, int64_t B, int64_t H,
+                   int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                   int is_causal, const uint8_t* mask, int dtype);
 
 /*
  * Launch plan (host-only introspection of the tile scheduler).

@@ -1,12 +1,12 @@
-"""MI355X-native fused scaled-dot-product-attention forward.
+"""MI355X-native fused scaled-dot-product attention: forward and gradients.
 
-The computation runs in one hand-written HIP kernel for gfx950 behind the C ABI declared in
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI declared in
 include/sdpa.h; this package is its thin Python binding (names mirror the C entry points).
 """
 from ._binding import (EXPORTS, LIB_PATH, SDPA_BF16, SDPA_F32, STATUS_NAMES, SdpaError, SdpaPlan,
-                       load_library, sdpa_check, sdpa_fwd, sdpa_plan, sdpa_plan_item,
-                       sdpa_strerror)
+                       load_library, sdpa_bwd, sdpa_bwd_check, sdpa_check, sdpa_fwd, sdpa_plan,
+                       sdpa_plan_item, sdpa_strerror)
 
-__all__ = ["sdpa_fwd", "sdpa_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item", "SdpaError",
+__all__ = ["sdpa_fwd", "sdpa_check", "sdpa_bwd", "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item", "SdpaError",
            "SdpaPlan", "SDPA_F32", "SDPA_BF16", "STATUS_NAMES", "LIB_PATH", "EXPORTS",
            "load_library"]

@@ -22,7 +22,8 @@ STATUS_NAMES = {
     8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE",
 }
 
-EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
+EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_bwd", "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan",
+           "sdpa_plan_item")
 
 
 class SdpaError(RuntimeError):
@@ -58,6 +59,12 @@ def load_library():
     lib.sdpa_fwd.restype = ctypes.c_int
     lib.sdpa_check.argtypes = common
     lib.sdpa_check.restype = ctypes.c_int
+    bwd_common = [vp] * 10 + [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.POINTER(i64),
+                              ctypes.c_float, ctypes.c_int, vp, ctypes.c_int]
+    lib.sdpa_bwd.argtypes = bwd_common + [vp]
+    lib.sdpa_bwd.restype = ctypes.c_int
+    lib.sdpa_bwd_check.argtypes = bwd_common
+    lib.sdpa_bwd_check.restype = ctypes.c_int
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
     lib.sdpa_strerror.restype = ctypes.c_char_p
     lib.sdpa_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -94,11 +101,7 @@ def _marshal(q, k, v, out, lse, mask, scale, is_causal):
     strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride()]
     mask_ptr, mask_keep = None, None
     if mask is not None:
-        m = mask.expand(*q.shape[:-1], Lk)
-        if m.dtype == torch.bool:
-            m = m.view(torch.uint8)
-        if m.dtype != torch.uint8:
-            raise TypeError("mask must be a bool or uint8 tensor")
+        m = _mask_view(mask, q.shape[:-1], Lk)
         strides += list(m.stride())
         mask_ptr, mask_keep = m.data_ptr(), m
     else:
@@ -160,6 +163,77 @@ def sdpa_fwd(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, mask=N
         status = load_library().sdpa_fwd(*args, handle)
     _raise_on(status)
     return out, lse
+
+
+def _mask_view(mask, lead_shape, Lk):
+    m = mask.expand(*lead_shape, Lk)
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    if m.dtype != torch.uint8:
+        raise TypeError("mask must be a bool or uint8 tensor")
+    return m
+
+
+def sdpa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, delta=None, *, scale=None,
+             is_causal=False, mask=None, stream=None):
+    """Gradients of the fused SDPA through the C ABI `sdpa_bwd` (bf16 only).
+
+    q, k, v, mask, scale, is_causal: as passed to sdpa_fwd; out and lse: what sdpa_fwd
+    returned for them; dout: the upstream gradient, shaped like out.  dq/dk/dv (shaped and
+    typed like q/k/v) and delta (float32 scratch shaped like lse, receives rowsum(dout *
+    out)) are allocated when not given.  Returns (dq, dk, dv); two kernels are enqueued on
+    `stream` (default: torch's current stream of q's device), nothing is synchronised.
+    """
+    _check_shapes(q, k, v, out, lse, mask)
+    for name, t, like in (("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t is not None and (tuple(t.shape) != tuple(like.shape) or t.dtype != q.dtype or
+                              t.device != q.device):
+            raise ValueError(f"{name} must match {'q' if like is q else 'k'} in shape, dtype "
+                             "and device")
+    if dout is None or lse is None:
+        raise ValueError("dout and the forward's lse are required")
+    if delta is not None and (tuple(delta.shape) != tuple(lse.shape) or
+                              delta.dtype != torch.float32 or not delta.is_contiguous() or
+                              delta.device != q.device):
+        raise ValueError("delta must be a contiguous float32 tensor shaped like lse")
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    delta = torch.empty(lse.shape, dtype=torch.float32, device=q.device) if delta is None else delta
+    rank = q.dim()
+    B, H, Lq, Lk, D = _sizes(q, k)
+    strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride(), *dout.stride(),
+               *dq.stride(), *dk.stride(), *dv.stride()]
+    mask_ptr = None
+    if mask is not None:
+        m = _mask_view(mask, q.shape[:-1], Lk)
+        strides += list(m.stride())
+        mask_ptr = m.data_ptr()
+    else:
+        strides += [0] * rank
+    arr = (ctypes.c_int64 * len(strides))(*strides)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        status = load_library().sdpa_bwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+            rank, B, H, Lq, Lk, D, arr, float(scale), 1 if is_causal else 0, mask_ptr,
+            _DTYPES.get(q.dtype, -1), handle)
+    _raise_on(status)
+    return dq, dk, dv
+
+
+def sdpa_bwd_check(ptrs, rank, B, H, Lq, Lk, D, strides, scale, is_causal, mask_ptr,
+                   dtype) -> int:
+    """The C ABI `sdpa_bwd_check` on raw integers: ptrs = the 10 pointers (q, k, v, out,
+    dout, lse, dq, dk, dv, delta) as ints, strides a list of 9*rank ints.  Host-only."""
+    arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
+    return load_library().sdpa_bwd_check(*ptrs, rank, B, H, Lq, Lk, D, arr, float(scale),
+                                         int(is_causal), mask_ptr, int(dtype))
 
 
 def sdpa_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, rank, B, H, Lq, Lk, D, strides, scale,

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsdpa_gfx950.so")
-SOURCES = ["sdpa_fwd_gfx950.hip", "sdpa_abi.cpp"]
+SOURCES = ["sdpa_fwd_gfx950.hip", "sdpa_bwd_gfx950.hip", "sdpa_abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -19,6 +19,35 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// One tensor's `rank` strides as canonical (b, h, row, col) strides: rank 3 [N,L,*] is
+// [1,N,L,*] with batch stride 0.  No stride may be negative; the innermost must be 1.
+int canon_strides(int rank, const int64_t* s, int64_t out[4]) {
+  if (rank == 4) {
+    for (int a = 0; a < 4; ++a) out[a] = s[a];
+  } else {
+    out[0] = 0;
+    out[1] = s[0];
+    out[2] = s[1];
+    out[3] = s[2];
+  }
+  for (int a = 0; a < 4; ++a)
+    if (out[a] < 0) return SDPA_ERR_STRIDE;
+  if (out[3] != 1) return SDPA_ERR_STRIDE;
+  return SDPA_OK;
+}
+
+// Shared checks of the sizes, head dim and scale.
+int check_sizes(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, float scale) {
+  if (rank != 3 && rank != 4) return SDPA_ERR_RANK;
+  if (rank == 3 && B != 1) return SDPA_ERR_RANK;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return SDPA_ERR_SHAPE;
+  if (Lq > kMaxDim || Lk > kMaxDim || B > kMaxDim || H > kMaxDim) return SDPA_ERR_SHAPE;
+  if (B != 0 && H > kMaxDim / B) return SDPA_ERR_SHAPE;
+  if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return SDPA_ERR_SCALE;
+  return SDPA_OK;
+}
+
 // Validate the arguments and build the canonical (b, h, row, col) problem.
 int normalise(const void* q, const void* k, const void* v, const void* out, const float* lse,
               int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
@@ -49,17 +78,8 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
       s4[t][0] = s4[t][1] = s4[t][2] = s4[t][3] = 0;
       continue;
     }
-    if (rank == 4) {
-      for (int a = 0; a < 4; ++a) s4[t][a] = s[a];
-    } else {
-      s4[t][0] = 0;
-      s4[t][1] = s[0];
-      s4[t][2] = s[1];
-      s4[t][3] = s[2];
-    }
-    for (int a = 0; a < 4; ++a)
-      if (s4[t][a] < 0) return SDPA_ERR_STRIDE;
-    if (s4[t][3] != 1) return SDPA_ERR_STRIDE;
+    const int st = canon_strides(rank, s, s4[t]);
+    if (st != SDPA_OK) return st;
   }
 
   if (any_rows && (!q || !out)) return SDPA_ERR_NULL;
@@ -101,6 +121,93 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
     p->scale = scale;
     p->causal = is_causal ? 1 : 0;
     p->dtype = dtype;
+  }
+  return SDPA_OK;
+}
+
+// Validate the backward's arguments and build its canonical problem.  Tensor order of
+// the strides: q, k, v, out, dout, dq, dk, dv, mask.
+int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
+                  const void* dout, const float* lse, const void* dq, const void* dk,
+                  const void* dv, const float* delta, int rank, int64_t B, int64_t H,
+                  int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                  int is_causal, const uint8_t* mask, int dtype, sdpa::BwdProblem* p) {
+  int st = check_sizes(rank, B, H, Lq, Lk, D, scale);
+  if (st != SDPA_OK) return st;
+  if (dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+  if (!strides) return SDPA_ERR_NULL;
+  const int64_t bh = B * H;
+  if (bh != 0 && ((Lq + sdpa::kBwdBlockQ - 1) / sdpa::kBwdBlockQ > kMaxDim / bh ||
+                  (Lk + sdpa::kBwdBlockK - 1) / sdpa::kBwdBlockK > kMaxDim / bh))
+    return SDPA_ERR_SHAPE;  // grid size
+  const bool rows = bh * Lq != 0;  // the dq kernel runs (and reads q, out, dout, lse)
+  const bool keys = bh * Lk != 0;  // the dkdv kernel runs (and reads k, v, writes dk, dv)
+
+  enum { Q, K, V, O, DO, DQ, DK, DV, M, NT };
+  int64_t s4[NT][4];
+  for (int t = 0; t < NT; ++t) {
+    if (t == M && !mask) {
+      s4[t][0] = s4[t][1] = s4[t][2] = s4[t][3] = 0;
+      continue;
+    }
+    st = canon_strides(rank, strides + t * rank, s4[t]);
+    if (st != SDPA_OK) return st;
+  }
+  // Every tensor is read or written when either kernel runs (q and dout are also staged
+  // by the dkdv kernel, k and v by the dq kernel), except that with Lk == 0 nothing of
+  // k, v, dk, dv exists and with Lq == 0 nothing of q, out, dout, dq, lse, delta.
+  const void* bases[8] = {q, k, v, out, dout, dq, dk, dv};
+  for (int t = 0; t < 8; ++t) {
+    const bool key_side = t == K || t == V || t == DK || t == DV;
+    if (!(key_side ? keys : rows)) continue;
+    if (!bases[t]) return SDPA_ERR_NULL;
+  }
+  if (rows && (!lse || !delta)) return SDPA_ERR_NULL;
+  for (int t = 0; t < 8; ++t) {
+    const bool key_side = t == K || t == V || t == DK || t == DV;
+    if (!(key_side ? keys : rows)) continue;
+    if (!aligned(bases[t], 16)) return SDPA_ERR_ALIGN;
+    for (int a = 0; a < 3; ++a)
+      if ((s4[t][a] * 2) % 16 != 0) return SDPA_ERR_ALIGN;
+  }
+  if ((lse && !aligned(lse, 4)) || (delta && !aligned(delta, 4))) return SDPA_ERR_ALIGN;
+  // Streamed tiles are addressed with 32-bit byte offsets from the head's base: K and V
+  // rows (dq kernel) and q and dout rows (dkdv kernel), plus one tile of overrun.
+  if (rows && keys) {
+    for (int t : {K, V})
+      if (s4[t][2] > kMaxDim / 2 / (Lk + sdpa::kBwdStep)) return SDPA_ERR_SHAPE;
+    for (int t : {Q, DO})
+      if (s4[t][2] > kMaxDim / 2 / (Lq + sdpa::kBwdStep)) return SDPA_ERR_SHAPE;
+  }
+
+  if (p) {
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->out = out;
+    p->dout = dout;
+    p->lse = lse;
+    p->delta = const_cast<float*>(delta);
+    p->dq = const_cast<void*>(dq);
+    p->dk = const_cast<void*>(dk);
+    p->dv = const_cast<void*>(dv);
+    p->mask = mask;
+    p->B = B;
+    p->H = H;
+    p->Lq = Lq;
+    p->Lk = Lk;
+    p->D = D;
+    memcpy(p->sq, s4[Q], sizeof p->sq);
+    memcpy(p->sk, s4[K], sizeof p->sk);
+    memcpy(p->sv, s4[V], sizeof p->sv);
+    memcpy(p->so, s4[O], sizeof p->so);
+    memcpy(p->sdo, s4[DO], sizeof p->sdo);
+    memcpy(p->sdq, s4[DQ], sizeof p->sdq);
+    memcpy(p->sdk, s4[DK], sizeof p->sdk);
+    memcpy(p->sdv, s4[DV], sizeof p->sdv);
+    memcpy(p->sm, s4[M], sizeof p->sm);
+    p->scale = scale;
+    p->causal = is_causal ? 1 : 0;
   }
   return SDPA_OK;
 }
@@ -150,6 +257,29 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
   return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
+int sdpa_bwd_check(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, const void* dq, const void* dk,
+                   const void* dv, const float* delta, int rank, int64_t B, int64_t H,
+                   int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                   int is_causal, const uint8_t* mask, int dtype) {
+  return normalise_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, rank, B, H, Lq, Lk, D,
+                       strides, scale, is_causal, mask, dtype, nullptr);
+}
+
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta, int rank, int64_t B,
+             int64_t H, int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+             int is_causal, const uint8_t* mask, int dtype, void* stream) {
+  sdpa::BwdProblem p;
+  const int st = normalise_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, rank, B, H, Lq, Lk,
+                               D, strides, scale, is_causal, mask, dtype, &p);
+  if (st != SDPA_OK) return st;
+  if (p.B * p.H * (p.Lq + p.Lk) == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  return sdpa::launch_bwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
 }
 
 const char* sdpa_strerror(int status) {

@@ -1,0 +1,635 @@
+// sdpa_bwd_gfx950.hip -- gradients of the fused scaled-dot-product attention for MI355X
+// (gfx950), bf16 inputs and outputs.
+//
+// The forward is out = P v with P the row softmax of S = scale * q.k^T over the visible
+// keys ("Profiling in PyTorch (part 3): attention", naive causal attention, five steps).
+// Its derivative for an upstream gradient dO, by the chain rule through those steps:
+//   dV = P^T dO,   dP = dO v^T,   dS = P * (dP - delta),   delta_i = sum_j P_ij dP_ij,
+//   dQ = scale * dS k,   dK = scale * dS^T q.
+// Because out = P v, delta_i also equals sum_d dO_id out_id, which costs one pass over
+// dO and out instead of a pass over P.  P itself is rebuilt from the scores and the
+// per-row log-sum-exp the forward exported (the DSA article's fused forward returns its
+// lse for the backward): P_ij = exp(scale q_i.k_j - lse_i), zero at hidden positions and
+// in rows with lse = -inf (no visible key), so the [L, L] matrices never reach memory.
+//
+// Two kernels, launched back to back on one stream, with no atomics and no workspace
+// beyond delta:
+//   * dq kernel: a workgroup owns 128 query rows of one (b, h), 32 per wave, and walks
+//     the key tiles; lane = query, exactly as in the forward: S^T = K Q^T and
+//     dP^T = V dO^T give each lane 16 keys of its own row, so lse and delta are per-lane
+//     scalars, and dQ^T += K^T dS^T accumulates in registers.  It also computes delta
+//     from its dO and out rows and stores it for the second kernel.
+//   * dkdv kernel: a workgroup owns 128 keys, 32 per wave, and walks the query tiles;
+//     lane = key: S = Q K^T and dP = dO V^T give each lane 16 queries of its own key's
+//     column, and dV^T += dO^T P, dK^T += Q^T dS accumulate in registers.
+// Each of the streamed tiles (K, V in the first kernel; Q, dO in the second) is the
+// left operand of one product (rows of 16 bytes, ds_read_b128) and, for K, Q and dO,
+// the transposed left operand of another (ds_read_b64_tr_b16).  The two read patterns
+// want different LDS row paddings for conflict-free banks, so such a tile is stored
+// twice per stage, once in each layout.
+#include <math.h>
+
+#include "sdpa_internal.h"
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle, no stride;
+// reads past num_records return zero.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  const uint8_t* mask;
+  int64_t sq[3], sk[3], sv[3], so[3], sdo[3], sdq[3], sdk[3], sdv[3], sm[3];
+  int32_t H, Lq, Lk, q_items, k_items, bh_count;
+  float scale;       // multiplies dQ and dK
+  float scale_log2;  // scale * log2(e): scores in base-2 units
+  int32_t mask_vec8; // mask rows may be read 8 bytes at a time
+};
+
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ inline float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline s16x4 ds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// Swaps bits 2 and 3 of a row index within 32 rows.  Reading the rows of a left operand
+// in this order makes the 32x32 accumulator hold, in half h of the lanes, rows 8h..8h+7
+// in registers 0..7 and 16+8h..16+8h+7 in registers 8..15: runs of 8 consecutive rows,
+// the operand layout the next product needs along its reduction dimension.
+__device__ inline int perm5(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Base-2 log-sum-exp of a row, from the forward's natural-log value; rows with no
+// visible key (lse = -inf) get +inf so that every probability of the row is 2^-inf = 0.
+__device__ inline float lse_base2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// Two fp32 values rounded to bf16 (nearest-even) and packed low-first.
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 p = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+}
+
+// The transposed operand of a 32x32x16 product from a row-major tile in LDS: rows are
+// the reduction index, columns the output rows.  Within each group of 16 lanes, lane i of
+// ds_read_b64_tr_b16 receives element i mod 4 of the 8-byte pieces addressed by lanes
+// 4e + i/4 (e = 0..3); addressing tile[row0 + e][col0 + 4q] from lane 4e + q therefore
+// hands lane i column col0 + i of four consecutive rows.  `tfrag` is that per-lane
+// address for row0 = 8 * (lane / 32), col0 = 16 * ((lane / 16) % 2); the operand of
+// reduction chunk c (rows 16c + 8h + 0..7 in half h) and output block dt (columns
+// 32dt + lane % 32) is two such reads, 4 rows apart.
+template <int PITCH>
+__device__ inline bf16x8 tr_operand(const char* tfrag, int c, int dt) {
+  const s16x4 lo = ds_read_tr(tfrag + (16 * c) * PITCH + 64 * dt);
+  const s16x4 hi = ds_read_tr(tfrag + (16 * c + 4) * PITCH + 64 * dt);
+  const s16x4 both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+__device__ inline int tr_lane_offset(int lane, int pitch) {
+  const int g16 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+  return (8 * (g16 >> 1) + e4) * pitch + (16 * (g16 & 1) + 4 * q4) * 2;
+}
+
+// Stores a 32 x D accumulator block set (registers 4g..4g+3 of block dt hold columns
+// 32dt + 8g + 4h + 0..3 of the lane's row) as one bf16 row, multiplied by `mul`.
+template <int D>
+__device__ inline void store_row_bf16(uint16_t* row, const f32x16 (&acc)[D / 32], float mul,
+                                      int hf) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t w0 = pack_bf16(acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul);
+      const uint32_t w1 = pack_bf16(acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul);
+      *reinterpret_cast<u32x2*>(row + 32 * dt + 8 * g + 4 * hf) = u32x2{w0, w1};
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dq kernel.  Workgroup: 128 query rows of one (b, h); wave w owns rows q0 + 32w + 0..31,
+// lane (li, hf) row q0 + 32w + li and head-dim half hf of each 16-wide chunk.  Per key
+// tile of 64 (two 32-key sub-tiles kt):
+//   S^T[kt]  = K[kt] Q^T        (K rows read in perm5 order: register r of half hf is key
+//   dP^T[kt] = V[kt] dO^T        32kt + 16(r/8) + 8hf + r%8)
+//   dS^T     = P^T * (dP^T - delta),  P^T = 2^(S^T scale log2e - lse2), hidden -> 0
+//   dQ^T    += K^T dS^T          (K^T by transposed reads, dS^T rounded to bf16)
+// LDS stage: K row copy | K transposed-read copy | V row copy.
+// ---------------------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kThreadsBwd) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_bf16(BwdArgs a) {
+  constexpr int BN = kBwdStep;
+  constexpr int NT = kThreadsBwd;
+  constexpr int DG = D / 8;           // 16-byte chunks per row
+  constexpr int CH = BN * DG / NT;    // chunks per thread per tile
+  constexpr int ROWS = NT / DG;       // tile rows covered by one chunk pass
+  constexpr int RP = k_pitch_bf16(D); // row-read pitch (bytes)
+  constexpr int TP = v_pitch_bf16(D); // transposed-read pitch (bytes)
+  constexpr int OFF_KT = BN * RP;
+  constexpr int OFF_V = OFF_KT + BN * TP;
+  constexpr int STAGE = OFF_V + BN * RP;
+  static_assert(CH * NT == BN * DG, "tile must split evenly over the workgroup");
+  static_assert(2 * STAGE == lds_bytes_bwd_dq(D), "plan and kernel disagree on LDS");
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;
+  const int hf = lane >> 5;
+
+  int64_t bh, qt;
+  decode_item(blockIdx.x, a.bh_count, a.q_items, CAUSAL, &bh, &qt);
+  const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.sq[0] + h * a.sq[1];
+  const uint16_t* ob = static_cast<const uint16_t*>(a.out) + b * a.so[0] + h * a.so[1];
+  const uint16_t* dob = static_cast<const uint16_t*>(a.dout) + b * a.sdo[0] + h * a.sdo[1];
+  const char* kb = static_cast<const char*>(a.k) + 2 * (b * a.sk[0] + h * a.sk[1]);
+  const char* vb = static_cast<const char*>(a.v) + 2 * (b * a.sv[0] + h * a.sv[1]);
+  uint16_t* dqb = static_cast<uint16_t*>(a.dq) + b * a.sdq[0] + h * a.sdq[1];
+  const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
+
+  const int q0 = int(qt) * kBwdBlockQ;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + li;
+  const bool q_ok = qi < a.Lq;
+  const bool wave_live = qw < a.Lq;
+
+  // Q^T and dO^T operands (chunk c = head dims 16c..16c+15, half hf supplies 8 of them),
+  // and delta = dO . out of this row from the same halves of dO and out.
+  bf16x8 qf[D / 16], dof[D / 16];
+  float dpart = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    u32x4 wq = {0, 0, 0, 0}, wd = {0, 0, 0, 0}, wo = {0, 0, 0, 0};
+    if (q_ok) {
+      wq = ld16(qb + int64_t(qi) * a.sq[2] + 16 * c + 8 * hf);
+      wd = ld16(dob + int64_t(qi) * a.sdo[2] + 16 * c + 8 * hf);
+      wo = ld16(ob + int64_t(qi) * a.so[2] + 16 * c + 8 * hf);
+    }
+    qf[c] = __builtin_bit_cast(bf16x8, wq);
+    dof[c] = __builtin_bit_cast(bf16x8, wd);
+    const bf16x8 of = __builtin_bit_cast(bf16x8, wo);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf(float(dof[c][e]), float(of[e]), dpart);
+  }
+  const float delta = pair_sum(dpart);
+  const float lse2 = q_ok ? lse_base2(a.lse[bh * a.Lq + qi]) : INFINITY;
+  if (q_ok && hf == 0) a.delta[bh * a.Lq + qi] = delta;
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  int kend = a.Lk;
+  if (CAUSAL) kend = min(kend, min(q0 + kBwdBlockQ, a.Lq));
+  const int ntiles = (kend + BN - 1) / BN;
+  const int wtiles = !wave_live ? 0 : CAUSAL ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
+
+  // Staging of K and V: buffer loads with the whole byte offset in the per-lane offset,
+  // checked by the hardware against the head's extent (rows past the end read zero; a
+  // tile index past the staged range is sent beyond the extent).  Offsets stay below
+  // 2^31: (Lk + 64) rows of K and of V span less than 2 GiB.
+  const int k_rowb = int(a.sk[2]) * 2, v_rowb = int(a.sv[2]) * 2;
+  const int k_ext = a.Lk > 0 ? (a.Lk - 1) * k_rowb + 2 * D : 0;
+  const int v_ext = a.Lk > 0 ? (a.Lk - 1) * v_rowb + 2 * D : 0;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, k_ext, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, v_ext, kBufferFlags);
+  const int ld_row = tid / DG, ld_col = tid % DG;
+  const int k_goff = ld_row * k_rowb + ld_col * 16;
+  const int v_goff = ld_row * v_rowb + ld_col * 16;
+  const int r_soff = ld_row * RP + ld_col * 16;
+  const int t_soff = ld_row * TP + ld_col * 16;
+  u32x4 kreg[CH], vreg[CH];
+  auto load = [&](int t) {
+    const int kbase = k_goff + (t < ntiles ? t * BN * k_rowb : k_ext);
+    const int vbase = v_goff + (t < ntiles ? t * BN * v_rowb : v_ext);
+#pragma unroll
+    for (int p = 0; p < CH; ++p) {
+      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, kbase + p * ROWS * k_rowb, 0, 0);
+      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vbase + p * ROWS * v_rowb, 0, 0);
+    }
+  };
+  auto store = [&](int st) {
+    char* s = lds + st * STAGE;
+#pragma unroll
+    for (int p = 0; p < CH; ++p) {
+      *reinterpret_cast<u32x4*>(s + r_soff + p * ROWS * RP) = kreg[p];
+      *reinterpret_cast<u32x4*>(s + OFF_KT + t_soff + p * ROWS * TP) = kreg[p];
+      *reinterpret_cast<u32x4*>(s + OFF_V + r_soff + p * ROWS * RP) = vreg[p];
+    }
+  };
+
+  const int rfrag = perm5(li) * RP + hf * 16;  // left-operand row of this lane
+  const int tfrag = tr_lane_offset(lane, TP);
+  const float c2 = a.scale_log2;
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+
+  auto compute = [&](int t) {
+    const char* st = lds + (t & 1) * STAGE;
+    const int k0 = t * BN;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = dp[kt][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, ld16(st + rfrag + kt * 32 * RP + 32 * c));
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kt], 0, 0, 0);
+      }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 vf =
+            __builtin_bit_cast(bf16x8, ld16(st + OFF_V + rfrag + kt * 32 * RP + 32 * c));
+        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[c], dp[kt], 0, 0, 0);
+      }
+
+    // x = S scale log2e - lse2 in base-2 units; hidden keys -> -inf.
+    float x[2][16];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[kt][r] = __builtin_fmaf(s[kt][r], c2, -lse2);
+    const bool edge = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > a.Lk);
+    if (edge || MASK) {
+      uint64_t mbits[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+      if (MASK && q_ok) {
+        const uint8_t* mrow = mb + int64_t(qi) * a.sm[2];
+#pragma unroll
+        for (int run = 0; run < 4; ++run) {
+          const int key0 = k0 + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
+          if (a.mask_vec8 && key0 + 8 <= a.Lk) {
+            mbits[run] = *reinterpret_cast<const uint64_t*>(mrow + key0);
+          } else {
+            uint64_t w = 0;
+            for (int e = 0; e < 8; ++e)
+              if (key0 + e < a.Lk) w |= uint64_t(mrow[key0 + e]) << (8 * e);
+            mbits[run] = w;
+          }
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
+          bool hide = key >= a.Lk;
+          if (CAUSAL) hide = hide || key > qi;
+          if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
+          if (hide) x[kt][r] = -INFINITY;
+        }
+    }
+    // dS^T operand: chunk c = keys 16c + 8hf + 0..7 (registers 8(c%2) .. +7 of kt = c/2)
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kt = c >> 1, r = 8 * (c & 1) + 2 * e;
+        const float d0 = exp2_fast(x[kt][r]) * (dp[kt][r] - delta);
+        const float d1 = exp2_fast(x[kt][r + 1]) * (dp[kt][r + 1] - delta);
+        w[e] = pack_bf16(d0, d1);
+      }
+      dsf[c] = __builtin_bit_cast(bf16x8, w);
+    }
+    const char* ktr = st + OFF_KT + tfrag;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<TP>(ktr, c, dt), dsf[c],
+                                                         dq[dt], 0, 0, 0);
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    load(t + 1);
+    if (t < wtiles) compute(t);
+    store((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (q_ok) store_row_bf16<D>(dqb + int64_t(qi) * a.sdq[2], dq, a.scale, hf);
+}
+
+// ---------------------------------------------------------------------------------------
+// dkdv kernel.  Workgroup: 128 keys of one (b, h); wave w owns keys k0 + 32w + 0..31,
+// lane (li, hf) key k0 + 32w + li.  Per query tile of 64 (two 32-query sub-tiles qs):
+//   S[qs]  = Q[qs] K^T            (Q rows read in perm5 order: register r of half hf is
+//   dP[qs] = dO[qs] V^T            query 32qs + 16(r/8) + 8hf + r%8)
+//   P = 2^(S scale log2e - lse2[query]), hidden -> 0;   dS = P * (dP - delta[query])
+//   dV^T += dO^T P,   dK^T += Q^T dS   (dO^T, Q^T by transposed reads; P, dS in bf16)
+// LDS stage: Q row copy | Q transposed-read copy | dO row copy | dO transposed-read copy |
+// lse2[64] | delta[64].
+// ---------------------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kThreadsBwd) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_bf16(BwdArgs a) {
+  constexpr int BQ = kBwdStep;
+  constexpr int NT = kThreadsBwd;
+  constexpr int DG = D / 8;
+  constexpr int CH = BQ * DG / NT;
+  constexpr int ROWS = NT / DG;
+  constexpr int RP = k_pitch_bf16(D);
+  constexpr int TP = v_pitch_bf16(D);
+  constexpr int OFF_QT = BQ * RP;
+  constexpr int OFF_DR = OFF_QT + BQ * TP;
+  constexpr int OFF_DT = OFF_DR + BQ * RP;
+  constexpr int OFF_LSE = OFF_DT + BQ * TP;
+  constexpr int OFF_DEL = OFF_LSE + 4 * BQ;
+  constexpr int STAGE = OFF_DEL + 4 * BQ;
+  static_assert(CH * NT == BQ * DG, "tile must split evenly over the workgroup");
+  static_assert(2 * STAGE == lds_bytes_bwd_dkdv(D), "plan and kernel disagree on LDS");
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;
+  const int hf = lane >> 5;
+
+  // Key tiles in index order, heads innermost: under a causal mask the first key tiles
+  // see the most queries, so the heaviest items are issued first.
+  int64_t bh, kt_idx;
+  decode_item(blockIdx.x, a.bh_count, a.k_items, false, &bh, &kt_idx);
+  const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
+  const char* qb = static_cast<const char*>(a.q) + 2 * (b * a.sq[0] + h * a.sq[1]);
+  const char* dob = static_cast<const char*>(a.dout) + 2 * (b * a.sdo[0] + h * a.sdo[1]);
+  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.sk[0] + h * a.sk[1];
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + b * a.sv[0] + h * a.sv[1];
+  uint16_t* dkb = static_cast<uint16_t*>(a.dk) + b * a.sdk[0] + h * a.sdk[1];
+  uint16_t* dvb = static_cast<uint16_t*>(a.dv) + b * a.sdv[0] + h * a.sdv[1];
+  const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
+  const float* lse_h = a.lse + bh * a.Lq;
+  const float* del_h = a.delta + bh * a.Lq;
+
+  const int k0 = int(kt_idx) * kBwdBlockK;
+  const int kw = k0 + 32 * wave;
+  const int kj = kw + li;
+  const bool k_ok = kj < a.Lk;
+  const bool wave_live = kw < a.Lk;
+
+  // K^T and V^T right operands (column = this lane's key, half hf supplies head dims
+  // 16c + 8hf .. +7 of chunk c), held for the whole query walk.
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    u32x4 wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
+    if (k_ok) {
+      wk = ld16(kb + int64_t(kj) * a.sk[2] + 16 * c + 8 * hf);
+      wv = ld16(vb + int64_t(kj) * a.sv[2] + 16 * c + 8 * hf);
+    }
+    kf[c] = __builtin_bit_cast(bf16x8, wk);
+    vf[c] = __builtin_bit_cast(bf16x8, wv);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  // Query tiles of the walk: with a causal mask, queries before k0 see none of the keys.
+  const int ntiles = (a.Lq + BQ - 1) / BQ;
+  const int tbeg = CAUSAL ? min(k0 / BQ, ntiles) : 0;
+
+  const int q_rowb = int(a.sq[2]) * 2, d_rowb = int(a.sdo[2]) * 2;
+  const int q_ext = a.Lq > 0 ? (a.Lq - 1) * q_rowb + 2 * D : 0;
+  const int d_ext = a.Lq > 0 ? (a.Lq - 1) * d_rowb + 2 * D : 0;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qb, 0, q_ext, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, d_ext, kBufferFlags);
+  const int ld_row = tid / DG, ld_col = tid % DG;
+  const int q_goff = ld_row * q_rowb + ld_col * 16;
+  const int d_goff = ld_row * d_rowb + ld_col * 16;
+  const int r_soff = ld_row * RP + ld_col * 16;
+  const int t_soff = ld_row * TP + ld_col * 16;
+  u32x4 qreg[CH], dreg[CH];
+  float rowval = 0.f;  // threads 0..63: lse2 of row tid; 64..127: delta of row tid - 64
+  auto load = [&](int t) {
+    const bool live = t < ntiles;
+    const int qbase = q_goff + (live ? t * BQ * q_rowb : q_ext);
+    const int dbase = d_goff + (live ? t * BQ * d_rowb : d_ext);
+#pragma unroll
+    for (int p = 0; p < CH; ++p) {
+      qreg[p] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qbase + p * ROWS * q_rowb, 0, 0);
+      dreg[p] = __builtin_amdgcn_raw_buffer_load_b128(drs, dbase + p * ROWS * d_rowb, 0, 0);
+    }
+    if (tid < 2 * BQ) {
+      const int row = t * BQ + (tid & (BQ - 1));
+      const bool ok = live && row < a.Lq;
+      if (tid < BQ) rowval = ok ? lse_base2(lse_h[row]) : INFINITY;
+      else rowval = ok ? del_h[row] : 0.f;
+    }
+  };
+  auto store = [&](int st) {
+    char* s = lds + st * STAGE;
+#pragma unroll
+    for (int p = 0; p < CH; ++p) {
+      *reinterpret_cast<u32x4*>(s + r_soff + p * ROWS * RP) = qreg[p];
+      *reinterpret_cast<u32x4*>(s + OFF_QT + t_soff + p * ROWS * TP) = qreg[p];
+      *reinterpret_cast<u32x4*>(s + OFF_DR + r_soff + p * ROWS * RP) = dreg[p];
+      *reinterpret_cast<u32x4*>(s + OFF_DT + t_soff + p * ROWS * TP) = dreg[p];
+    }
+    if (tid < 2 * BQ) reinterpret_cast<float*>(s + OFF_LSE)[tid] = rowval;
+  };
+
+  const int rfrag = perm5(li) * RP + hf * 16;
+  const int tfrag = tr_lane_offset(lane, TP);
+  const float c2 = a.scale_log2;
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
+
+  auto compute = [&](int t) {
+    const char* st = lds + (t & 1) * STAGE;
+    const int qt0 = t * BQ;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qs][r] = dp[qs][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const bf16x8 qa = __builtin_bit_cast(bf16x8, ld16(st + rfrag + qs * 32 * RP + 32 * c));
+        s[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], s[qs], 0, 0, 0);
+      }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const bf16x8 da =
+            __builtin_bit_cast(bf16x8, ld16(st + OFF_DR + rfrag + qs * 32 * RP + 32 * c));
+        dp[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[c], dp[qs], 0, 0, 0);
+      }
+
+    // chunk c holds queries qt0 + 16c + 8hf + e (e = 0..7): registers 8(c%2)+e of qs = c/2
+    const float* lse2s = reinterpret_cast<const float*>(st + OFF_LSE);
+    const float* dels = reinterpret_cast<const float*>(st + OFF_DEL);
+    const bool edge = CAUSAL && qt0 < kw + 31;
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qc = 16 * c + 8 * hf;  // first query of the run, within the tile
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + qc);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + qc + 4);
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dels + qc);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(dels + qc + 4);
+      const float lrun[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      const float drun[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      u32x4 wp, wd;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float p[2], ds[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int qs = c >> 1, r = 8 * (c & 1) + 2 * e + u;
+          const int qrow = qt0 + qc + 2 * e + u;
+          float xv = __builtin_fmaf(s[qs][r], c2, -lrun[2 * e + u]);
+          if (edge || MASK) {
+            bool hide = false;
+            if (CAUSAL) hide = kj > qrow;
+            if (MASK) hide = hide || !k_ok || qrow >= a.Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
+            if (hide) xv = -INFINITY;
+          }
+          p[u] = exp2_fast(xv);
+          ds[u] = p[u] * (dp[qs][r] - drun[2 * e + u]);
+        }
+        wp[e] = pack_bf16(p[0], p[1]);
+        wd[e] = pack_bf16(ds[0], ds[1]);
+      }
+      pf[c] = __builtin_bit_cast(bf16x8, wp);
+      dsf[c] = __builtin_bit_cast(bf16x8, wd);
+    }
+    const char* qtr = st + OFF_QT + tfrag;
+    const char* dtr = st + OFF_DT + tfrag;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<TP>(dtr, c, dt), pf[c],
+                                                         dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<TP>(qtr, c, dt), dsf[c],
+                                                         dk[dt], 0, 0, 0);
+      }
+  };
+
+  load(tbeg);
+  store(tbeg & 1);
+  __syncthreads();
+  for (int t = tbeg; t < ntiles; ++t) {
+    load(t + 1);
+    // the wave's keys are visible to some query of the tile iff its last query >= kw
+    if (wave_live && (!CAUSAL || t * BQ + BQ - 1 >= kw)) compute(t);
+    store((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (k_ok) {
+    store_row_bf16<D>(dkb + int64_t(kj) * a.sdk[2], dk, a.scale, hf);
+    store_row_bf16<D>(dvb + int64_t(kj) * a.sdv[2], dv, 1.f, hf);
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+hipError_t launch_pair(const BwdArgs& a, unsigned grid_q, unsigned grid_k, hipStream_t s) {
+  void* args[] = {const_cast<BwdArgs*>(&a)};
+  if (grid_q) {
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_bf16<D, CAUSAL, MASK>),
+                                         dim3(grid_q), dim3(kThreadsBwd), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  if (grid_k)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_bf16<D, CAUSAL, MASK>),
+                           dim3(grid_k), dim3(kThreadsBwd), args, 0, s);
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, bool causal, unsigned gq, unsigned gk, hipStream_t s) {
+  const bool m = a.mask != nullptr;
+  if (causal) return m ? launch_pair<D, true, true>(a, gq, gk, s) : launch_pair<D, true, false>(a, gq, gk, s);
+  return m ? launch_pair<D, false, true>(a, gq, gk, s) : launch_pair<D, false, false>(a, gq, gk, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
+  BwdArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.out = p.out;
+  a.dout = p.dout;
+  a.lse = p.lse;
+  a.delta = p.delta;
+  a.dq = p.dq;
+  a.dk = p.dk;
+  a.dv = p.dv;
+  a.mask = p.mask;
+  for (int i = 0; i < 3; ++i) {
+    a.sq[i] = p.sq[i];
+    a.sk[i] = p.sk[i];
+    a.sv[i] = p.sv[i];
+    a.so[i] = p.so[i];
+    a.sdo[i] = p.sdo[i];
+    a.sdq[i] = p.sdq[i];
+    a.sdk[i] = p.sdk[i];
+    a.sdv[i] = p.sdv[i];
+    a.sm[i] = p.sm[i];
+  }
+  a.H = int32_t(p.H);
+  a.Lq = int32_t(p.Lq);
+  a.Lk = int32_t(p.Lk);
+  a.bh_count = int32_t(p.B * p.H);
+  a.q_items = int32_t((p.Lq + kBwdBlockQ - 1) / kBwdBlockQ);
+  a.k_items = int32_t((p.Lk + kBwdBlockK - 1) / kBwdBlockK);
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * kLog2e;
+  a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
+                p.sm[1] % 8 == 0 && p.sm[2] % 8 == 0;
+  const unsigned gq = unsigned(int64_t(a.q_items) * a.bh_count);
+  const unsigned gk = unsigned(int64_t(a.k_items) * a.bh_count);
+  if (p.D == 64) return launch_bwd_d<64>(a, p.causal != 0, gq, gk, stream);
+  return launch_bwd_d<128>(a, p.causal != 0, gq, gk, stream);
+}
+
+}  // namespace sdpa

@@ -65,4 +65,45 @@ constexpr int64_t lds_bytes_f32(int D) {
 // p must already be validated.  Returns a hipError_t.
 hipError_t launch_fwd(const Problem& p, hipStream_t stream);
 
+// ---- backward (bf16) ----
+// Two kernels, each a workgroup of 4 waves (one per SIMD): the dQ kernel owns 128 query
+// rows of one (b, h) and walks key tiles of 64; the dK/dV kernel owns 128 keys and walks
+// query tiles of 64.  The dQ kernel runs first and also writes delta = rowsum(dO * O),
+// which the dK/dV kernel reads.
+constexpr int kThreadsBwd = 256;
+constexpr int kBwdBlockQ = 128;
+constexpr int kBwdBlockK = 128;
+constexpr int kBwdStep = 64;
+// LDS per workgroup of the two backward kernels: two stages, each holding the streamed
+// tiles once in row-read layout (pitch k_pitch_bf16) and once in transposed-read layout
+// (pitch v_pitch_bf16); the dK/dV kernel also stages the tile's lse and delta.
+constexpr int64_t lds_bytes_bwd_dq(int D) {
+  return 2 * int64_t(kBwdStep) * (2 * k_pitch_bf16(D) + v_pitch_bf16(D));
+}
+constexpr int64_t lds_bytes_bwd_dkdv(int D) {
+  return 2 * (int64_t(kBwdStep) * 2 * (k_pitch_bf16(D) + v_pitch_bf16(D)) + 8 * kBwdStep);
+}
+
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  const uint8_t* mask;
+  int64_t B, H, Lq, Lk, D;
+  int64_t sq[4], sk[4], sv[4], so[4], sdo[4], sdq[4], sdk[4], sdv[4], sm[4];
+  float scale;
+  int causal;
+};
+
+// Launches the dQ kernel (B*H*Lq > 0) and then the dK/dV kernel (B*H*Lk > 0) on
+// `stream`.  p must already be validated.  Returns a hipError_t.
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
+
 }  // namespace sdpa

@@ -1,0 +1,250 @@
+"""GPU parity of the backward: sdpa_bwd (through the C ABI) against the fp64 oracle's
+gradients, on the forward's own out and lse.
+
+Tolerance (max-abs over each compared block of dq, dk or dv):
+    |g - g_oracle| <= GRAD_TOL * max(1, max |g_oracle|).
+Gradients are sums over up to L terms and are not O(1) like the forward's output, so the
+forward's bf16 bound of 1e-2 is taken relative to the largest gradient of the block.
+Rows and keys that the method defines as exactly zero (a query with no visible key, a
+key no query sees) must be exactly zero.  Small problems are compared on every element;
+at full size whole heads (or, for the long-sequence workload, query rows and key rows
+that a smaller oracle problem determines exactly) plus properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import sdpa_bwd_oracle
+from scaled_dot_product_11_amd import SdpaError, sdpa_bwd, sdpa_fwd
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 1e-2
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def to_dev(t):
+    if t is None:
+        return None
+    d = t.to(DEV)
+    assert d.stride() == t.stride()
+    return d
+
+
+def compare_grads(got, ref, where="", names=("dq", "dk", "dv")):
+    """Gate of the module docstring; returns the normalised errors {name: err / scale}."""
+    errs = {}
+    for name, g, r in zip(names, got, ref):
+        g = g.float().cpu().double().numpy() if torch.is_tensor(g) else g
+        assert g.shape == r.shape, f"{where} {name}: shape {g.shape} vs {r.shape}"
+        if r.size == 0:
+            continue
+        assert np.all(np.isfinite(g)), f"{where} {name}: non-finite values"
+        scale = max(1.0, float(np.abs(r).max()))
+        err = float(np.abs(g - r).max())
+        errs[name] = err / scale
+        assert err <= GRAD_TOL * scale, \
+            f"{where} {name}: max-abs error {err:.3e} > {GRAD_TOL} * {scale:.3e}"
+    return errs
+
+
+def rand_inputs(seed, B, H, Lq, Lk, D, mask_mode=None, p_keep=0.3):
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = W.draw_qkv(g, (B, H, Lq, D), (B, H, Lk, D))
+    mask = None
+    if mask_mode is not None:
+        mask = torch.rand((B, 1 if mask_mode == "bcast" else H, Lq, Lk), generator=g) < p_keep
+        if Lq > 3:  # a few query rows with no visible key
+            mask[:, :, torch.randperm(Lq, generator=g)[:2], :] = False
+        if Lk > 3:  # a few keys no query sees
+            mask[:, :, :, torch.randperm(Lk, generator=g)[:2]] = False
+    return q, k, v, mask
+
+
+def gpu_grads(q, k, v, dout, mask, causal, scale=None, poison=True):
+    """Forward and backward on the GPU; the gradient buffers start as NaN so that an
+    element the kernels never write shows up."""
+    qd, kd, vd, dd, md = to_dev(q), to_dev(k), to_dev(v), to_dev(dout), to_dev(mask)
+    out, lse = sdpa_fwd(qd, kd, vd, mask=md, is_causal=causal, scale=scale)
+    bufs = [torch.full(t.shape, math.nan, dtype=t.dtype, device=DEV) if poison else None
+            for t in (q, k, v)]
+    dq, dk, dv = sdpa_bwd(qd, kd, vd, out, dd, lse, *bufs, mask=md, is_causal=causal,
+                          scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+SHAPES = [(1, 1), (33, 33), (64, 64), (127, 127), (129, 129), (200, 200), (77, 300), (300, 77)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mode", ["none", "causal", "mask", "causal_mask", "bcast_mask"])
+def test_bwd_ragged_small(D, mode):
+    causal = "causal" in mode
+    mm = None if mode in ("none", "causal") else ("bcast" if mode == "bcast_mask" else "full")
+    for n, (Lq, Lk) in enumerate(SHAPES):
+        q, k, v, mask = rand_inputs(1000 + 10 * n + D, 2, 3, Lq, Lk, D, mm)
+        dout = W.upstream_grad(2000 + n, q)
+        got = gpu_grads(q, k, v, dout, mask, causal)
+        ref = sdpa_bwd_oracle(q, k, v, dout, mask=mask, is_causal=causal)
+        where = f"D={D} {mode} Lq={Lq} Lk={Lk}"
+        compare_grads(got, ref, where)
+        # exact zeros: query rows with no visible key, keys no query sees
+        vis = torch.ones(2, 3, Lq, Lk, dtype=torch.bool)
+        if causal:
+            vis &= torch.ones(Lq, Lk, dtype=torch.bool).tril()
+        if mask is not None:
+            vis &= mask.expand(2, 3, Lq, Lk)
+        dq, dk, dv = (t.cpu() for t in got)
+        assert torch.all(dq[~vis.any(-1)] == 0), where
+        assert torch.all(dk[~vis.any(-2)] == 0) and torch.all(dv[~vis.any(-2)] == 0), where
+
+
+def test_bwd_rank3_equals_rank4_small():
+    q, k, v, _ = rand_inputs(7, 1, 5, 150, 150, 128)
+    dout = W.upstream_grad(8, q)
+    g4 = gpu_grads(q, k, v, dout, None, True)
+    g3 = gpu_grads(q[0], k[0], v[0], dout[0], None, True)
+    for a, b in zip(g4, g3):
+        assert torch.equal(a[0], b)
+    compare_grads(g3, sdpa_bwd_oracle(q[0], k[0], v[0], dout[0], is_causal=True), "rank3")
+
+
+def test_bwd_strided_inputs_and_outputs():
+    """[B,L,H,D] buffers viewed as [B,H,L,D] for every input and every gradient."""
+    B, H, L, D = 2, 3, 130, 64
+    g = torch.Generator().manual_seed(9)
+    q, k, v, dout = (W._randn(g, (B, L, H, D), torch.bfloat16).transpose(1, 2) for _ in range(4))
+    qd, kd, vd, dd = (to_dev(t) for t in (q, k, v, dout))
+    out, lse = sdpa_fwd(qd, kd, vd, is_causal=True)
+    grads = [torch.full((B, L, H, D), math.nan, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+             for _ in range(3)]
+    dq, dk, dv = sdpa_bwd(qd, kd, vd, out, dd, lse, *grads, is_causal=True)
+    torch.cuda.synchronize()
+    assert dq.data_ptr() == grads[0].data_ptr() and not dq.is_contiguous()
+    compare_grads((dq, dk, dv), sdpa_bwd_oracle(q, k, v, dout, is_causal=True), "strided")
+
+
+def test_bwd_no_queries_and_no_keys():
+    # Lq == 0: nothing reaches k or v, so dk = dv = 0 must still be written
+    q, k, v, _ = rand_inputs(11, 1, 2, 0, 70, 64)
+    dk, dv = gpu_grads(q, k, v, W.upstream_grad(12, q), None, False)[1:]
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+    # Lk == 0: every row is empty, dq = 0
+    q, k, v, _ = rand_inputs(13, 1, 2, 70, 0, 64)
+    dq = gpu_grads(q, k, v, W.upstream_grad(14, q), None, False)[0]
+    assert torch.all(dq == 0)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.0])
+def test_bwd_unusual_scales(scale):
+    q, k, v, _ = rand_inputs(15, 1, 2, 96, 96, 64)
+    dout = W.upstream_grad(16, q)
+    got = gpu_grads(q, k, v, dout, None, True, scale=scale)
+    compare_grads(got, sdpa_bwd_oracle(q, k, v, dout, is_causal=True, scale=scale),
+                  f"scale={scale}")
+
+
+def test_bwd_invalid_arguments_raise():
+    q, k, v, _ = rand_inputs(17, 1, 1, 8, 8, 64)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    out, lse = sdpa_fwd(qd, kd, vd)
+    with pytest.raises(SdpaError, match="SDPA_ERR_DTYPE"):
+        f = [t.float() for t in (qd, kd, vd, out)]
+        sdpa_bwd(*f[:3], f[3], f[3], lse)
+    with pytest.raises(SdpaError, match="SDPA_ERR_HEAD_DIM"):
+        z = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=DEV)
+        sdpa_bwd(z, z, z, z, z, lse)
+
+
+# ---------------------------------------------------------------------------------------
+# full-size workloads
+
+def test_bwd_config2_full_oracle():
+    wl = W.config2()
+    dout = W.upstream_grad(21, wl.q)
+    got = gpu_grads(wl.q, wl.k, wl.v, dout, None, True, wl.scale)
+    compare_grads(got, sdpa_bwd_oracle(wl.q, wl.k, wl.v, dout, is_causal=True, scale=wl.scale),
+                  wl.name)
+
+
+def test_bwd_config3_rank3_equals_rank4_and_heads():
+    wl3, wl4 = W.config3(rank=3), W.config3(rank=4)
+    dout4 = W.upstream_grad(31, wl4.q)
+    dout3 = dout4.reshape(128, 2048, 128)
+    g3 = gpu_grads(wl3.q, wl3.k, wl3.v, dout3, None, True, wl3.scale, poison=False)
+    g4 = gpu_grads(wl4.q, wl4.k, wl4.v, dout4, None, True, wl4.scale, poison=False)
+    for a, b in zip(g3, g4):
+        assert torch.equal(a, b.reshape(a.shape))
+    heads = [0, 77, 127]
+    sl = lambda t: t[heads].contiguous()
+    ref = sdpa_bwd_oracle(sl(wl3.q), sl(wl3.k), sl(wl3.v), sl(dout3), is_causal=True,
+                          scale=wl3.scale)
+    compare_grads([g[heads] for g in g3], ref, wl3.name + " heads 0,77,127")
+
+
+def test_bwd_config4_long_sequence_sampled():
+    """[1,32,8192,128] causal with [B,L,H,D] strides.  Exactly determined by small oracle
+    problems: dq of query row i (row i alone against keys 0..i, no mask), and dk, dv of the
+    last 256 keys (queries L-256.. against all keys, the causal triangle as a mask; no
+    earlier query sees those keys)."""
+    wl = W.config4()
+    dout = W.upstream_grad(41, wl.q, blhd=True)
+    dq, dk, dv = gpu_grads(wl.q, wl.k, wl.v, dout, None, True, wl.scale, poison=False)
+    L, T = 8192, 256
+    rng = np.random.default_rng(4)
+    heads = [0, 31]
+    for h in heads:
+        rows = sorted({0, 1, 63, 64, 127, 128, 4095, L - 2, L - 1} |
+                      set(rng.integers(0, L, size=12).tolist()))
+        for i in rows:
+            ref = sdpa_bwd_oracle(wl.q[:, h:h + 1, i:i + 1], wl.k[:, h:h + 1, :i + 1],
+                                  wl.v[:, h:h + 1, :i + 1], dout[:, h:h + 1, i:i + 1],
+                                  scale=wl.scale)
+            compare_grads([dq[:, h:h + 1, i:i + 1]], ref[:1], f"c4 h={h} dq row {i}")
+    # both heads in one oracle call (it runs heads in parallel)
+    tri = torch.arange(L)[None, :] <= (torch.arange(T)[:, None] + (L - T))
+    ref = sdpa_bwd_oracle(wl.q[:, heads, L - T:], wl.k[:, heads], wl.v[:, heads],
+                          dout[:, heads, L - T:], mask=tri[None, None], scale=wl.scale)
+    compare_grads([dk[:, heads, L - T:], dv[:, heads, L - T:]],
+                  [ref[1][:, :, L - T:], ref[2][:, :, L - T:]], "c4 last keys",
+                  names=("dk", "dv"))
+    # every row sees key 0, so the rows of P sum to one and sum_j dV_j = sum_i dO_i
+    sdv = dv.double().sum(dim=2).cpu()
+    sdo = dout.double().sum(dim=2)
+    scale = max(1.0, float(sdo.abs().max()))
+    assert float((sdv - sdo).abs().max()) <= GRAD_TOL * scale
+
+
+def test_bwd_config5_bool_mask_heads():
+    wl = W.config5()
+    dout = W.upstream_grad(51, wl.q)
+    dq, dk, dv = gpu_grads(wl.q, wl.k, wl.v, dout, wl.mask, False, wl.scale)
+    empty = wl.extra["empty_rows"]
+    for b in range(2):
+        assert torch.all(dq[b][:, empty[b].to(DEV)] == 0)
+    # heads (b=0, h=0) and (b=1, h=7) as one two-head problem with their batch's mask
+    sel = lambda t: torch.stack([t[0, 0], t[1, 7]])[None]
+    mask = torch.stack([wl.mask[0, 0], wl.mask[1, 0]])[None]
+    ref = sdpa_bwd_oracle(sel(wl.q), sel(wl.k), sel(wl.v), sel(dout), mask=mask,
+                          scale=wl.scale)
+    compare_grads([sel(g) for g in (dq, dk, dv)], ref, "c5 heads (0,0) (1,7)")
+
+
+def test_bwd_deterministic_repeats():
+    wl = W.config2()
+    dout = W.upstream_grad(61, wl.q)
+    first = gpu_grads(wl.q, wl.k, wl.v, dout, None, True, wl.scale)
+    for _ in range(2):
+        again = gpu_grads(wl.q, wl.k, wl.v, dout, None, True, wl.scale)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)

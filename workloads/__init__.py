@@ -62,6 +62,19 @@ def random_qkv(seed, q_shape, k_shape=None, dtype=torch.bfloat16, device="cpu", 
     return q.to(device), k.to(device), v.to(device)
 
 
+def upstream_grad(seed, like, device="cpu", blhd=False):
+    """An upstream gradient dout for an output shaped like `like` (rank 3 or 4): i.i.d.
+    N(0,1) in like's dtype from a fresh generator seeded with `seed`.  With blhd (rank 4),
+    the draw is a [B,L,H,D] buffer viewed as [B,H,L,D] through a transpose, the layout of
+    the long-sequence workload."""
+    g = torch.Generator().manual_seed(seed)
+    shape = tuple(like.shape)
+    if blhd:
+        B, H, L, D = shape
+        return _randn(g, (B, L, H, D), like.dtype).to(device).transpose(1, 2)
+    return _randn(g, shape, like.dtype).to(device)
+
+
 def bernoulli_mask(seed, shape, p_keep, empty_rows_frac=0.0, device="cpu"):
     """Bool mask [..., Lq, Lk]: True (visible) with probability p_keep; then, per leading
     index, round(empty_rows_frac * Lq) query rows chosen by randperm are set all-False."""
