@@ -1,5 +1,5 @@
 """Host-only tests of the C ABI: the library loads without a GPU, exports every entry point
-declared in include/*.h, and sdpa_check / sdpa_plan behave as documented.  No kernel is
+declared in include/*.h, and sdpa_check / sdpa_bwd_check / sdpa_plan behave as documented.  No kernel is
 launched here."""
 import glob
 import os
@@ -26,8 +26,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     decl = declared_functions()
-    assert set(decl) >= {"sdpa_fwd", "sdpa_check", "sdpa_strerror", "sdpa_plan",
-                         "sdpa_plan_item"}
+    assert set(decl) >= {"sdpa_fwd", "sdpa_check", "sdpa_bwd", "sdpa_bwd_check", "sdpa_strerror",
+                         "sdpa_plan", "sdpa_plan_item"}
     out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
@@ -219,3 +219,93 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU only"):
         sd.sdpa_fwd(q, q, q)
+
+
+# ---- sdpa_bwd_check ------------------------------------------------------------------
+
+def bargs(B=2, H=3, Lq=100, Lk=90, D=64, dtype=sd.SDPA_BF16, mask=False, **over):
+    """Arguments of sdpa_bwd_check: pointers q, k, v, out, dout, lse, dq, dk, dv, delta."""
+    q = [H * Lq * D, Lq * D, D, 1]
+    k = [H * Lk * D, Lk * D, D, 1]
+    m = [0, 0, Lk, 1] if mask else [0, 0, 0, 0]
+    ptrs = [A + i * 0x10000 for i in range(10)]
+    a = dict(ptrs=ptrs, rank=4, B=B, H=H, Lq=Lq, Lk=Lk, D=D,
+             strides=q + k + k + q + q + q + k + k + m, scale=0.125, is_causal=1,
+             mask_ptr=A + 0xA0000 if mask else None, dtype=dtype)
+    a.update(over)
+    return a
+
+
+def bcheck(**kw):
+    return sd.sdpa_bwd_check(**kw)
+
+
+def with_ptr(i, value, **kw):
+    a = bargs(**kw)
+    a["ptrs"] = list(a["ptrs"])
+    a["ptrs"][i] = value
+    return a
+
+
+def with_stride(i, value, **kw):
+    a = bargs(**kw)
+    a["strides"] = list(a["strides"])
+    a["strides"][i] = value
+    return a
+
+
+def test_bwd_check_valid_and_rank3():
+    assert bcheck(**bargs()) == OK
+    assert bcheck(**bargs(mask=True, D=128)) == OK
+    r3 = bargs(B=1)
+    s = r3["strides"]
+    r3["strides"] = [x for t in range(9) for x in s[4 * t + 1:4 * t + 4]]
+    r3["rank"] = 3
+    assert bcheck(**r3) == OK
+
+
+def test_bwd_check_errors():
+    assert bcheck(**bargs(dtype=sd.SDPA_F32)) == DTYPE  # the backward is bf16 only
+    assert bcheck(**bargs(D=96)) == HEAD
+    assert bcheck(**bargs(rank=5)) == RANK
+    assert bcheck(**bargs(Lq=-1)) == SHAPE
+    assert bcheck(**bargs(scale=float("nan"))) == SCALE
+    assert bcheck(**bargs(strides=None)) == NULL
+    for i in range(10):  # every pointer is required for a non-empty problem
+        assert bcheck(**with_ptr(i, None)) == NULL, i
+    for i in range(10):  # 16-byte tensors, 4-byte lse and delta
+        st = bcheck(**with_ptr(i, A + 4))
+        assert st == (OK if i in (5, 9) else ALIGN), i
+        assert bcheck(**with_ptr(i, A + 2)) == ALIGN, i
+    for t in range(8):  # innermost stride 1, outer strides 16-byte multiples, none negative
+        assert bcheck(**with_stride(4 * t + 3, 2)) == STRIDE, t
+        assert bcheck(**with_stride(4 * t + 2, 68)) == ALIGN, t
+        assert bcheck(**with_stride(4 * t + 1, -64)) == STRIDE, t
+    assert bcheck(**with_stride(35, 2, mask=True)) == STRIDE  # mask key stride
+    assert bcheck(**with_stride(35, 2, mask=False)) == OK     # ignored without a mask
+    # q and dout rows (plus a tile) must span less than 2 GiB
+    assert bcheck(**with_stride(2, 1024, Lq=2 ** 20, D=128)) == SHAPE
+    assert bcheck(**with_stride(18, 1024, Lq=2 ** 20, D=128)) == SHAPE
+    assert bcheck(**with_stride(2, 512, Lq=2 ** 20, D=128)) == OK
+
+
+def test_bwd_check_empty_sides():
+    # no queries: q, out, dout, dq, lse, delta are never touched
+    a = bargs(Lq=0)
+    a["ptrs"] = [None if i in (0, 3, 4, 5, 6, 9) else p for i, p in enumerate(a["ptrs"])]
+    assert bcheck(**a) == OK
+    # no keys: k, v, dk, dv are never touched
+    a = bargs(Lk=0)
+    a["ptrs"] = [None if i in (1, 2, 7, 8) else p for i, p in enumerate(a["ptrs"])]
+    assert bcheck(**a) == OK
+
+
+def test_bwd_rejects_before_any_device_call():
+    import ctypes
+    lib = sd.load_library()
+    a = bargs(D=96)
+    arr = (ctypes.c_int64 * 36)(*a["strides"])
+    st = lib.sdpa_bwd(*a["ptrs"], 4, 2, 3, 100, 90, 96, arr, 0.125, 1, None, 1, None)
+    assert st == HEAD
+    st = lib.sdpa_bwd(*([None] * 10), 4, 0, 3, 100, 90, 64, arr, 0.125, 1, None, 1, None)
+    assert st == OK  # B == 0: nothing to do
