@@ -13,6 +13,13 @@ credited.  The roofline peak is MI355X's dense bf16 matrix-core rate,
 
 Prints one JSON line.  `--report PATH` also writes per-workload timings (all five
 configurations, rank-3 vs rank-4) to PATH.
+
+`--pass bwd` measures the gradients instead: one step = one sdpa_bwd call (its dq and dk/dv
+kernels) on the same workload, with the forward's out and lse and an upstream gradient
+(N(0,1), same [B,L,H,D] layout) resident before the timed region, gradients written in the
+inputs' layout.  Its algorithmic work is 10*D flops per visible pair: five products of
+2*D (the scores recomputed once, since P is never stored; dP; dV; dQ; dK).  The second
+recomputation of S and dP inside the dq kernel is not credited.
 """
 import argparse
 import json
@@ -30,6 +37,7 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12  # 2516.58
 PEAK_F32_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
+BWD_METRIC = "causal SDPA bwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
 # HBM bytes per launch of the fused kernel on the default workload: FETCH_SIZE and
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
@@ -60,6 +68,12 @@ def step_flops(wl):
     score matrix, so a masked problem is counted dense."""
     B, H, Lq, Lk, D = wl.shape4()
     return 4 * D * B * H * visible_pairs(Lq, Lk, wl.is_causal)
+
+
+def bwd_step_flops(wl):
+    """Algorithmic flops of one backward: 10*D per visible pair (five products of 2*D)."""
+    B, H, Lq, Lk, D = wl.shape4()
+    return 10 * D * B * H * visible_pairs(Lq, Lk, wl.is_causal)
 
 
 def time_kernel(fn, steps, warmup):
@@ -113,6 +127,36 @@ def cpu_baseline(wl, target_s=12.0, seed=0):
                       f"pairs, {threads} OpenMP threads, host cpu: {cpu_model()}"}
 
 
+def cpu_baseline_bwd(wl, target_s=12.0):
+    """The fp64 backward oracle on a bounded sample of the same workload: the causal
+    top-left corner [0, T) of the first 8 heads (an exact causal problem of its own, run
+    one head per thread), T grown from 512 until about target_s; algorithmic flops of its
+    visible pairs / time, in TFLOP/s."""
+    import oracle
+    import workloads as W
+    B, H, Lq, Lk, D = wl.shape4()
+    nh = min(8, H)
+    dout = W.upstream_grad(41, wl.q, blhd=True)
+
+    def run(T):
+        sl = lambda t: t[:1, :nh, :T]
+        t0 = time.perf_counter()
+        oracle.sdpa_bwd_oracle(sl(wl.q), sl(wl.k), sl(wl.v), sl(dout), is_causal=wl.is_causal,
+                               scale=wl.scale)
+        return time.perf_counter() - t0, 10 * D * nh * visible_pairs(T, T, wl.is_causal)
+
+    T = 512
+    dt, fl = run(T)
+    while dt < target_s / 4 and 2 * T <= Lq:  # cost grows ~4x per doubling
+        T *= 2
+        dt, fl = run(T)
+    threads = min(nh, oracle.default_threads())
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"causal top-left corner L={T} of heads 0..{nh - 1} of the same workload, "
+                      f"fp64 backward oracle, {dt:.2f} s for {fl / 1e9:.2f} GFLOP of visible "
+                      f"pairs, one head per thread, host cpu: {cpu_model()}"}
+
+
 def cpu_model():
     try:
         for ln in open("/proc/cpuinfo"):
@@ -152,12 +196,77 @@ def bench_workload(wl, steps, warmup):
             "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12}
 
 
+def bench_bwd(wl, steps, warmup):
+    import torch
+    import workloads as W
+    from scaled_dot_product_11_amd import sdpa_bwd, sdpa_fwd
+    q, k, v, m = to_device(wl, "cuda")
+    dout = W.upstream_grad(41, wl.q, device="cuda", blhd=True)
+    out, lse = sdpa_fwd(q, k, v, mask=m, is_causal=wl.is_causal, scale=wl.scale)
+    grads = [torch.empty_like(t) for t in (q, k, v)]  # keeps the inputs' strides
+    for g, t in zip(grads, (q, k, v)):
+        assert g.stride() == t.stride()
+    delta = torch.empty_like(lse)
+
+    def fn():
+        sdpa_bwd(q, k, v, out, dout, lse, *grads, delta, mask=m, is_causal=wl.is_causal,
+                 scale=wl.scale)
+    wall, per = time_kernel(fn, steps, warmup)
+    flops = bwd_step_flops(wl)
+    return {"workload": wl.name, "flops": flops, "wall_s": wall, "steps": steps,
+            "kernel_ms_mean": statistics.fmean(per), "kernel_ms_median": statistics.median(per),
+            "kernel_ms_min": min(per), "kernel_ms_max": max(per),
+            "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12}
+
+
+def main_bwd(args, props):
+    import workloads as W
+    wl = W.config4()
+    r = bench_bwd(wl, args.steps, args.warmup)
+    ms_per_step = r["wall_s"] / args.steps * 1e3
+    value = r["flops"] / (ms_per_step * 1e-3) / 1e12
+    achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
+    line = {
+        "metric": BWD_METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "pass": "bwd", "shape_bhld": [1, 32, 8192, 128],
+                   "layout": "[B,L,H,D] buffers viewed as [B,H,L,D], gradients alike",
+                   "is_causal": True, "scale": wl.scale, "flops_per_step": r["flops"],
+                   "flop_convention": "10*D per visible (i,j) pair, causal-adjusted",
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "device": props.name, "cus": props.multi_processor_count},
+        # one step is two kernels (dq, then dk/dv) timed together by events on the stream
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernels": "bwd_dq_bf16 + bwd_dkdv_bf16",
+                     "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
+                     "kernel_ms_median": round(r["kernel_ms_median"], 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(wl)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd (default): the fused forward; bwd: its gradients")
     ap.add_argument("--report", default=None, help="write per-workload timings here")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one elementwise kernel reading and writing this many MiB "
@@ -172,6 +281,9 @@ def main():
     import workloads as W
     assert torch.cuda.is_available(), "no GPU visible"
     props = torch.cuda.get_device_properties(0)
+    if args.which == "bwd":
+        main_bwd(args, props)
+        return
 
     wl = W.config4()
     r = bench_workload(wl, args.steps, args.warmup)

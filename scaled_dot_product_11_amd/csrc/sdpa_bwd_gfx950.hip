@@ -14,20 +14,23 @@
 //
 // Two kernels, launched back to back on one stream, with no atomics and no workspace
 // beyond delta:
-//   * dq kernel: a workgroup owns 128 query rows of one (b, h), 32 per wave, and walks
+//   * dq kernel: a workgroup owns 256 query rows of one (b, h), 32 per wave, and walks
 //     the key tiles; lane = query, exactly as in the forward: S^T = K Q^T and
 //     dP^T = V dO^T give each lane 16 keys of its own row, so lse and delta are per-lane
 //     scalars, and dQ^T += K^T dS^T accumulates in registers.  It also computes delta
 //     from its dO and out rows and stores it for the second kernel.
-//   * dkdv kernel: a workgroup owns 128 keys, 32 per wave, and walks the query tiles;
-//     lane = key: S = Q K^T and dP = dO V^T give each lane 16 queries of its own key's
-//     column, and dV^T += dO^T P, dK^T += Q^T dS accumulate in registers.
+//   * dkdv kernel: a workgroup owns 128 keys, 32 per pair of waves, and walks the query
+//     tiles; lane = key: S = Q K^T and dP = dO V^T give each lane 16 queries of its own
+//     key's column; one wave of the pair accumulates dV^T += dO^T P, the other
+//     dK^T += Q^T dS.
 // Each of the streamed tiles (K, V in the first kernel; Q, dO in the second) is the
 // left operand of one product (rows of 16 bytes, ds_read_b128) and, for K, Q and dO,
 // the transposed left operand of another (ds_read_b64_tr_b16).  The two read patterns
 // want different LDS row paddings for conflict-free banks, so such a tile is stored
 // twice per stage, once in each layout.
 #include <math.h>
+
+#include <type_traits>
 
 #include "sdpa_internal.h"
 
@@ -70,6 +73,26 @@ struct BwdArgs {
 };
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// With one wave per SIMD nothing else hides the latency of an LDS read, and left alone the
+// scheduler reads each operand just before its product.  This orders the NMFMA products
+// of the current scheduling region behind their reads (READS operand reads per product)
+// with a lookahead of AHEAD products: the reads of the first AHEAD products, then one
+// product per READS reads, then the last AHEAD products.
+template <int NMFMA, int READS, int AHEAD>
+__device__ inline void pipeline_lds_reads() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD, 0);
+}
 
 __device__ inline float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -135,7 +158,9 @@ __device__ inline void store_row_bf16(uint16_t* row, const f32x16 (&acc)[D / 32]
 }
 
 // ---------------------------------------------------------------------------------------
-// dq kernel.  Workgroup: 128 query rows of one (b, h); wave w owns rows q0 + 32w + 0..31,
+// dq kernel.  Workgroup: 256 query rows of one (b, h) in 8 waves, two per SIMD, so that
+// one wave's vector work and operand reads overlap the other's products; wave w owns
+// rows q0 + 32w + 0..31,
 // lane (li, hf) row q0 + 32w + li and head-dim half hf of each 16-wide chunk.  Per key
 // tile of 64 (two 32-key sub-tiles kt):
 //   S^T[kt]  = K[kt] Q^T        (K rows read in perm5 order: register r of half hf is key
@@ -145,10 +170,10 @@ __device__ inline void store_row_bf16(uint16_t* row, const f32x16 (&acc)[D / 32]
 // LDS stage: K row copy | K transposed-read copy | V row copy.
 // ---------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreadsBwd) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsBwdQ) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_bf16(BwdArgs a) {
   constexpr int BN = kBwdStep;
-  constexpr int NT = kThreadsBwd;
+  constexpr int NT = kThreadsBwdQ;
   constexpr int DG = D / 8;           // 16-byte chunks per row
   constexpr int CH = BN * DG / NT;    // chunks per thread per tile
   constexpr int ROWS = NT / DG;       // tile rows covered by one chunk pass
@@ -279,6 +304,8 @@ void bwd_dq_bf16(BwdArgs a) {
             __builtin_bit_cast(bf16x8, ld16(st + OFF_V + rfrag + kt * 32 * RP + 32 * c));
         dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[c], dp[kt], 0, 0, 0);
       }
+    pipeline_lds_reads<4 * (D / 16), 1, 4>();
+    __builtin_amdgcn_sched_barrier(0);
 
     // x = S scale log2e - lse2 in base-2 units; hidden keys -> -inf.
     float x[2][16];
@@ -330,12 +357,14 @@ void bwd_dq_bf16(BwdArgs a) {
       dsf[c] = __builtin_bit_cast(bf16x8, w);
     }
     const char* ktr = st + OFF_KT + tfrag;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
         dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<TP>(ktr, c, dt), dsf[c],
                                                          dq[dt], 0, 0, 0);
+    pipeline_lds_reads<4 * (D / 32), 2, 4>();
   };
 
   load(0);
@@ -352,20 +381,27 @@ void bwd_dq_bf16(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// dkdv kernel.  Workgroup: 128 keys of one (b, h); wave w owns keys k0 + 32w + 0..31,
-// lane (li, hf) key k0 + 32w + li.  Per query tile of 64 (two 32-query sub-tiles qs):
-//   S[qs]  = Q[qs] K^T            (Q rows read in perm5 order: register r of half hf is
-//   dP[qs] = dO[qs] V^T            query 32qs + 16(r/8) + 8hf + r%8)
-//   P = 2^(S scale log2e - lse2[query]), hidden -> 0;   dS = P * (dP - delta[query])
-//   dV^T += dO^T P,   dK^T += Q^T dS   (dO^T, Q^T by transposed reads; P, dS in bf16)
-// LDS stage: Q row copy | Q transposed-read copy | dO row copy | dO transposed-read copy |
+// dkdv kernel.  Workgroup: 128 keys of one (b, h) in 8 waves, two per SIMD.  The two waves
+// of a SIMD own the same 32 keys k0 + 32(w % 4) + 0..31 (lane (li, hf): key
+// k0 + 32(w % 4) + li) and split the products between them, so that each holds only one
+// accumulator block and the pair fits two waves per SIMD:
+//   both:     S[qs] = Q[qs] K^T         (Q rows read in perm5 order: register r of half hf
+//                                         is query 32qs + 16(r/8) + 8hf + r%8)
+//             P = 2^(S scale log2e - lse2[query]), hidden -> 0
+//   P wave:   dV^T += dO^T P             (dO^T by transposed reads, P in bf16)
+//   dS wave:  dP[qs] = dO[qs] V^T,  dS = P * (dP - delta[query]),
+//             dK^T += Q^T dS             (Q^T by transposed reads, dS in bf16)
+// The scores are computed by both waves (a fifth product per pair instead of an exchange
+// of P through LDS, which holds the staged tiles); the dS wave carries three products and
+// the P wave two, and on each SIMD one wave's vector work runs under the other's products.
+// The P waves also stage the tiles.  LDS stage: Q row copy | Q transposed-read copy | dO row copy | dO transposed-read copy |
 // lse2[64] | delta[64].
 // ---------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreadsBwd) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsBwdK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_bf16(BwdArgs a) {
   constexpr int BQ = kBwdStep;
-  constexpr int NT = kThreadsBwd;
+  constexpr int NT = kThreadsBwdK / 2;  // the P waves stage the tiles
   constexpr int DG = D / 8;
   constexpr int CH = BQ * DG / NT;
   constexpr int ROWS = NT / DG;
@@ -384,6 +420,7 @@ void bwd_dkdv_bf16(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool ds_wave = wave >= 4;  // wave-uniform role
   const int li = lane & 31;
   const int hf = lane >> 5;
 
@@ -403,20 +440,20 @@ void bwd_dkdv_bf16(BwdArgs a) {
   const float* del_h = a.delta + bh * a.Lq;
 
   const int k0 = int(kt_idx) * kBwdBlockK;
-  const int kw = k0 + 32 * wave;
+  const int kw = k0 + 32 * (wave & 3);
   const int kj = kw + li;
   const bool k_ok = kj < a.Lk;
   const bool wave_live = kw < a.Lk;
 
-  // K^T and V^T right operands (column = this lane's key, half hf supplies head dims
-  // 16c + 8hf .. +7 of chunk c), held for the whole query walk.
+  // K^T right operand of S (both waves) and V^T right operand of dP (dS wave): column =
+  // this lane's key, half hf supplies head dims 16c + 8hf .. +7 of chunk c.
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     u32x4 wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
     if (k_ok) {
       wk = ld16(kb + int64_t(kj) * a.sk[2] + 16 * c + 8 * hf);
-      wv = ld16(vb + int64_t(kj) * a.sv[2] + 16 * c + 8 * hf);
+      if (ds_wave) wv = ld16(vb + int64_t(kj) * a.sv[2] + 16 * c + 8 * hf);
     }
     kf[c] = __builtin_bit_cast(bf16x8, wk);
     vf[c] = __builtin_bit_cast(bf16x8, wv);
@@ -471,101 +508,118 @@ void bwd_dkdv_bf16(BwdArgs a) {
   const int tfrag = tr_lane_offset(lane, TP);
   const float c2 = a.scale_log2;
 
-  f32x16 dk[D / 32], dv[D / 32];
+  // dV^T (P wave) or dK^T (dS wave)
+  f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
-  auto compute = [&](int t) {
+  // One query tile for one role.  The 32-query sub-tiles are taken one at a time (their
+  // scores, then their P or dS), so only one sub-tile of S and dP is live at once.
+  auto compute = [&](auto role, int t) {
+    constexpr bool DS = decltype(role)::value;
     const char* st = lds + (t & 1) * STAGE;
     const int qt0 = t * BQ;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[qs][r] = dp[qs][r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const bf16x8 qa = __builtin_bit_cast(bf16x8, ld16(st + rfrag + qs * 32 * RP + 32 * c));
-        s[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[c], s[qs], 0, 0, 0);
-      }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const bf16x8 da =
-            __builtin_bit_cast(bf16x8, ld16(st + OFF_DR + rfrag + qs * 32 * RP + 32 * c));
-        dp[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[c], dp[qs], 0, 0, 0);
-      }
-
-    // chunk c holds queries qt0 + 16c + 8hf + e (e = 0..7): registers 8(c%2)+e of qs = c/2
     const float* lse2s = reinterpret_cast<const float*>(st + OFF_LSE);
     const float* dels = reinterpret_cast<const float*>(st + OFF_DEL);
     const bool edge = CAUSAL && qt0 < kw + 31;
-    bf16x8 pf[4], dsf[4];
+    bf16x8 opf[4];  // P (P wave) or dS (dS wave): chunk c = queries 16c + 8hf + 0..7
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int qc = 16 * c + 8 * hf;  // first query of the run, within the tile
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + qc);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + qc + 4);
-      const f32x4 d0 = *reinterpret_cast<const f32x4*>(dels + qc);
-      const f32x4 d1 = *reinterpret_cast<const f32x4*>(dels + qc + 4);
-      const float lrun[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      const float drun[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      u32x4 wp, wd;
+    for (int qs = 0; qs < 2; ++qs) {
+      f32x16 sc, dp;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float p[2], ds[2];
+      for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
+      // Operands are read two chunks ahead of their products; the fences keep that order
+      // (near the register limit the scheduler would otherwise read each operand just
+      // before its product and wait out the full LDS latency every time).
+      bf16x8 qa[3], da[3];
+      auto read = [&](int c) {
+        qa[c % 3] = __builtin_bit_cast(bf16x8, ld16(st + rfrag + qs * 32 * RP + 32 * c));
+        if (DS)
+          da[c % 3] = __builtin_bit_cast(bf16x8, ld16(st + OFF_DR + rfrag + qs * 32 * RP + 32 * c));
+      };
+      read(0);
+      read(1);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int qs = c >> 1, r = 8 * (c & 1) + 2 * e + u;
-          const int qrow = qt0 + qc + 2 * e + u;
-          float xv = __builtin_fmaf(s[qs][r], c2, -lrun[2 * e + u]);
-          if (edge || MASK) {
-            bool hide = false;
-            if (CAUSAL) hide = kj > qrow;
-            if (MASK) hide = hide || !k_ok || qrow >= a.Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
-            if (hide) xv = -INFINITY;
-          }
-          p[u] = exp2_fast(xv);
-          ds[u] = p[u] * (dp[qs][r] - drun[2 * e + u]);
+      for (int c = 0; c < D / 16; ++c) {
+        if (c + 2 < D / 16) read(c + 2);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kf[c], sc, 0, 0, 0);
+        if (DS) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c % 3], vf[c], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int c = 2 * qs + g;
+        const int qc = 16 * c + 8 * hf;  // first query of the run, within the tile
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + qc);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + qc + 4);
+        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+        if (DS) {
+          d0 = *reinterpret_cast<const f32x4*>(dels + qc);
+          d1 = *reinterpret_cast<const f32x4*>(dels + qc + 4);
         }
-        wp[e] = pack_bf16(p[0], p[1]);
-        wd[e] = pack_bf16(ds[0], ds[1]);
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float o[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int i = 2 * e + u, r = 8 * g + i;
+            const int qrow = qt0 + qc + i;
+            float xv = __builtin_fmaf(sc[r], c2, -(i < 4 ? l0[i] : l1[i - 4]));
+            if (edge || MASK) {
+              bool hide = false;
+              if (CAUSAL) hide = kj > qrow;
+              if (MASK) hide = hide || !k_ok || qrow >= a.Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
+              if (hide) xv = -INFINITY;
+            }
+            const float p = exp2_fast(xv);
+            o[u] = DS ? p * (dp[r] - (i < 4 ? d0[i] : d1[i - 4])) : p;
+          }
+          w[e] = pack_bf16(o[0], o[1]);
+        }
+        opf[c] = __builtin_bit_cast(bf16x8, w);
       }
-      pf[c] = __builtin_bit_cast(bf16x8, wp);
-      dsf[c] = __builtin_bit_cast(bf16x8, wd);
     }
-    const char* qtr = st + OFF_QT + tfrag;
-    const char* dtr = st + OFF_DT + tfrag;
+    // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); operands two products ahead
+    const char* ltr = st + (DS ? OFF_QT : OFF_DT) + tfrag;
+    constexpr int NP = 4 * (D / 32);  // products, i = c * (D / 32) + dt
+    bf16x8 ta[3];
+    auto tread = [&](int i) { ta[i % 3] = tr_operand<TP>(ltr, i / (D / 32), i % (D / 32)); };
+    __builtin_amdgcn_sched_barrier(0);
+    tread(0);
+    tread(1);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<TP>(dtr, c, dt), pf[c],
-                                                         dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<TP>(qtr, c, dt), dsf[c],
-                                                         dk[dt], 0, 0, 0);
-      }
+    for (int i = 0; i < NP; ++i) {
+      if (i + 2 < NP) tread(i + 2);
+      acc[i % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i % 3], opf[i / (D / 32)],
+                                                                  acc[i % (D / 32)], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  load(tbeg);
-  store(tbeg & 1);
-  __syncthreads();
-  for (int t = tbeg; t < ntiles; ++t) {
-    load(t + 1);
-    // the wave's keys are visible to some query of the tile iff its last query >= kw
-    if (wave_live && (!CAUSAL || t * BQ + BQ - 1 >= kw)) compute(t);
-    store((t + 1) & 1);
+  // The two roles run separate loops with the same barriers, one per query tile, so that
+  // the staging registers (P waves only) never count against the dS waves' products.  A
+  // wave's keys are visible to some query of tile t iff the tile's last query is >= kw.
+  if (!ds_wave) {
+    load(tbeg);
+    store(tbeg & 1);
     __syncthreads();
-  }
-
-  if (k_ok) {
-    store_row_bf16<D>(dkb + int64_t(kj) * a.sdk[2], dk, a.scale, hf);
-    store_row_bf16<D>(dvb + int64_t(kj) * a.sdv[2], dv, 1.f, hf);
+    for (int t = tbeg; t < ntiles; ++t) {
+      load(t + 1);
+      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 >= kw)) compute(std::false_type{}, t);
+      store((t + 1) & 1);
+      __syncthreads();
+    }
+    if (k_ok) store_row_bf16<D>(dvb + int64_t(kj) * a.sdv[2], acc, 1.f, hf);
+  } else {
+    __syncthreads();
+    for (int t = tbeg; t < ntiles; ++t) {
+      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 >= kw)) compute(std::true_type{}, t);
+      __syncthreads();
+    }
+    if (k_ok) store_row_bf16<D>(dkb + int64_t(kj) * a.sdk[2], acc, a.scale, hf);
   }
 }
 
@@ -574,12 +628,12 @@ hipError_t launch_pair(const BwdArgs& a, unsigned grid_q, unsigned grid_k, hipSt
   void* args[] = {const_cast<BwdArgs*>(&a)};
   if (grid_q) {
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_bf16<D, CAUSAL, MASK>),
-                                         dim3(grid_q), dim3(kThreadsBwd), args, 0, s);
+                                         dim3(grid_q), dim3(kThreadsBwdQ), args, 0, s);
     if (e != hipSuccess) return e;
   }
   if (grid_k)
     return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_bf16<D, CAUSAL, MASK>),
-                           dim3(grid_k), dim3(kThreadsBwd), args, 0, s);
+                           dim3(grid_k), dim3(kThreadsBwdK), args, 0, s);
   return hipSuccess;
 }
 

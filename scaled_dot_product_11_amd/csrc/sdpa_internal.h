@@ -66,12 +66,13 @@ constexpr int64_t lds_bytes_f32(int D) {
 hipError_t launch_fwd(const Problem& p, hipStream_t stream);
 
 // ---- backward (bf16) ----
-// Two kernels, each a workgroup of 4 waves (one per SIMD): the dQ kernel owns 128 query
-// rows of one (b, h) and walks key tiles of 64; the dK/dV kernel owns 128 keys and walks
-// query tiles of 64.  The dQ kernel runs first and also writes delta = rowsum(dO * O),
-// which the dK/dV kernel reads.
-constexpr int kThreadsBwd = 256;
-constexpr int kBwdBlockQ = 128;
+// Two kernels of 8 waves (two per SIMD): the dQ kernel owns 256 query rows of one (b, h)
+// and walks key tiles of 64; the dK/dV kernel owns 128 keys and walks query tiles of 64.
+// The dQ kernel runs first and also writes delta = rowsum(dO * O), which the dK/dV kernel
+// reads.
+constexpr int kThreadsBwdQ = 512;
+constexpr int kThreadsBwdK = 512;
+constexpr int kBwdBlockQ = 256;
 constexpr int kBwdBlockK = 128;
 constexpr int kBwdStep = 64;
 // LDS per workgroup of the two backward kernels: two stages, each holding the streamed
