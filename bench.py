@@ -45,13 +45,17 @@ BWD_METRIC = "causal SDPA bwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 
 TRAFFIC_BYTES = 484244 * 1024
 TRAFFIC_KERNEL_SHA256 = "e61d876b7a1cce9d"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
+# The same for one backward call (dq and dk/dv kernels together).
+BWD_TRAFFIC_BYTES = 1647942 * 1024
+BWD_TRAFFIC_KERNEL_SHA256 = "a1ad613950f96445"
+BWD_KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_bwd_gfx950.hip")
 
 
-def measured_traffic():
+def measured_traffic(source=KERNEL_SOURCE, sha=TRAFFIC_KERNEL_SHA256, nbytes=TRAFFIC_BYTES):
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
+    with open(source, "rb") as f:
         current = hashlib.sha256(f.read()).hexdigest()
-    return TRAFFIC_BYTES if current.startswith(TRAFFIC_KERNEL_SHA256) else None
+    return nbytes if current.startswith(sha) else None
 
 
 def visible_pairs(Lq, Lk, causal):
@@ -196,6 +200,18 @@ def bench_workload(wl, steps, warmup):
             "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12}
 
 
+def copy_calibration(mib):
+    """One elementwise kernel that reads `mib` MiB and writes `mib` MiB: the HBM counters
+    read for it give their scale factor against known traffic."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
 def bench_bwd(wl, steps, warmup):
     import torch
     import workloads as W
@@ -248,7 +264,9 @@ def main_bwd(args, props):
         # one step is two kernels (dq, then dk/dv) timed together by events on the stream
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(BWD_KERNEL_SOURCE, BWD_TRAFFIC_KERNEL_SHA256,
+                                                 BWD_TRAFFIC_BYTES),
                      "kernels": "bwd_dq_bf16 + bwd_dkdv_bf16",
                      "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
                      "kernel_ms_median": round(r["kernel_ms_median"], 4)},
@@ -256,6 +274,8 @@ def main_bwd(args, props):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_bwd(wl)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
     print(json.dumps(line), flush=True)
 
 
@@ -321,14 +341,7 @@ def main():
         line["cpu_baseline"] = cpu_baseline(wl)
 
     if args.copy_calibration_mib:
-        # one elementwise kernel that reads N bytes and writes N bytes: the HBM counters
-        # read for it give their scale factor against known traffic
-        n = args.copy_calibration_mib * 2 ** 20 // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
+        copy_calibration(args.copy_calibration_mib)
 
     if args.report:
         rows = [r]

@@ -114,9 +114,11 @@ const char* sdpa_strerror(int status);
 /*
  * sdpa_bwd -- gradients dq, dk, dv of sdpa_fwd for an upstream gradient dout, bf16 only.
  *
- * The derivative of the forward above by the chain rule through its steps (the pages
- * define no backward; the forward's exported lse is what it reuses, as the fused
- * forward of "Optimizing DeepSeek Sparse Attention with FlashInfer" returns its lse):
+ * The derivative of the forward above by the chain rule through its steps.  The pages
+ * define no backward; it reuses the forward's exported lse, as the fused forward of
+ * "[flashinfer] FlashInfer, Cake DSA 커널 최적화: Sparse Attention 성능 2배 향상" returns its
+ * lse for its backward (section 2, In-place Strided dout 처리, which also takes a strided
+ * dout without copying it, as here):
  *
  *   P[i,j]  = exp(scale * q_i.k_j - lse[i]) for visible (i,j), else 0  (all 0 if lse = -inf)
  *   dv[j,:] = sum_i P[i,j] dout[i,:]

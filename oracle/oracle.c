@@ -31,7 +31,8 @@
  * The backward (oracle_sdpa_bwd) is the derivative of the same function, written out with
  * the chain rule through the five steps: none of the pages defines a backward, but its
  * result is fixed by the forward; it is the step after the forward that the exported LSE
- * exists for (the FlashInfer DSA article's fused forward returns `lse` for its backward).
+ * exists for (the fused forward of "[flashinfer] FlashInfer, Cake DSA 커널 최적화: Sparse
+ * Attention 성능 2배 향상" returns `lse` for its backward, section 2).
  *
  * Parity pins: see tests/test_oracle_*.py (brute force, closed forms, invariants,
  * hand-derived golden cases, the library's fp64 math-backend SDPA; for the backward,

@@ -8,8 +8,9 @@
 //   dQ = scale * dS k,   dK = scale * dS^T q.
 // Because out = P v, delta_i also equals sum_d dO_id out_id, which costs one pass over
 // dO and out instead of a pass over P.  P itself is rebuilt from the scores and the
-// per-row log-sum-exp the forward exported (the DSA article's fused forward returns its
-// lse for the backward): P_ij = exp(scale q_i.k_j - lse_i), zero at hidden positions and
+// per-row log-sum-exp the forward exported (the fused forward of "[flashinfer] FlashInfer,
+// Cake DSA 커널 최적화: Sparse Attention 성능 2배 향상" returns its lse for the backward,
+// section 2): P_ij = exp(scale q_i.k_j - lse_i), zero at hidden positions and
 // in rows with lse = -inf (no visible key), so the [L, L] matrices never reach memory.
 //
 // Two kernels, launched back to back on one stream, with no atomics and no workspace
@@ -73,26 +74,6 @@ struct BwdArgs {
 };
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
-// With one wave per SIMD nothing else hides the latency of an LDS read, and left alone the
-// scheduler reads each operand just before its product.  This orders the NMFMA products
-// of the current scheduling region behind their reads (READS operand reads per product)
-// with a lookahead of AHEAD products: the reads of the first AHEAD products, then one
-// product per READS reads, then the last AHEAD products.
-template <int NMFMA, int READS, int AHEAD>
-__device__ inline void pipeline_lds_reads() {
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS * AHEAD, 0);
-#pragma unroll
-  for (int i = 0; i < NMFMA - AHEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, AHEAD, 0);
-}
 
 __device__ inline float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -289,23 +270,26 @@ void bwd_dq_bf16(BwdArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = dp[kt][r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, ld16(st + rfrag + kt * 32 * RP + 32 * c));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kt], 0, 0, 0);
-      }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 vf =
-            __builtin_bit_cast(bf16x8, ld16(st + OFF_V + rfrag + kt * 32 * RP + 32 * c));
-        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[c], dp[kt], 0, 0, 0);
-      }
-    pipeline_lds_reads<4 * (D / 16), 1, 4>();
+    // Products i = 4c + 2kt + {0: S, 1: dP}, their K or V operand read two products
+    // ahead; the fences keep that order.
+    constexpr int NP = 4 * (D / 16);
+    bf16x8 fa[3];
+    auto fread = [&](int i) {
+      const int c = i >> 2, kt = (i >> 1) & 1;
+      fa[i % 3] = __builtin_bit_cast(
+          bf16x8, ld16(st + ((i & 1) ? OFF_V : 0) + rfrag + kt * 32 * RP + 32 * c));
+    };
     __builtin_amdgcn_sched_barrier(0);
+    fread(0);
+    fread(1);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i + 2 < NP) fread(i + 2);
+      const int c = i >> 2, kt = (i >> 1) & 1;
+      if (i & 1) dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i % 3], dof[c], dp[kt], 0, 0, 0);
+      else s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i % 3], qf[c], s[kt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // x = S scale log2e - lse2 in base-2 units; hidden keys -> -inf.
     float x[2][16];
@@ -356,15 +340,21 @@ void bwd_dq_bf16(BwdArgs a) {
       }
       dsf[c] = __builtin_bit_cast(bf16x8, w);
     }
+    // dQ^T += K^T dS^T, operands two products ahead (i = c * (D / 32) + dt)
     const char* ktr = st + OFF_KT + tfrag;
+    constexpr int NQ = 4 * (D / 32);
+    bf16x8 ta[3];
+    auto tread = [&](int i) { ta[i % 3] = tr_operand<TP>(ktr, i / (D / 32), i % (D / 32)); };
     __builtin_amdgcn_sched_barrier(0);
+    tread(0);
+    tread(1);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<TP>(ktr, c, dt), dsf[c],
-                                                         dq[dt], 0, 0, 0);
-    pipeline_lds_reads<4 * (D / 32), 2, 4>();
+    for (int i = 0; i < NQ; ++i) {
+      if (i + 2 < NQ) tread(i + 2);
+      dq[i % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i % 3], dsf[i / (D / 32)],
+                                                                 dq[i % (D / 32)], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   load(0);
