@@ -10,11 +10,15 @@
  *                                                      scale * q[b,h,i,:].k[b,h,j,:]
  *   lse[b,h,i]   = log sum_{visible j} exp(scale * q[b,h,i,:].k[b,h,j,:])   (natural log)
  *
- *   key j is visible to query i iff (!is_causal || j <= i) && (mask == NULL || mask[b,h,i,j] != 0)
+ *   key j is visible to query i iff causal(i, j) && (mask == NULL || mask[b,h,i,j] != 0),
+ *   causal(i, j) = true (SDPA_CAUSAL_NONE), j <= i (SDPA_CAUSAL_TOP_LEFT) or
+ *                  j <= i + Lk - Lq (SDPA_CAUSAL_BOTTOM_RIGHT)
  *
  * A query row with no visible key returns an all-zero output row and lse = -inf (the safe
  * softmax of the math-backend section; no NaN is ever produced for finite inputs).  The
- * causal triangle is aligned top-left (j <= i) also when Lq != Lk.
+ * pages draw the causal triangle only for Lq == Lk, where both alignments agree; top-left
+ * is the default reading, and bottom-right (the last query sees every key) serves queries
+ * that continue a longer key sequence, such as decoding.
  *
  * Rank-3 and rank-4 inputs take the same fused kernel (the PyTorch 2.14 note on rank-3
  * SDPA inputs): a rank-3 [N,L,D] input is computed exactly as the rank-4 input
@@ -52,7 +56,15 @@ enum sdpa_status {
   SDPA_ERR_STRIDE = 6,   /* innermost stride != 1, or a negative stride                  */
   SDPA_ERR_ALIGN = 7,    /* q/k/v/out base or row stride not 16-byte aligned, lse not 4  */
   SDPA_ERR_SCALE = 8,    /* scale is NaN or infinite                                     */
-  SDPA_ERR_DEVICE = 9    /* the stream's device is not gfx950, or the launch failed      */
+  SDPA_ERR_DEVICE = 9,   /* the stream's device is not gfx950, or the launch failed      */
+  SDPA_ERR_CAUSAL = 10   /* causal mode not an sdpa_causal value                         */
+};
+
+/* Causal modes (the is_causal / causal arguments). */
+enum sdpa_causal {
+  SDPA_CAUSAL_NONE = 0,
+  SDPA_CAUSAL_TOP_LEFT = 1,     /* key j visible to query i iff j <= i                   */
+  SDPA_CAUSAL_BOTTOM_RIGHT = 2  /* iff j <= i + Lk - Lq: the last query sees every key  */
 };
 
 /*
@@ -82,8 +94,8 @@ enum sdpa_status {
  *   scale         finite multiplier of q.k applied after the dot product (the usual
  *                 choice is 1/sqrt(D); any finite value, including 0 or negative, is
  *                 accepted).
- *   is_causal     nonzero: hide keys j > i (top-left triangle); combines with a mask
- *                 by intersection.
+ *   is_causal     an sdpa_causal mode (0 none, 1 top-left, 2 bottom-right); combines
+ *                 with a mask by intersection.  Other values: SDPA_ERR_CAUSAL.
  *   mask          NULL, or a device pointer to bytes, nonzero = visible, 0 = hidden.
  *   dtype         an sdpa_dtype.
  *   stream        a hipStream_t (NULL = the null stream of the current device).
@@ -110,6 +122,52 @@ int sdpa_check(const void* q, const void* k, const void* v, const void* out, con
 
 /* sdpa_strerror -- a static, human-readable message for a status code. */
 const char* sdpa_strerror(int status);
+
+/*
+ * sdpa_fwd_varlen -- the fused forward over a batch of sequences of different lengths
+ * packed along the token axis (the cu_seqlens layout of the packed-document kernels in
+ * "[flashinfer] FlashInfer, Cake DSA 커널 최적화: Sparse Attention 성능 2배 향상", section 3,
+ * Varlen 인덱스 준비 최적화).  Sequence s owns query tokens cu_seqlens_q[s] ..
+ * cu_seqlens_q[s+1]-1 and key tokens cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1; each of its
+ * heads is the problem of sdpa_fwd on those rows alone (no attention across sequences),
+ * with the causal mode applied per sequence (bottom-right uses that sequence's own lengths).
+ *
+ *   q, out        device [total_q, H, D], k, v device [total_k, H, D], of `dtype`, any token
+ *                 and head strides, unit dim stride, bases and strides (bytes) multiples of
+ *                 16.  q/out may be NULL when nothing is computed, k/v when total_k == 0.
+ *   lse           NULL, or device [H, total_q] contiguous floats (natural log, -inf for
+ *                 rows with no visible key), 4-byte aligned.
+ *   cu_seqlens_q, cu_seqlens_k
+ *                 device int32 arrays of nseq + 1 non-decreasing offsets from 0 to total_q
+ *                 (total_k), 4-byte aligned.  Their contents are not validated on the host;
+ *                 the kernel clamps every offset into [0, total] and makes them
+ *                 non-decreasing, so any contents keep every access in bounds (rows of a
+ *                 sequence past the clamped range are then left unwritten).
+ *   nseq          number of sequences (>= 0).
+ *   max_seqlen_q  an upper bound of every cu_seqlens_q[s+1] - cu_seqlens_q[s], at most
+ *                 total_q (it sizes the launch; query rows past it are not written).
+ *   total_q, total_k, H, D
+ *                 sizes; D in {64, 128}; (total_k + 64) times the token stride of k (and of
+ *                 v) must stay below 2 GiB.
+ *   strides       12 element strides: (token, head, dim) for q, k, v, out.
+ *   scale, causal, dtype, stream
+ *                 as in sdpa_fwd (causal: an sdpa_causal mode).
+ *
+ * One kernel launch; nothing allocated, freed or synchronised.  Returns a status as
+ * sdpa_fwd does; nseq * H * total_q * max_seqlen_q == 0 is a no-op returning SDPA_OK.
+ */
+int sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t nseq,
+                    int64_t max_seqlen_q, int64_t total_q, int64_t total_k, int64_t H, int64_t D,
+                    const int64_t* strides, float scale, int causal, int dtype, void* stream);
+
+/* sdpa_fwd_varlen_check -- the host-side validation of sdpa_fwd_varlen alone (no stream,
+ * no HIP call, no device read). */
+int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int64_t nseq, int64_t max_seqlen_q,
+                          int64_t total_q, int64_t total_k, int64_t H, int64_t D,
+                          const int64_t* strides, float scale, int causal, int dtype);
 
 /*
  * sdpa_bwd -- gradients dq, dk, dv of sdpa_fwd for an upstream gradient dout, bf16 only.
@@ -149,7 +207,7 @@ const char* sdpa_strerror(int status);
  *   strides       9*rank element strides, tensor-major: q, k, v, out, dout, dq, dk, dv,
  *                 mask, each in its own axis order as in sdpa_fwd.
  *   scale, is_causal, mask
- *                 exactly as passed to sdpa_fwd.
+ *                 exactly as passed to sdpa_fwd (all three causal modes).
  *   dtype         SDPA_BF16 (anything else: SDPA_ERR_DTYPE).
  *   stream        a hipStream_t (NULL = the null stream of the current device).
  *
@@ -170,7 +228,7 @@ int sdpa_bwd_check(const void* q, const void* k, const void* v, const void* out,
                    int is_causal, const uint8_t* mask, int dtype);
 
 /*
- * Launch plan (host-only introspection of the tile scheduler).
+ * Launch plan (host-only introspection of the tile scheduler of sdpa_fwd).
  *
  * A work item is one (b*H + h, query tile) pair: block_m query rows of one head, which
  * walk the key/value tiles of block_n keys.  With is_causal the items are issued

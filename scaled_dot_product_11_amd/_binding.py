@@ -14,16 +14,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdpa_gfx950.so")
 
 SDPA_F32, SDPA_BF16 = 0, 1
+SDPA_CAUSAL_NONE, SDPA_CAUSAL_TOP_LEFT, SDPA_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 _DTYPES = {torch.float32: SDPA_F32, torch.bfloat16: SDPA_BF16}
 
 STATUS_NAMES = {
     0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_RANK", 3: "SDPA_ERR_SHAPE",
     4: "SDPA_ERR_HEAD_DIM", 5: "SDPA_ERR_DTYPE", 6: "SDPA_ERR_STRIDE", 7: "SDPA_ERR_ALIGN",
-    8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE",
+    8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE", 10: "SDPA_ERR_CAUSAL",
 }
 
-EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_bwd", "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan",
-           "sdpa_plan_item")
+EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
+           "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
 
 
 class SdpaError(RuntimeError):
@@ -65,6 +66,12 @@ def load_library():
     lib.sdpa_bwd.restype = ctypes.c_int
     lib.sdpa_bwd_check.argtypes = bwd_common
     lib.sdpa_bwd_check.restype = ctypes.c_int
+    varlen_common = [vp] * 7 + [i64] * 6 + [ctypes.POINTER(i64), ctypes.c_float, ctypes.c_int,
+                                        ctypes.c_int]
+    lib.sdpa_fwd_varlen.argtypes = varlen_common + [vp]
+    lib.sdpa_fwd_varlen.restype = ctypes.c_int
+    lib.sdpa_fwd_varlen_check.argtypes = varlen_common
+    lib.sdpa_fwd_varlen_check.restype = ctypes.c_int
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
     lib.sdpa_strerror.restype = ctypes.c_char_p
     lib.sdpa_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -84,6 +91,19 @@ def sdpa_strerror(status: int) -> str:
 def _raise_on(status):
     if status != 0:
         raise SdpaError(status, sdpa_strerror(status))
+
+
+def causal_mode(is_causal):
+    """The C ABI causal mode for a bool (True = top-left) or an int 0 / 1 / 2."""
+    if isinstance(is_causal, bool):
+        return SDPA_CAUSAL_TOP_LEFT if is_causal else SDPA_CAUSAL_NONE
+    return int(is_causal)
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _sizes(q, k):
@@ -111,7 +131,7 @@ def _marshal(q, k, v, out, lse, mask, scale, is_causal):
         scale = 1.0 / math.sqrt(D)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
             None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr,
-            float(scale), 1 if is_causal else 0, mask_ptr, dtype]
+            float(scale), causal_mode(is_causal), mask_ptr, dtype]
     return args, mask_keep
 
 
@@ -144,8 +164,8 @@ def sdpa_fwd(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, mask=N
 
     q: [N,Lq,D] or [B,H,Lq,D]; k, v: [N,Lk,D] or [B,H,Lk,D]; bf16 or fp32 cuda tensors with
     unit innermost stride (any other strides).  mask: optional bool/uint8 tensor
-    broadcastable to q.shape[:-1] + (Lk,), True/nonzero = visible.  scale defaults to
-    1/sqrt(D).  out/lse are allocated when not given (out contiguous, lse float32
+    broadcastable to q.shape[:-1] + (Lk,), True/nonzero = visible.  is_causal: False/True
+    (top-left) or a mode 0 / 1 / 2 (2 = bottom-right).  scale defaults to 1/sqrt(D).  out/lse are allocated when not given (out contiguous, lse float32
     [..., Lq]).  Returns (out, lse) -- lse is None when return_lse is False and no lse
     tensor was passed.  The kernel is enqueued on `stream` (default: torch's current
     stream of q's device); nothing is synchronised.
@@ -156,9 +176,7 @@ def sdpa_fwd(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, mask=N
     if lse is None and return_lse:
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     args, _keep = _marshal(q, k, v, out, lse, mask, scale, is_causal)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
         status = load_library().sdpa_fwd(*args, handle)
     _raise_on(status)
@@ -214,17 +232,78 @@ def sdpa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, delta=None, *, 
     arr = (ctypes.c_int64 * len(strides))(*strides)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
         status = load_library().sdpa_bwd(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-            rank, B, H, Lq, Lk, D, arr, float(scale), 1 if is_causal else 0, mask_ptr,
+            rank, B, H, Lq, Lk, D, arr, float(scale), causal_mode(is_causal), mask_ptr,
             _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return dq, dk, dv
+
+
+def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None, lse=None, *,
+                    scale=None, is_causal=False, stream=None, return_lse=True):
+    """Fused forward over packed variable-length sequences through the C ABI
+    `sdpa_fwd_varlen`.
+
+    q: [total_q, H, D], k, v: [total_k, H, D] (bf16 or fp32 cuda tensors, unit dim stride);
+    cu_seqlens_q / cu_seqlens_k: int32 cuda tensors of nseq + 1 offsets; max_seqlen_q: an
+    int bound of the query lengths (it sizes the launch).  is_causal: False/True (top-left)
+    or a mode 0 / 1 / 2, applied per sequence.  out ([total_q, H, D]) and lse ([H, total_q]
+    float32) are allocated when not given.  Returns (out, lse).
+    """
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k and v must be [tokens, H, D]")
+    if tuple(k.shape) != tuple(v.shape) or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k and v must be [total_k, H, D] with q's H and D")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same nseq + 1 >= 1 entries")
+    ts = (q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
+    if any(t is not None and t.device.type != "cuda" for t in ts):
+        raise ValueError("sdpa_fwd_varlen runs on the GPU only: every tensor must be on a cuda device")
+    if len({t.device for t in ts if t is not None}) != 1:
+        raise ValueError("all tensors must be on the same device")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    elif lse is not None and (tuple(lse.shape) != (H, total_q) or lse.dtype != torch.float32 or
+                              not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [H, total_q]")
+    strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride()]
+    arr = (ctypes.c_int64 * 12)(*strides)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        status = load_library().sdpa_fwd_varlen(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), cu_seqlens_q.data_ptr(),
+            cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, int(max_seqlen_q), total_q,
+            total_k, H, D, arr, float(scale), causal_mode(is_causal), _DTYPES.get(q.dtype, -1),
+            handle)
+    _raise_on(status)
+    return out, lse
+
+
+def sdpa_fwd_varlen_check(ptrs, nseq, max_seqlen_q, total_q, total_k, H, D, strides, scale,
+                          causal, dtype) -> int:
+    """The C ABI `sdpa_fwd_varlen_check` on raw integers: ptrs = the 7 pointers (q, k, v,
+    out, lse, cu_seqlens_q, cu_seqlens_k) as ints, strides a list of 12 ints.  Host-only."""
+    arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
+    return load_library().sdpa_fwd_varlen_check(*ptrs, nseq, max_seqlen_q, total_q, total_k, H,
+                                                D, arr, float(scale), int(causal), int(dtype))
 
 
 def sdpa_bwd_check(ptrs, rank, B, H, Lq, Lk, D, strides, scale, is_causal, mask_ptr,

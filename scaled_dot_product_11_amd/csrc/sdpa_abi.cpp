@@ -62,6 +62,7 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
   if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
+  if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
 
   const int64_t bh = B * H;
   const int64_t bm = sdpa::block_m(dtype);
@@ -119,7 +120,10 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
     memcpy(p->so, s4[3], sizeof p->so);
     memcpy(p->sm, s4[4], sizeof p->sm);
     p->scale = scale;
-    p->causal = is_causal ? 1 : 0;
+    p->causal = is_causal;
+    p->varlen = 0;
+    p->cu_q = p->cu_k = nullptr;
+    p->nseq = p->max_seqlen_q = 0;
     p->dtype = dtype;
   }
   return SDPA_OK;
@@ -136,6 +140,7 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
   if (st != SDPA_OK) return st;
   if (dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
+  if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t bh = B * H;
   if (bh != 0 && ((Lq + sdpa::kBwdBlockQ - 1) / sdpa::kBwdBlockQ > kMaxDim / bh ||
                   (Lk + sdpa::kBwdBlockK - 1) / sdpa::kBwdBlockK > kMaxDim / bh))
@@ -207,7 +212,85 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
     memcpy(p->sdv, s4[DV], sizeof p->sdv);
     memcpy(p->sm, s4[M], sizeof p->sm);
     p->scale = scale;
-    p->causal = is_causal ? 1 : 0;
+    p->causal = is_causal;
+  }
+  return SDPA_OK;
+}
+
+// Validate a packed variable-length forward and build its problem.  Tensors are
+// [tokens, H, D]; strides holds (token, head, dim) for q, k, v, out.
+int normalise_varlen(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const int32_t* cu_q, const int32_t* cu_k, int64_t nseq,
+                     int64_t max_seqlen_q, int64_t total_q, int64_t total_k, int64_t H,
+                     int64_t D, const int64_t* strides, float scale, int causal, int dtype,
+                     sdpa::Problem* p) {
+  if (nseq < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0) return SDPA_ERR_SHAPE;
+  if (nseq >= kMaxDim || H > kMaxDim || total_q > kMaxDim || total_k > kMaxDim)
+    return SDPA_ERR_SHAPE;
+  if (max_seqlen_q > total_q) return SDPA_ERR_SHAPE;
+  if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+  if (!strides) return SDPA_ERR_NULL;
+  if (!isfinite(scale)) return SDPA_ERR_SCALE;
+  if (causal < SDPA_CAUSAL_NONE || causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
+  const int64_t heads = nseq * H;
+  const int64_t q_tiles = (max_seqlen_q + sdpa::block_m(dtype) - 1) / sdpa::block_m(dtype);
+  if (heads != 0 && q_tiles > kMaxDim / heads) return SDPA_ERR_SHAPE;  // grid size
+  const bool any_rows = heads != 0 && total_q != 0 && max_seqlen_q != 0;
+
+  int64_t s4[4][4];
+  for (int t = 0; t < 4; ++t) {
+    const int64_t* st = strides + 3 * t;
+    s4[t][0] = 0;
+    s4[t][1] = st[1];
+    s4[t][2] = st[0];
+    s4[t][3] = st[2];
+    for (int a = 0; a < 4; ++a)
+      if (s4[t][a] < 0) return SDPA_ERR_STRIDE;
+    if (s4[t][3] != 1) return SDPA_ERR_STRIDE;
+  }
+  if (any_rows && (!q || !out || !cu_q || !cu_k)) return SDPA_ERR_NULL;
+  if (any_rows && total_k != 0 && (!k || !v)) return SDPA_ERR_NULL;
+  const int64_t esize = dtype == SDPA_BF16 ? 2 : 4;
+  const void* bases[4] = {q, k, v, out};
+  for (int t = 0; t < 4; ++t) {
+    if (!any_rows || (!bases[t] && (t == 1 || t == 2) && total_k == 0)) continue;
+    if (!aligned(bases[t], 16)) return SDPA_ERR_ALIGN;
+    for (int a = 1; a < 3; ++a)
+      if ((s4[t][a] * esize) % 16 != 0) return SDPA_ERR_ALIGN;
+  }
+  if ((lse && !aligned(lse, 4)) || (cu_q && !aligned(cu_q, 4)) || (cu_k && !aligned(cu_k, 4)))
+    return SDPA_ERR_ALIGN;
+  // a sequence's K/V rows are addressed with 32-bit byte offsets from its first row
+  if (any_rows)
+    for (int t = 1; t <= 2; ++t)
+      if (s4[t][2] > kMaxDim / esize / (total_k + sdpa::block_n(dtype))) return SDPA_ERR_SHAPE;
+
+  if (p) {
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->out = const_cast<void*>(out);
+    p->lse = const_cast<float*>(lse);
+    p->mask = nullptr;
+    p->cu_q = cu_q;
+    p->cu_k = cu_k;
+    p->B = 1;
+    p->H = H;
+    p->Lq = total_q;
+    p->Lk = total_k;
+    p->D = D;
+    p->nseq = nseq;
+    p->max_seqlen_q = max_seqlen_q;
+    memcpy(p->sq, s4[0], sizeof p->sq);
+    memcpy(p->sk, s4[1], sizeof p->sk);
+    memcpy(p->sv, s4[2], sizeof p->sv);
+    memcpy(p->so, s4[3], sizeof p->so);
+    memset(p->sm, 0, sizeof p->sm);
+    p->scale = scale;
+    p->causal = causal;
+    p->varlen = 1;
+    p->dtype = dtype;
   }
   return SDPA_OK;
 }
@@ -259,6 +342,30 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
 }
 
+int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int64_t nseq, int64_t max_seqlen_q,
+                          int64_t total_q, int64_t total_k, int64_t H, int64_t D,
+                          const int64_t* strides, float scale, int causal, int dtype) {
+  return normalise_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q,
+                          total_q, total_k, H, D, strides, scale, causal, dtype, nullptr);
+}
+
+int sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t nseq,
+                    int64_t max_seqlen_q, int64_t total_q, int64_t total_k, int64_t H, int64_t D,
+                    const int64_t* strides, float scale, int causal, int dtype, void* stream) {
+  sdpa::Problem p;
+  const int st = normalise_varlen(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, nseq,
+                                  max_seqlen_q, total_q, total_k, H, D, strides, scale, causal,
+                                  dtype, &p);
+  if (st != SDPA_OK) return st;
+  if (p.nseq * p.H * p.Lq * p.max_seqlen_q == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
 int sdpa_bwd_check(const void* q, const void* k, const void* v, const void* out,
                    const void* dout, const float* lse, const void* dq, const void* dk,
                    const void* dv, const float* delta, int rank, int64_t B, int64_t H,
@@ -297,6 +404,8 @@ const char* sdpa_strerror(int status) {
       return "q/k/v/out base pointers and outer strides must be 16-byte aligned, lse 4-byte";
     case SDPA_ERR_SCALE: return "scale must be finite";
     case SDPA_ERR_DEVICE: return "device is not gfx950 or the kernel launch failed";
+    case SDPA_ERR_CAUSAL:
+      return "causal mode must be 0 (none), 1 (top-left) or 2 (bottom-right)";
     default: return "unknown sdpa status";
   }
 }

@@ -71,6 +71,7 @@ struct BwdArgs {
   float scale;       // multiplies dQ and dK
   float scale_log2;  // scale * log2(e): scores in base-2 units
   int32_t mask_vec8; // mask rows may be read 8 bytes at a time
+  int32_t coff;      // causal: key j visible to query i iff j <= i + coff
 };
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -213,10 +214,12 @@ void bwd_dq_bf16(BwdArgs a) {
   if (q_ok && hf == 0) a.delta[bh * a.Lq + qi] = delta;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  const int coff = a.coff;
   int kend = a.Lk;
-  if (CAUSAL) kend = min(kend, min(q0 + kBwdBlockQ, a.Lq));
+  if (CAUSAL) kend = max(0, min(kend, min(q0 + kBwdBlockQ, a.Lq) + coff));
   const int ntiles = (kend + BN - 1) / BN;
-  const int wtiles = !wave_live ? 0 : CAUSAL ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
+  const int wlast = qw + 31 + coff;  // last key any row of the wave may see (causal)
+  const int wtiles = !wave_live ? 0 : CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
 
   // Staging of K and V: buffer loads with the whole byte offset in the per-lane offset,
   // checked by the hardware against the head's extent (rows past the end read zero; a
@@ -297,7 +300,7 @@ void bwd_dq_bf16(BwdArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[kt][r] = __builtin_fmaf(s[kt][r], c2, -lse2);
-    const bool edge = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > a.Lk);
+    const bool edge = (CAUSAL && k0 + BN - 1 > qw + coff) || (k0 + BN > a.Lk);
     if (edge || MASK) {
       uint64_t mbits[4] = {~0ull, ~0ull, ~0ull, ~0ull};
       if (MASK && q_ok) {
@@ -321,7 +324,7 @@ void bwd_dq_bf16(BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
           bool hide = key >= a.Lk;
-          if (CAUSAL) hide = hide || key > qi;
+          if (CAUSAL) hide = hide || key > qi + coff;
           if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
           if (hide) x[kt][r] = -INFINITY;
         }
@@ -450,9 +453,11 @@ void bwd_dkdv_bf16(BwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // Query tiles of the walk: with a causal mask, queries before k0 see none of the keys.
+  // Query tiles of the walk: with a causal mask, queries i with i + coff < k0 see none of
+  // the keys.
+  const int coff = a.coff;
   const int ntiles = (a.Lq + BQ - 1) / BQ;
-  const int tbeg = CAUSAL ? min(k0 / BQ, ntiles) : 0;
+  const int tbeg = CAUSAL ? min(max(0, k0 - coff) / BQ, ntiles) : 0;
 
   const int q_rowb = int(a.sq[2]) * 2, d_rowb = int(a.sdo[2]) * 2;
   const int q_ext = a.Lq > 0 ? (a.Lq - 1) * q_rowb + 2 * D : 0;
@@ -513,7 +518,7 @@ void bwd_dkdv_bf16(BwdArgs a) {
     const int qt0 = t * BQ;
     const float* lse2s = reinterpret_cast<const float*>(st + OFF_LSE);
     const float* dels = reinterpret_cast<const float*>(st + OFF_DEL);
-    const bool edge = CAUSAL && qt0 < kw + 31;
+    const bool edge = CAUSAL && qt0 + coff < kw + 31;
     bf16x8 opf[4];  // P (P wave) or dS (dS wave): chunk c = queries 16c + 8hf + 0..7
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
@@ -560,7 +565,7 @@ void bwd_dkdv_bf16(BwdArgs a) {
             float xv = __builtin_fmaf(sc[r], c2, -(i < 4 ? l0[i] : l1[i - 4]));
             if (edge || MASK) {
               bool hide = false;
-              if (CAUSAL) hide = kj > qrow;
+              if (CAUSAL) hide = kj > qrow + coff;
               if (MASK) hide = hide || !k_ok || qrow >= a.Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
               if (hide) xv = -INFINITY;
             }
@@ -591,14 +596,14 @@ void bwd_dkdv_bf16(BwdArgs a) {
 
   // The two roles run separate loops with the same barriers, one per query tile, so that
   // the staging registers (P waves only) never count against the dS waves' products.  A
-  // wave's keys are visible to some query of tile t iff the tile's last query is >= kw.
+  // wave's keys are visible to some query of tile t iff the tile's last query + coff >= kw.
   if (!ds_wave) {
     load(tbeg);
     store(tbeg & 1);
     __syncthreads();
     for (int t = tbeg; t < ntiles; ++t) {
       load(t + 1);
-      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 >= kw)) compute(std::false_type{}, t);
+      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw)) compute(std::false_type{}, t);
       store((t + 1) & 1);
       __syncthreads();
     }
@@ -606,7 +611,7 @@ void bwd_dkdv_bf16(BwdArgs a) {
   } else {
     __syncthreads();
     for (int t = tbeg; t < ntiles; ++t) {
-      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 >= kw)) compute(std::true_type{}, t);
+      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw)) compute(std::true_type{}, t);
       __syncthreads();
     }
     if (k_ok) store_row_bf16<D>(dkb + int64_t(kj) * a.sdk[2], acc, a.scale, hf);
@@ -670,6 +675,7 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   a.scale_log2 = p.scale * kLog2e;
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
                 p.sm[1] % 8 == 0 && p.sm[2] % 8 == 0;
+  a.coff = p.causal == 2 ? int32_t(p.Lk - p.Lq) : 0;
   const unsigned gq = unsigned(int64_t(a.q_items) * a.bh_count);
   const unsigned gk = unsigned(int64_t(a.k_items) * a.bh_count);
   if (p.D == 64) return launch_bwd_d<64>(a, p.causal != 0, gq, gk, stream);

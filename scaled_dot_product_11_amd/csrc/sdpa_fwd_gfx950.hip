@@ -40,6 +40,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Kernel arguments: canonical (b, h, row) strides in elements; the innermost stride is 1.
+// Packed variable-length problems use the row stride for tokens and the head stride for
+// heads; Lq and Lk are then the total token counts and bh_count = sequences * H.
 struct Args {
   const void* q;
   const void* k;
@@ -47,11 +49,56 @@ struct Args {
   void* out;
   float* lse;
   const uint8_t* mask;
+  const int32_t* cu_q;  // variable-length only: sequence s owns query tokens cu_q[s] ..
+  const int32_t* cu_k;  // cu_q[s+1]-1 and key tokens cu_k[s] .. cu_k[s+1]-1
   int64_t sq[3], sk[3], sv[3], so[3], sm[3];
   int32_t H, Lq, Lk, q_tiles, bh_count;
   float scale_log2;  // scale * log2(e): scores are kept in base-2 units
   int32_t mask_vec8; // mask rows may be read 8 bytes at a time
+  int32_t bottom_right;  // causal alignment: key j visible iff j <= i + (Lk - Lq)
 };
+
+// The rows one work item serves: the element offsets of row 0 of its head in q, k, v, out
+// and the mask, the index of row 0's lse, its row counts, and the causal offset (key j is
+// visible to query i iff j <= i + coff: 0 aligns the triangle top-left, Lk - Lq
+// bottom-right).  Dense problems: head (b, h) of the strided tensors.  Packed
+// variable-length problems: head h of sequence s of the [tokens, H, D] tensors, the lse
+// laid out [H, total query tokens]; the sequence offsets are clamped into [0, total] and
+// made non-decreasing, so that any contents of cu_q / cu_k keep every access in bounds.
+struct Item {
+  int64_t q, k, v, o, m, lse;
+  int Lq, Lk, coff;
+};
+
+template <bool VARLEN>
+__device__ inline Item item_of(const Args& a, int64_t bh) {
+  Item it;
+  if (!VARLEN) {
+    const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
+    it.q = b * a.sq[0] + h * a.sq[1];
+    it.k = b * a.sk[0] + h * a.sk[1];
+    it.v = b * a.sv[0] + h * a.sv[1];
+    it.o = b * a.so[0] + h * a.so[1];
+    it.m = b * a.sm[0] + h * a.sm[1];
+    it.lse = bh * a.Lq;
+    it.Lq = a.Lq;
+    it.Lk = a.Lk;
+  } else {
+    const int64_t s = bh / a.H, h = bh - (bh / a.H) * a.H;
+    const int q_lo = min(max(a.cu_q[s], 0), a.Lq), q_hi = min(max(a.cu_q[s + 1], q_lo), a.Lq);
+    const int k_lo = min(max(a.cu_k[s], 0), a.Lk), k_hi = min(max(a.cu_k[s + 1], k_lo), a.Lk);
+    it.q = q_lo * a.sq[2] + h * a.sq[1];
+    it.o = q_lo * a.so[2] + h * a.so[1];
+    it.k = k_lo * a.sk[2] + h * a.sk[1];
+    it.v = k_lo * a.sv[2] + h * a.sv[1];
+    it.m = 0;
+    it.lse = h * a.Lq + q_lo;
+    it.Lq = q_hi - q_lo;
+    it.Lk = k_hi - k_lo;
+  }
+  it.coff = a.bottom_right ? it.Lk - it.Lq : 0;
+  return it;
+}
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -133,7 +180,7 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-template <int D, bool CAUSAL, bool MASK, bool POS>
+template <int D, bool CAUSAL, bool MASK, bool POS, bool VARLEN>
 __global__ __launch_bounds__(kThreadsBf16) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16(Args a) {
   constexpr int BN = kBlockNBf16;
@@ -160,18 +207,20 @@ void fwd_bf16(Args a) {
 
   int64_t bh, qt;
   decode_item(blockIdx.x, a.bh_count, a.q_tiles, CAUSAL, &bh, &qt);
-  const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.sq[0] + h * a.sq[1];
-  const char* kb = static_cast<const char*>(a.k) + 2 * (b * a.sk[0] + h * a.sk[1]);
-  const char* vb = static_cast<const char*>(a.v) + 2 * (b * a.sv[0] + h * a.sv[1]);
-  uint16_t* ob = static_cast<uint16_t*>(a.out) + b * a.so[0] + h * a.so[1];
-  const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
-
+  const Item it = item_of<VARLEN>(a, bh);
+  const int Lq = it.Lq, Lk = it.Lk, coff = it.coff;
   const int q0 = int(qt) * kBlockMBf16;
+  if (VARLEN && q0 >= Lq) return;  // a tile past this sequence's rows (whole workgroup)
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + it.q;
+  const char* kb = static_cast<const char*>(a.k) + 2 * it.k;
+  const char* vb = static_cast<const char*>(a.v) + 2 * it.v;
+  uint16_t* ob = static_cast<uint16_t*>(a.out) + it.o;
+  const uint8_t* mb = MASK ? a.mask + it.m : nullptr;
+
   const int qw = q0 + 32 * slice;  // first query row of this wave
   const int qi = qw + li;          // this lane's query row
-  const bool q_ok = qi < a.Lq;
-  const bool wave_live = qw < a.Lq;
+  const bool q_ok = qi < Lq;
+  const bool wave_live = qw < Lq;
 
   // Q^T operand fragments, held for the whole key walk: chunk c covers head dims
   // 16c..16c+15, half hf supplies dims 16c+8hf..16c+8hf+7.
@@ -187,11 +236,12 @@ void fwd_bf16(Args a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // Key tiles the workgroup stages (keys that can be visible to some stored row), and
-  // the tiles this wave computes on (with a causal mask: tiles 0 .. (qw + 31) / 64).
-  int kend = a.Lk;
-  if (CAUSAL) kend = min(kend, min(q0 + kBlockMBf16, a.Lq));
+  // the tiles this wave computes on (with a causal mask: tiles 0 .. (qw + 31 + coff) / 64).
+  int kend = Lk;
+  if (CAUSAL) kend = max(0, min(kend, min(q0 + kBlockMBf16, Lq) + coff));
   const int ntiles = (kend + BN - 1) / BN;
-  const int wtiles = !wave_live ? 0 : CAUSAL ? min(ntiles, (qw + 31) / BN + 1) : ntiles;
+  const int wlast = qw + 31 + coff;  // last key any row of the wave may see (causal)
+  const int wtiles = !wave_live ? 0 : CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
 
   // ---- global -> register -> LDS staging of K and V tiles.  All 512 threads stage: the
   // loads of K(t+1) and V(t) are issued at the start of step t, K(t+1) is written to LDS
@@ -204,8 +254,8 @@ void fwd_bf16(Args a) {
   // the stores are exact.  Offsets stay below 2^31: the caller guarantees that
   // (Lk + 64) rows of K and of V span less than 2 GiB. ----
   const int k_rowb = int(a.sk[2]) * 2, v_rowb = int(a.sv[2]) * 2;  // row strides, bytes
-  const int k_ext = a.Lk > 0 ? (a.Lk - 1) * k_rowb + 2 * D : 0;
-  const int v_ext = a.Lk > 0 ? (a.Lk - 1) * v_rowb + 2 * D : 0;
+  const int k_ext = Lk > 0 ? (Lk - 1) * k_rowb + 2 * D : 0;
+  const int v_ext = Lk > 0 ? (Lk - 1) * v_rowb + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, k_ext, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, v_ext, kBufferFlags);
   const int ld_row = tid / DG, ld_col = tid % DG;  // this thread's first chunk
@@ -341,7 +391,7 @@ void fwd_bf16(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][r] *= a.scale_log2;
     }
-    const bool edge = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > a.Lk);
+    const bool edge = (CAUSAL && k0 + BN - 1 > qw + coff) || (k0 + BN > Lk);
     if (edge || MASK) {
       // Mask bytes of this lane's keys: runs of 8 at k0 + 32kt + 16g + 8hf.
       uint64_t mbits[4] = {~0ull, ~0ull, ~0ull, ~0ull};
@@ -350,12 +400,12 @@ void fwd_bf16(Args a) {
 #pragma unroll
         for (int run = 0; run < 4; ++run) {
           const int key0 = k0 + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
-          if (a.mask_vec8 && key0 + 8 <= a.Lk) {
+          if (a.mask_vec8 && key0 + 8 <= Lk) {
             mbits[run] = *reinterpret_cast<const uint64_t*>(mrow + key0);
           } else {
             uint64_t w = 0;
             for (int e = 0; e < 8; ++e)
-              if (key0 + e < a.Lk) w |= uint64_t(mrow[key0 + e]) << (8 * e);
+              if (key0 + e < Lk) w |= uint64_t(mrow[key0 + e]) << (8 * e);
             mbits[run] = w;
           }
         }
@@ -365,8 +415,8 @@ void fwd_bf16(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
-          bool hide = key >= a.Lk;
-          if (CAUSAL) hide = hide || key > qi;
+          bool hide = key >= Lk;
+          if (CAUSAL) hide = hide || key > qi + coff;
           if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
           if (hide) s[kt][r] = -INFINITY;
         }
@@ -462,7 +512,7 @@ void fwd_bf16(Args a) {
         *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * g + 4 * hf) = u32x2{w[0], w[1]};
       }
     if (a.lse && hf == 0)
-      a.lse[bh * a.Lq + qi] =
+      a.lse[it.lse + qi] =
           l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
@@ -472,7 +522,7 @@ void fwd_bf16(Args a) {
 // fp32 kernel: fp32 MFMA 32x32x2 (true fp32 products, fp32 accumulation) for both
 // products; same decomposition as the bf16 kernel, probabilities stay fp32.
 // ---------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool VARLEN>
 __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   constexpr int DG = D / 4;                             // 16-byte groups per row
   constexpr int CH = kBlockNF32 * DG / kThreadsF32;           // chunks per thread per tile
@@ -491,26 +541,28 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
 
   int64_t bh, qt;
   decode_item(blockIdx.x, a.bh_count, a.q_tiles, CAUSAL, &bh, &qt);
-  const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const float* qb = static_cast<const float*>(a.q) + b * a.sq[0] + h * a.sq[1];
-  const float* kb = static_cast<const float*>(a.k) + b * a.sk[0] + h * a.sk[1];
-  const float* vb = static_cast<const float*>(a.v) + b * a.sv[0] + h * a.sv[1];
-  float* ob = static_cast<float*>(a.out) + b * a.so[0] + h * a.so[1];
-  const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
-
+  const Item it = item_of<VARLEN>(a, bh);
+  const int Lq = it.Lq, Lk = it.Lk, coff = it.coff;
   const int q0 = int(qt) * kBlockMF32;
+  if (VARLEN && q0 >= Lq) return;  // a tile past this sequence's rows (whole workgroup)
+  const float* qb = static_cast<const float*>(a.q) + it.q;
+  const float* kb = static_cast<const float*>(a.k) + it.k;
+  const float* vb = static_cast<const float*>(a.v) + it.v;
+  float* ob = static_cast<float*>(a.out) + it.o;
+  const uint8_t* mb = MASK ? a.mask + it.m : nullptr;
+
   const int qw = q0 + wave * 32;
   const int qi = qw + li;
-  const bool q_ok = qi < a.Lq;
-  const bool wave_live = qw < a.Lq;
+  const bool q_ok = qi < Lq;
+  const bool wave_live = qw < Lq;
 
   // Q^T operand: chunk c supplies head dim 2c + hf.
   float qf[D / 2];
 #pragma unroll
   for (int c = 0; c < D / 2; ++c) qf[c] = q_ok ? qb[int64_t(qi) * a.sq[2] + 2 * c + hf] : 0.f;
 
-  int kend = a.Lk;
-  if (CAUSAL) kend = min(kend, min(q0 + kBlockMF32, a.Lq));
+  int kend = Lk;
+  if (CAUSAL) kend = max(0, min(kend, min(q0 + kBlockMF32, Lq) + coff));
   const int ntiles = (kend + kBlockNF32 - 1) / kBlockNF32;
 
   u32x4 kreg[CH], vreg[CH];
@@ -521,7 +573,7 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
       const int c = tid + p * kThreadsF32;
       const int row = c / DG, col = (c % DG) * 4;
       const int key = k0 + row;
-      const bool ok = key < a.Lk;
+      const bool ok = key < Lk;
       kreg[p] = ok ? ld16(kb + int64_t(key) * a.sk[2] + col) : u32x4{0, 0, 0, 0};
       vreg[p] = ok ? ld16(vb + int64_t(key) * a.sv[2] + col) : u32x4{0, 0, 0, 0};
     }
@@ -559,7 +611,7 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
     const float* ks = lds + buf * STAGE;
     const float* vs = ks + K_ELEMS;
     const int k0 = t * kBlockNF32;
-    const bool tile_live = wave_live && (!CAUSAL || k0 <= qw + 31);
+    const bool tile_live = wave_live && (!CAUSAL || k0 <= qw + 31 + coff);
 
     if (tile_live) {
       // S^T = K . Q^T ; lane (li, hf) register r of sub-tile kt holds key
@@ -569,7 +621,7 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-        const bool sub_live = !CAUSAL || (k0 + 32 * kt <= qw + 31);
+        const bool sub_live = !CAUSAL || (k0 + 32 * kt <= qw + 31 + coff);
         if (sub_live) {
 #pragma unroll
           for (int c = 0; c < D / 2; ++c)
@@ -579,7 +631,7 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
       }
 
       float x[2][16];
-      const bool edge = (CAUSAL && k0 + kBlockNF32 - 1 > qw) || (k0 + kBlockNF32 > a.Lk);
+      const bool edge = (CAUSAL && k0 + kBlockNF32 - 1 > qw + coff) || (k0 + kBlockNF32 > Lk);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -587,8 +639,8 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
           float xv = s[kt][r] * a.scale_log2;
           if (edge || MASK) {
             const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
-            bool hide = key >= a.Lk;
-            if (CAUSAL) hide = hide || key > qi;
+            bool hide = key >= Lk;
+            if (CAUSAL) hide = hide || key > qi + coff;
             if (MASK && !hide && q_ok) hide = mb[int64_t(qi) * a.sm[2] + key] == 0;
             if (hide) xv = -INFINITY;
           }
@@ -651,28 +703,32 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
         *reinterpret_cast<u32x4*>(orow + 32 * dt + 8 * g + 4 * hf) = w;
       }
     if (a.lse && hf == 0)
-      a.lse[bh * a.Lq + qi] =
+      a.lse[it.lse + qi] =
           l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <int D, bool CAUSAL, bool MASK, bool VARLEN>
 hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Args*>(&a)};
   const void* fn;
   if (dtype == 1)
-    fn = a.scale_log2 > 0.f ? reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, true>)
-                            : reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, false>);
+    fn = a.scale_log2 > 0.f ? reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, true, VARLEN>)
+                            : reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, false, VARLEN>);
   else
-    fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK>);
+    fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK, VARLEN>);
   return hipLaunchKernel(fn, dim3(grid), dim3(block_threads(dtype)), args, 0, stream);
 }
 
 template <int D>
-hipError_t launch_d(const Args& a, int dtype, bool causal, unsigned grid, hipStream_t s) {
+hipError_t launch_d(const Args& a, int dtype, bool causal, bool varlen, unsigned grid,
+                    hipStream_t s) {
+  if (varlen)  // packed sequences take no mask
+    return causal ? launch<D, true, false, true>(a, dtype, grid, s)
+                  : launch<D, false, false, true>(a, dtype, grid, s);
   const bool m = a.mask != nullptr;
-  if (causal) return m ? launch<D, true, true>(a, dtype, grid, s) : launch<D, true, false>(a, dtype, grid, s);
-  return m ? launch<D, false, true>(a, dtype, grid, s) : launch<D, false, false>(a, dtype, grid, s);
+  if (causal) return m ? launch<D, true, true, false>(a, dtype, grid, s) : launch<D, true, false, false>(a, dtype, grid, s);
+  return m ? launch<D, false, true, false>(a, dtype, grid, s) : launch<D, false, false, false>(a, dtype, grid, s);
 }
 
 }  // namespace
@@ -685,6 +741,8 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.out = p.out;
   a.lse = p.lse;
   a.mask = p.mask;
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
   for (int i = 0; i < 3; ++i) {
     a.sq[i] = p.sq[i];
     a.sk[i] = p.sk[i];
@@ -695,14 +753,17 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.H = int32_t(p.H);
   a.Lq = int32_t(p.Lq);
   a.Lk = int32_t(p.Lk);
-  a.q_tiles = int32_t((p.Lq + block_m(p.dtype) - 1) / block_m(p.dtype));
-  a.bh_count = int32_t(p.B * p.H);
+  // dense: B*H heads of Lq rows; packed: nseq*H heads of up to max_seqlen_q rows
+  const int64_t rows = p.varlen ? p.max_seqlen_q : p.Lq;
+  a.q_tiles = int32_t((rows + block_m(p.dtype) - 1) / block_m(p.dtype));
+  a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);
   a.scale_log2 = p.scale * kLog2e;
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
                 p.sm[1] % 8 == 0 && p.sm[2] % 8 == 0;
+  a.bottom_right = p.causal == 2;
   const unsigned grid = unsigned(int64_t(a.q_tiles) * a.bh_count);
-  if (p.D == 64) return launch_d<64>(a, p.dtype, p.causal != 0, grid, stream);
-  return launch_d<128>(a, p.dtype, p.causal != 0, grid, stream);
+  if (p.D == 64) return launch_d<64>(a, p.dtype, p.causal != 0, p.varlen != 0, grid, stream);
+  return launch_d<128>(a, p.dtype, p.causal != 0, p.varlen != 0, grid, stream);
 }
 
 }  // namespace sdpa

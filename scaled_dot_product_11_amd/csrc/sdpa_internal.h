@@ -23,7 +23,9 @@ constexpr int block_n(int dtype) { return dtype == 1 ? kBlockNBf16 : kBlockNF32;
 constexpr int block_threads(int dtype) { return dtype == 1 ? kThreadsBf16 : kThreadsF32; }
 
 // Rank-3 [N,L,D] and rank-4 [B,H,L,D] inputs both become this (b, h, row, col) view;
-// every stride is in elements of the tensor's own type.
+// every stride is in elements of the tensor's own type.  Packed variable-length inputs
+// [tokens, H, D] use the h and row strides (b stride 0), Lq / Lk are the token totals,
+// and cu_q / cu_k (device, nseq + 1 entries) delimit the sequences.
 struct Problem {
   const void* q;
   const void* k;
@@ -31,10 +33,14 @@ struct Problem {
   void* out;
   float* lse;
   const uint8_t* mask;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
   int64_t B, H, Lq, Lk, D;
+  int64_t nseq, max_seqlen_q;  // packed only
   int64_t sq[4], sk[4], sv[4], so[4], sm[4];
   float scale;
-  int causal;
+  int causal;  // 0 none, 1 top-left (j <= i), 2 bottom-right (j <= i + Lk - Lq)
+  int varlen;
   int dtype;
 };
 

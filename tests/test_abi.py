@@ -309,3 +309,71 @@ def test_bwd_rejects_before_any_device_call():
     assert st == HEAD
     st = lib.sdpa_bwd(*([None] * 10), 4, 0, 3, 100, 90, 64, arr, 0.125, 1, None, 1, None)
     assert st == OK  # B == 0: nothing to do
+
+
+# ---- causal modes and sdpa_fwd_varlen_check ----------------------------------------------
+
+CAUSAL_ERR = 10
+
+
+def test_causal_modes():
+    for mode in (0, 1, 2):
+        assert check(**args4(is_causal=mode)) == OK
+        assert bcheck(**bargs(is_causal=mode)) == OK
+    for mode in (-1, 3, 7):
+        assert check(**args4(is_causal=mode)) == CAUSAL_ERR
+        assert bcheck(**bargs(is_causal=mode)) == CAUSAL_ERR
+    assert "bottom-right" in sd.sdpa_strerror(CAUSAL_ERR)
+
+
+def vargs(nseq=3, max_q=50, total_q=100, total_k=90, H=4, D=64, dtype=sd.SDPA_BF16, **over):
+    """Arguments of sdpa_fwd_varlen_check: q, k, v, out, lse, cu_q, cu_k; [tokens, H, D]."""
+    q = [H * D, D, 1]
+    a = dict(ptrs=[A + i * 0x10000 for i in range(7)], nseq=nseq, max_seqlen_q=max_q,
+             total_q=total_q, total_k=total_k, H=H, D=D, strides=q + q + q + q, scale=0.125,
+             causal=2, dtype=dtype)
+    a.update(over)
+    return a
+
+
+def vcheck(**kw):
+    return sd.sdpa_fwd_varlen_check(**kw)
+
+
+def test_varlen_check():
+    assert vcheck(**vargs()) == OK
+    assert vcheck(**vargs(dtype=sd.SDPA_F32, D=128)) == OK
+    assert vcheck(**vargs(D=96)) == HEAD
+    assert vcheck(**vargs(dtype=3)) == DTYPE
+    assert vcheck(**vargs(causal=4)) == CAUSAL_ERR
+    assert vcheck(**vargs(nseq=-1)) == SHAPE
+    assert vcheck(**vargs(max_q=101)) == SHAPE  # longer than every token
+    assert vcheck(**vargs(strides=None)) == NULL
+    assert vcheck(**vargs(scale=float("inf"))) == SCALE
+    for i in (0, 1, 2, 3, 5, 6):  # q, k, v, out, cu_q, cu_k are required; lse is not
+        a = vargs()
+        a["ptrs"] = list(a["ptrs"])
+        a["ptrs"][i] = None
+        assert vcheck(**a) == NULL, i
+    a = vargs()
+    a["ptrs"] = list(a["ptrs"])
+    a["ptrs"][4] = None
+    assert vcheck(**a) == OK
+    for i, bad in ((0, A + 8), (3, A + 4), (4, A + 2), (5, A + 2)):
+        a = vargs()
+        a["ptrs"] = list(a["ptrs"])
+        a["ptrs"][i] = bad
+        assert vcheck(**a) == ALIGN, i
+    s = vargs()["strides"]
+    for idx, val, want in ((2, 2, STRIDE), (0, -64, STRIDE), (0, 68, ALIGN), (4, 60, ALIGN)):
+        a = vargs()
+        a["strides"] = list(s)
+        a["strides"][idx] = val
+        assert vcheck(**a) == want, (idx, val)
+    # empty problems need no pointers at all
+    assert vcheck(**vargs(nseq=0, max_q=0, total_q=0, total_k=0, ptrs=[None] * 7)) == OK
+    # k rows (plus a tile) must span less than 2 GiB from a sequence's first row
+    big = vargs(total_k=2 ** 20, D=128)
+    big["strides"] = list(big["strides"])
+    big["strides"][3] = 1024
+    assert vcheck(**big) == SHAPE

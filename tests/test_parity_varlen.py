@@ -1,0 +1,187 @@
+"""GPU parity of the bottom-right causal alignment (forward and backward) and of packed
+variable-length batches (sdpa_fwd_varlen), through the C ABI, against the fp64 oracle.
+
+Bottom-right visibility (key j visible to query i iff j <= i + Lk - Lq) is handed to the
+oracle as an explicit boolean mask, the lower triangle shifted by Lk - Lq, so the oracle's
+pinned mask path is the reference.  A packed batch is, by definition, each sequence's
+heads computed on their own rows: the oracle runs per sequence on [1, H, L_s, D] views.
+Tolerances are those of test_parity (forward) and test_parity_bwd (backward).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import sdpa_bwd_oracle, sdpa_oracle
+from scaled_dot_product_11_amd import sdpa_bwd, sdpa_fwd, sdpa_fwd_varlen
+from test_parity import DEV, compare, to_dev
+from test_parity_bwd import compare_grads
+
+pytestmark = pytest.mark.gpu
+
+BOTTOM_RIGHT = 2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def br_mask(Lq, Lk):
+    """Bottom-right causal visibility as a bool [Lq, Lk] mask."""
+    return torch.ones(Lq, Lk, dtype=torch.bool).tril(Lk - Lq)
+
+
+def rand4(seed, B, H, Lq, Lk, D, dtype):
+    g = torch.Generator().manual_seed(seed)
+    return W.draw_qkv(g, (B, H, Lq, D), (B, H, Lk, D), dtype=dtype)
+
+
+SHAPES = [(1, 1), (5, 300), (77, 300), (300, 77), (129, 129), (64, 200), (200, 64), (256, 1000)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bottom_right_forward(dtype, D):
+    for n, (Lq, Lk) in enumerate(SHAPES):
+        q, k, v = rand4(100 + n, 2, 3, Lq, Lk, D, dtype)
+        out, lse = sdpa_fwd(to_dev(q), to_dev(k), to_dev(v), is_causal=BOTTOM_RIGHT)
+        torch.cuda.synchronize()
+        ro, rl = sdpa_oracle(q, k, v, mask=br_mask(Lq, Lk))
+        compare(out, lse, ro, rl, dtype, f"bottom-right D={D} Lq={Lq} Lk={Lk}")
+        if Lq == Lk:  # both alignments are the same triangle: same kernel work, same bits
+            o1, l1 = sdpa_fwd(to_dev(q), to_dev(k), to_dev(v), is_causal=True)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, out) and torch.equal(l1, lse)
+
+
+def test_bottom_right_with_mask_intersects():
+    q, k, v = rand4(7, 2, 2, 90, 250, 64, torch.bfloat16)
+    g = torch.Generator().manual_seed(8)
+    m = torch.rand((2, 2, 90, 250), generator=g) < 0.4
+    m[0, 1, 5] = False
+    out, lse = sdpa_fwd(to_dev(q), to_dev(k), to_dev(v), mask=to_dev(m), is_causal=BOTTOM_RIGHT)
+    torch.cuda.synchronize()
+    ro, rl = sdpa_oracle(q, k, v, mask=m & br_mask(90, 250))
+    compare(out, lse, ro, rl, torch.bfloat16, "bottom-right + mask")
+
+
+@pytest.mark.parametrize("Lq", [1, 3, 16])
+def test_decode_shapes(Lq):
+    """A few new queries at the end of a long key sequence: bottom-right causal."""
+    q, k, v = rand4(20 + Lq, 1, 8, Lq, 4096, 128, torch.bfloat16)
+    out, lse = sdpa_fwd(to_dev(q), to_dev(k), to_dev(v), is_causal=BOTTOM_RIGHT)
+    torch.cuda.synchronize()
+    ro, rl = sdpa_oracle(q, k, v, mask=br_mask(Lq, 4096))
+    compare(out, lse, ro, rl, torch.bfloat16, f"decode Lq={Lq}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bottom_right_backward(D):
+    for n, (Lq, Lk) in enumerate([(5, 300), (77, 300), (300, 77), (129, 129), (200, 64)]):
+        q, k, v = rand4(200 + n, 2, 2, Lq, Lk, D, torch.bfloat16)
+        dout = W.upstream_grad(300 + n, q)
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        out, lse = sdpa_fwd(qd, kd, vd, is_causal=BOTTOM_RIGHT)
+        bufs = [torch.full(t.shape, float("nan"), dtype=t.dtype, device=DEV) for t in (q, k, v)]
+        got = sdpa_bwd(qd, kd, vd, out, to_dev(dout), lse, *bufs, is_causal=BOTTOM_RIGHT)
+        torch.cuda.synchronize()
+        ref = sdpa_bwd_oracle(q, k, v, dout, mask=br_mask(Lq, Lk))
+        compare_grads(got, ref, f"bottom-right bwd D={D} Lq={Lq} Lk={Lk}")
+        vis = br_mask(Lq, Lk)
+        dq, dk, dv = (t.cpu() for t in got)
+        assert torch.all(dq[:, :, ~vis.any(-1)] == 0)  # rows before the triangle
+        assert torch.all(dk[:, :, ~vis.any(-2)] == 0) and torch.all(dv[:, :, ~vis.any(-2)] == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# packed variable-length batches
+
+def seq_view(t, lo, hi):
+    """Rows lo..hi-1 of a packed [tokens, H, D] tensor as the [1, H, L, D] view."""
+    return t[lo:hi].transpose(0, 1).unsqueeze(0)
+
+
+def check_varlen(q, k, v, cq, ck, out, lse, causal, dtype, where, rows=None):
+    """Every sequence against the oracle on its own rows (or on `rows` of each sequence:
+    a dict s -> flat row ids of its [1, H, L_s] problem)."""
+    cq, ck = cq.tolist(), ck.tolist()
+    out, lse = out.cpu(), lse.cpu()
+    for s in range(len(cq) - 1):
+        qs, ks, vs = (seq_view(t, a, b) for t, a, b in ((q, cq[s], cq[s + 1]), (k, ck[s], ck[s + 1]),
+                                                        (v, ck[s], ck[s + 1])))
+        Lq, Lk = cq[s + 1] - cq[s], ck[s + 1] - ck[s]
+        mask = br_mask(Lq, Lk) if causal == BOTTOM_RIGHT else None
+        got_o, got_l = seq_view(out, cq[s], cq[s + 1])[0], lse[:, cq[s]:cq[s + 1]]
+        r = None if rows is None else rows.get(s)
+        if rows is not None and r is None:
+            continue
+        ro, rl = sdpa_oracle(qs, ks, vs, mask=mask, is_causal=causal == 1, rows=r)
+        if r is None:
+            compare(got_o[None], got_l[None], ro, rl, dtype, f"{where} seq {s}")
+        else:
+            H, D = got_o.shape[0], got_o.shape[-1]
+            idx = torch.from_numpy(r)
+            compare(got_o.reshape(-1, D)[idx], got_l.reshape(-1)[idx], ro, rl, dtype,
+                    f"{where} seq {s} sampled")
+
+
+Q_LENGTHS = [0, 1, 77, 256, 300, 5, 129]
+K_LENGTHS = [3, 1, 77, 300, 256, 0, 129]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [0, 1, 2], ids=["none", "top_left", "bottom_right"])
+def test_varlen_small(dtype, D, causal):
+    q, k, v, cq, ck = W.packed(31 + D + causal, Q_LENGTHS, K_LENGTHS, 4, D, dtype=dtype)
+    out = torch.full(q.shape, float("nan"), dtype=dtype, device=DEV)
+    out, lse = sdpa_fwd_varlen(to_dev(q), to_dev(k), to_dev(v), to_dev(cq), to_dev(ck),
+                               max(Q_LENGTHS), out=out, is_causal=causal)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any(), "every output row is written"
+    check_varlen(q, k, v, cq, ck, out, lse, causal, dtype, f"varlen D={D} causal={causal}")
+
+
+def test_varlen_equals_dense_bitwise():
+    """Equal lengths: the packed batch [B*L, H, D] is the dense [B, L, H, D] problem."""
+    B, L, H, D = 3, 300, 4, 128
+    q, k, v, cq, ck = W.packed(41, [L] * B, [L] * B, H, D)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    ov, lv = sdpa_fwd_varlen(qd, kd, vd, to_dev(cq), to_dev(ck), L, is_causal=True)
+    dense = [t.view(B, L, H, D).transpose(1, 2) for t in (qd, kd, vd)]
+    od, ld = sdpa_fwd(*dense, is_causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ov.view(B, L, H, D), od.transpose(1, 2))
+    assert torch.equal(lv.view(H, B, L), ld.permute(1, 0, 2))
+
+
+def test_varlen_strided_from_packed_qkv():
+    """q, k, v as slices of one [tokens, 3, H, D] buffer: token stride 3*H*D."""
+    lengths = [70, 1, 200]
+    T, H, D = sum(lengths), 2, 64
+    g = torch.Generator().manual_seed(51)
+    qkv = torch.randn(T, 3, H, D, generator=g).to(torch.bfloat16)
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    cq = torch.tensor([0, 70, 71, 271], dtype=torch.int32)
+    qkv_d = qkv.to(DEV)
+    out, lse = sdpa_fwd_varlen(qkv_d[:, 0], qkv_d[:, 1], qkv_d[:, 2], cq.to(DEV), cq.to(DEV), 200,
+                               is_causal=True)
+    torch.cuda.synchronize()
+    check_varlen(q, k, v, cq, cq, out, lse, 1, torch.bfloat16, "packed qkv")
+
+
+def test_varlen_documents_workload_sampled():
+    """Packed documents, 32768 tokens, H=32, D=128, causal: sampled rows of every document."""
+    wl = W.config_varlen()
+    cq = wl.extra["cu_seqlens_q"]
+    out, lse = sdpa_fwd_varlen(to_dev(wl.q), to_dev(wl.k), to_dev(wl.v), to_dev(cq), to_dev(cq),
+                               max(wl.extra["lengths"]), is_causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows, H = {}, wl.q.shape[1]
+    for s, L in enumerate(wl.extra["lengths"]):
+        pick = {0, L - 1, H * L - 1} | set(rng.integers(0, H * L, size=24).tolist())
+        rows[s] = np.array(sorted(pick), dtype=np.int64)
+    check_varlen(wl.q, wl.k, wl.v, cq, cq, out, lse, 1, torch.bfloat16, wl.name, rows=rows)

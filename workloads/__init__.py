@@ -144,6 +144,42 @@ def config5(device="cpu"):
                     extra={"empty_rows": torch.stack(empty)})
 
 
+def doc_lengths(seed, total, lo=128, hi=8192):
+    """Document lengths for a packed batch: log-uniform integers in [lo, hi] drawn from a
+    generator seeded with `seed` until they sum to `total` (the last one cut to fit)."""
+    g = torch.Generator().manual_seed(seed)
+    lengths, left = [], total
+    while left > 0:
+        u = torch.rand((), generator=g).item()
+        n = int(round(math.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))))
+        n = min(max(n, 1), left)
+        lengths.append(n)
+        left -= n
+    return lengths
+
+
+def packed(seed, q_lengths, k_lengths, H, D, dtype=torch.bfloat16, device="cpu", mult=1.0):
+    """Packed variable-length inputs: q [sum q_lengths, H, D], k and v [sum k_lengths, H, D]
+    i.i.d. N(0, mult^2) drawn in the order q, k, v, and the int32 offsets cu_seqlens_q,
+    cu_seqlens_k (nseq + 1 entries each)."""
+    g = torch.Generator().manual_seed(seed)
+    tq, tk = sum(q_lengths), sum(k_lengths)
+    q, k, v = draw_qkv(g, (tq, H, D), (tk, H, D), dtype=dtype, mult=mult)
+    cq = torch.tensor([0] + list(q_lengths), dtype=torch.int64).cumsum(0).to(torch.int32)
+    ck = torch.tensor([0] + list(k_lengths), dtype=torch.int64).cumsum(0).to(torch.int32)
+    return q.to(device), k.to(device), v.to(device), cq.to(device), ck.to(device)
+
+
+def config_varlen(device="cpu"):
+    """Packed documents, bf16, causal: H=32, D=128, 32768 tokens split into documents of
+    log-uniform lengths in [128, 8192] (seed 6), queries and keys of the same documents."""
+    lengths = doc_lengths(6, 32768)
+    q, k, v, cq, ck = packed(6, lengths, lengths, 32, 128, device=device)
+    return Workload("varlen_bf16_causal_h32_d128_t32768", q, k, v, None, True,
+                    1 / math.sqrt(128), "packed documents, 32768 tokens, H=32, D=128, causal",
+                    extra={"lengths": lengths, "cu_seqlens_q": cq, "cu_seqlens_k": ck})
+
+
 CONFIGS = {
     "c1": config1,
     "c2": config2,
