@@ -14,6 +14,10 @@ credited.  The roofline peak is MI355X's dense bf16 matrix-core rate,
 Prints one JSON line.  `--report PATH` also writes per-workload timings (all five
 configurations, rank-3 vs rank-4) to PATH.
 
+`--pass varlen` measures sdpa_fwd_varlen on packed documents: 32768 tokens in documents of
+log-uniform lengths in [128, 8192] (seeded), H=32, D=128, bf16, causal per document; work
+is 4*D per visible pair summed over the documents.
+
 `--pass bwd` measures the gradients instead: one step = one sdpa_bwd call (its dq and dk/dv
 kernels) on the same workload, with the forward's out and lse and an upstream gradient
 (N(0,1), same [B,L,H,D] layout) resident before the timed region, gradients written in the
@@ -38,6 +42,8 @@ PEAK_F32_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
 BWD_METRIC = "causal SDPA bwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
+VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), "
+                 "32768 tokens H=32 D=128")
 # HBM bytes per launch of the fused kernel on the default workload: FETCH_SIZE and
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
@@ -235,6 +241,80 @@ def bench_bwd(wl, steps, warmup):
             "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12}
 
 
+def cpu_baseline_varlen(wl, target_s=12.0, seed=0):
+    """The fp64 oracle on a bounded sample of query rows of every document, on the host
+    cores; flops of the sampled rows / time, in TFLOP/s."""
+    import numpy as np
+    import oracle
+    H, D = wl.q.shape[1], wl.q.shape[2]
+    cq = wl.extra["cu_seqlens_q"].tolist()
+    rng = np.random.default_rng(seed)
+
+    def run(per_doc):
+        fl, t0 = 0, time.perf_counter()
+        for s, L in enumerate(wl.extra["lengths"]):
+            view = lambda t: t[cq[s]:cq[s + 1]].transpose(0, 1).unsqueeze(0)
+            rows = np.sort(rng.choice(H * L, size=min(per_doc, H * L), replace=False))
+            oracle.sdpa_oracle(view(wl.q), view(wl.k), view(wl.v), is_causal=True,
+                               scale=wl.scale, rows=rows)
+            fl += int(4 * D * ((rows % L) + 1).sum())
+        return time.perf_counter() - t0, fl
+
+    n = 16
+    dt, fl = run(n)
+    n = int(max(16, n * target_s / max(dt, 1e-3)))
+    dt, fl = run(n)
+    threads = oracle.default_threads()
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows drawn uniformly from each of the "
+                      f"{len(wl.extra['lengths'])} documents (all heads), fp64 oracle, "
+                      f"{dt:.2f} s for {fl / 1e9:.2f} GFLOP of visible pairs, {threads} OpenMP "
+                      f"threads, host cpu: {cpu_model()}"}
+
+
+def main_varlen(args, props):
+    import torch
+    import workloads as W
+    from scaled_dot_product_11_amd import sdpa_fwd_varlen
+    wl = W.config_varlen()
+    q, k, v = (t.to("cuda") for t in (wl.q, wl.k, wl.v))
+    cq = wl.extra["cu_seqlens_q"].to("cuda")
+    lengths = wl.extra["lengths"]
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+
+    def fn():
+        sdpa_fwd_varlen(q, k, v, cq, cq, max(lengths), out, lse, is_causal=True, scale=wl.scale)
+    wall, per = time_kernel(fn, args.steps, args.warmup)
+    H, D = q.shape[1], q.shape[2]
+    flops = 4 * D * H * sum(visible_pairs(L, L, True) for L in lengths)
+    ms_per_step = wall / args.steps * 1e3
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    mean = statistics.fmean(per)
+    achieved = flops / (mean * 1e-3) / 1e12
+    line = {
+        "metric": VARLEN_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "pass": "varlen", "tokens": int(q.shape[0]), "heads": H,
+                   "head_dim": D, "documents": len(lengths), "max_len": max(lengths),
+                   "is_causal": True, "scale": wl.scale, "flops_per_step": flops,
+                   "flop_convention": "4*D per visible (i,j) pair within each document",
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "device": props.name, "cus": props.multi_processor_count},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_ms_mean": round(mean, 4),
+                     "kernel_ms_median": round(statistics.median(per), 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_varlen(wl)
+    print(json.dumps(line), flush=True)
+
+
 def main_bwd(args, props):
     import workloads as W
     wl = W.config4()
@@ -285,8 +365,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="fwd (default): the fused forward; bwd: its gradients")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "varlen"), default="fwd",
+                    help="fwd (default): the fused forward; bwd: its gradients; varlen: the "
+                         "forward over packed documents")
     ap.add_argument("--report", default=None, help="write per-workload timings here")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one elementwise kernel reading and writing this many MiB "
@@ -303,6 +384,9 @@ def main():
     props = torch.cuda.get_device_properties(0)
     if args.which == "bwd":
         main_bwd(args, props)
+        return
+    if args.which == "varlen":
+        main_varlen(args, props)
         return
 
     wl = W.config4()
