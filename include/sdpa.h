@@ -57,7 +57,8 @@ enum sdpa_status {
   SDPA_ERR_ALIGN = 7,    /* q/k/v/out base or row stride not 16-byte aligned, lse not 4  */
   SDPA_ERR_SCALE = 8,    /* scale is NaN or infinite                                     */
   SDPA_ERR_DEVICE = 9,   /* the stream's device is not gfx950, or the launch failed      */
-  SDPA_ERR_CAUSAL = 10   /* causal mode not an sdpa_causal value                         */
+  SDPA_ERR_CAUSAL = 10,  /* causal mode not an sdpa_causal value                         */
+  SDPA_ERR_WORKSPACE = 11 /* workspace smaller than sdpa_fwd_splitkv_workspace() bytes   */
 };
 
 /* Causal modes (the is_causal / causal arguments). */
@@ -122,6 +123,49 @@ int sdpa_check(const void* q, const void* k, const void* v, const void* out, con
 
 /* sdpa_strerror -- a static, human-readable message for a status code. */
 const char* sdpa_strerror(int status);
+
+/*
+ * sdpa_fwd_splitkv -- sdpa_fwd (no mask) with the keys of every head split into chunks
+ * that separate workgroups process in parallel, for problems with few query rows per head
+ * and many keys (decoding: one or a few new queries against a long key sequence), where
+ * one workgroup per (head, query tile) would leave most of the chip idle.  Each chunk's
+ * workgroup writes its rows' softmax-normalised partial output and partial lse to
+ * `workspace`; a second kernel merges them exactly through the lse (the same merge that
+ * combines attention over disjoint key sets, which the exported lse of the pages' fused
+ * forward exists for):  lse = log sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) out_s.
+ * The result equals sdpa_fwd's up to the order of the floating-point sums.
+ *
+ *   q, k, v, out, lse, rank, B..D, scale, is_causal, dtype, stream
+ *                 as in sdpa_fwd (all three causal modes); there is no mask.
+ *   strides       4*rank element strides: q, k, v, out.
+ *   num_splits    requested number of key chunks, 1..1024, or 0 for the library's choice
+ *                 (enough workgroups to fill the chip, at least 512 keys per chunk, at most
+ *                 64 chunks).  Chunks hold a multiple of 64 keys, so fewer may be used.
+ *   workspace     device memory of at least sdpa_fwd_splitkv_workspace(...) bytes,
+ *                 16-byte aligned, owned by the caller; its contents on entry do not
+ *                 matter and on return are scratch.  Calls that share a workspace must not
+ *                 overlap in time.
+ *   workspace_bytes  its size (SDPA_ERR_WORKSPACE if smaller than needed).
+ *
+ * Two launches on `stream` (chunks, then the merge); nothing allocated or synchronised.
+ */
+int sdpa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                     const int64_t* strides, float scale, int is_causal, int64_t num_splits,
+                     void* workspace, int64_t workspace_bytes, int dtype, void* stream);
+
+/* sdpa_fwd_splitkv_check -- the host-side validation of sdpa_fwd_splitkv alone. */
+int sdpa_fwd_splitkv_check(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, int rank, int64_t B, int64_t H, int64_t Lq,
+                           int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                           int is_causal, int64_t num_splits, const void* workspace,
+                           int64_t workspace_bytes, int dtype);
+
+/* sdpa_fwd_splitkv_workspace -- workspace bytes sdpa_fwd_splitkv needs for these sizes and
+ * requested num_splits (0 = the library's choice): nsplit * B*H * Lq * (D + 1) * 4.
+ * Returns minus an sdpa_status for invalid sizes. */
+int64_t sdpa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                   int64_t num_splits, int dtype);
 
 /*
  * sdpa_fwd_varlen -- the fused forward over a batch of sequences of different lengths

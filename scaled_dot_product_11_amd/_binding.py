@@ -20,10 +20,11 @@ _DTYPES = {torch.float32: SDPA_F32, torch.bfloat16: SDPA_BF16}
 STATUS_NAMES = {
     0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_RANK", 3: "SDPA_ERR_SHAPE",
     4: "SDPA_ERR_HEAD_DIM", 5: "SDPA_ERR_DTYPE", 6: "SDPA_ERR_STRIDE", 7: "SDPA_ERR_ALIGN",
-    8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE", 10: "SDPA_ERR_CAUSAL",
+    8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE", 10: "SDPA_ERR_CAUSAL", 11: "SDPA_ERR_WORKSPACE",
 }
 
-EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
+EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_fwd_splitkv", "sdpa_fwd_splitkv_check",
+           "sdpa_fwd_splitkv_workspace", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
            "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
 
 
@@ -72,6 +73,14 @@ def load_library():
     lib.sdpa_fwd_varlen.restype = ctypes.c_int
     lib.sdpa_fwd_varlen_check.argtypes = varlen_common
     lib.sdpa_fwd_varlen_check.restype = ctypes.c_int
+    split_common = [vp] * 5 + [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.POINTER(i64),
+                               ctypes.c_float, ctypes.c_int, i64, vp, i64, ctypes.c_int]
+    lib.sdpa_fwd_splitkv.argtypes = split_common + [vp]
+    lib.sdpa_fwd_splitkv.restype = ctypes.c_int
+    lib.sdpa_fwd_splitkv_check.argtypes = split_common
+    lib.sdpa_fwd_splitkv_check.restype = ctypes.c_int
+    lib.sdpa_fwd_splitkv_workspace.argtypes = [i64] * 6 + [ctypes.c_int]
+    lib.sdpa_fwd_splitkv_workspace.restype = i64
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
     lib.sdpa_strerror.restype = ctypes.c_char_p
     lib.sdpa_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -241,6 +250,58 @@ def sdpa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, delta=None, *, 
             _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return dq, dk, dv
+
+
+def sdpa_fwd_splitkv_workspace(B, H, Lq, Lk, D, num_splits=0, dtype=SDPA_BF16) -> int:
+    """The C ABI `sdpa_fwd_splitkv_workspace`: workspace bytes (host-only)."""
+    n = load_library().sdpa_fwd_splitkv_workspace(B, H, Lq, Lk, D, int(num_splits), int(dtype))
+    if n < 0:
+        _raise_on(-n)
+    return n
+
+
+def sdpa_fwd_splitkv(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, num_splits=0,
+                     workspace=None, stream=None, return_lse=True):
+    """sdpa_fwd with the keys split across workgroups (C ABI `sdpa_fwd_splitkv`), for few
+    query rows against many keys.  Same tensors as sdpa_fwd, no mask.  num_splits: 0 lets
+    the library choose.  workspace: a cuda tensor of at least sdpa_fwd_splitkv_workspace()
+    bytes (allocated with torch when not given).  Returns (out, lse)."""
+    _check_shapes(q, k, v, out, lse, None)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    rank = q.dim()
+    B, H, Lq, Lk, D = _sizes(q, k)
+    dtype = _DTYPES.get(q.dtype, -1)
+    need = sdpa_fwd_splitkv_workspace(B, H, Lq, Lk, D, num_splits, dtype) if dtype >= 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride()]
+    arr = (ctypes.c_int64 * len(strides))(*strides)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        status = load_library().sdpa_fwd_splitkv(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr, float(scale),
+            causal_mode(is_causal), int(num_splits), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), dtype, handle)
+    _raise_on(status)
+    return out, lse
+
+
+def sdpa_fwd_splitkv_check(ptrs, rank, B, H, Lq, Lk, D, strides, scale, causal, num_splits,
+                           workspace_ptr, workspace_bytes, dtype) -> int:
+    """The C ABI `sdpa_fwd_splitkv_check` on raw integers: ptrs = (q, k, v, out, lse),
+    strides a list of 4*rank ints.  Host-only."""
+    arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
+    return load_library().sdpa_fwd_splitkv_check(*ptrs, rank, B, H, Lq, Lk, D, arr, float(scale),
+                                                 int(causal), int(num_splits), workspace_ptr,
+                                                 int(workspace_bytes), int(dtype))
 
 
 def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None, lse=None, *,

@@ -124,6 +124,8 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
     p->varlen = 0;
     p->cu_q = p->cu_k = nullptr;
     p->nseq = p->max_seqlen_q = 0;
+    p->nsplit = p->split_len = 0;
+    p->ws_o = p->ws_lse = nullptr;
     p->dtype = dtype;
   }
   return SDPA_OK;
@@ -290,7 +292,54 @@ int normalise_varlen(const void* q, const void* k, const void* v, const void* ou
     p->scale = scale;
     p->causal = causal;
     p->varlen = 1;
+    p->nsplit = p->split_len = 0;
+    p->ws_o = p->ws_lse = nullptr;
     p->dtype = dtype;
+  }
+  return SDPA_OK;
+}
+
+// Split keys: the dense forward's validation (4 tensors, no mask), then the split plan and
+// the workspace: [nsplit][B*H][Lq][D] partial outputs followed by [nsplit][B*H][Lq] lse,
+// fp32.  Returns the bytes needed through *need (also on SDPA_ERR_WORKSPACE).
+constexpr int64_t kMaxSplits = 1024;
+
+int splitkv_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, int64_t num_splits,
+                  int dtype, int64_t* nsplit, int64_t* split_len, int64_t* need) {
+  if (num_splits < 0 || num_splits > kMaxSplits) return SDPA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  const int64_t q_tiles = (Lq + sdpa::block_m(dtype) - 1) / sdpa::block_m(dtype);
+  sdpa::splitkv_plan(bh, q_tiles, Lk, num_splits, nsplit, split_len);
+  if (bh != 0 && q_tiles > kMaxDim / bh / *nsplit) return SDPA_ERR_SHAPE;  // grid size
+  *need = *nsplit * bh * Lq * (D + 1) * 4;
+  return SDPA_OK;
+}
+
+int normalise_splitkv(const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                      int64_t D, const int64_t* strides, float scale, int is_causal,
+                      int64_t num_splits, const void* workspace, int64_t workspace_bytes,
+                      int dtype, sdpa::Problem* p) {
+  if (!strides) return SDPA_ERR_NULL;
+  if (rank != 3 && rank != 4) return SDPA_ERR_RANK;
+  int64_t s5[20] = {0};
+  for (int i = 0; i < 4 * rank; ++i) s5[i] = strides[i];
+  int st = normalise(q, k, v, out, lse, rank, B, H, Lq, Lk, D, s5, scale, is_causal, nullptr,
+                     dtype, p);
+  if (st != SDPA_OK) return st;
+  int64_t nsplit, split_len, need;
+  st = splitkv_sizes(B, H, Lq, Lk, D, num_splits, dtype, &nsplit, &split_len, &need);
+  if (st != SDPA_OK) return st;
+  if (B * H * Lq != 0) {
+    if (!workspace) return SDPA_ERR_NULL;
+    if (!aligned(workspace, 16)) return SDPA_ERR_ALIGN;
+    if (workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+  }
+  if (p) {
+    p->nsplit = nsplit;
+    p->split_len = split_len;
+    p->ws_o = static_cast<float*>(const_cast<void*>(workspace));
+    p->ws_lse = p->ws_o ? p->ws_o + nsplit * B * H * Lq * D : nullptr;
   }
   return SDPA_OK;
 }
@@ -335,6 +384,41 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   sdpa::Problem p;
   const int st = normalise(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal,
                            mask, dtype, &p);
+  if (st != SDPA_OK) return st;
+  if (p.B * p.H * p.Lq == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
+int64_t sdpa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                   int64_t num_splits, int dtype) {
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || B > kMaxDim || H > kMaxDim || Lq > kMaxDim ||
+      Lk > kMaxDim || (B != 0 && H > kMaxDim / B))
+    return -SDPA_ERR_SHAPE;
+  if (D != 64 && D != 128) return -SDPA_ERR_HEAD_DIM;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16) return -SDPA_ERR_DTYPE;
+  int64_t nsplit, split_len, need;
+  const int st = splitkv_sizes(B, H, Lq, Lk, D, num_splits, dtype, &nsplit, &split_len, &need);
+  return st != SDPA_OK ? -st : need;
+}
+
+int sdpa_fwd_splitkv_check(const void* q, const void* k, const void* v, const void* out,
+                           const float* lse, int rank, int64_t B, int64_t H, int64_t Lq,
+                           int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                           int is_causal, int64_t num_splits, const void* workspace,
+                           int64_t workspace_bytes, int dtype) {
+  return normalise_splitkv(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal,
+                           num_splits, workspace, workspace_bytes, dtype, nullptr);
+}
+
+int sdpa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                     const int64_t* strides, float scale, int is_causal, int64_t num_splits,
+                     void* workspace, int64_t workspace_bytes, int dtype, void* stream) {
+  sdpa::Problem p;
+  const int st = normalise_splitkv(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale,
+                                   is_causal, num_splits, workspace, workspace_bytes, dtype, &p);
   if (st != SDPA_OK) return st;
   if (p.B * p.H * p.Lq == 0) return SDPA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -406,6 +490,8 @@ const char* sdpa_strerror(int status) {
     case SDPA_ERR_DEVICE: return "device is not gfx950 or the kernel launch failed";
     case SDPA_ERR_CAUSAL:
       return "causal mode must be 0 (none), 1 (top-left) or 2 (bottom-right)";
+    case SDPA_ERR_WORKSPACE:
+      return "workspace smaller than sdpa_fwd_splitkv_workspace() bytes";
     default: return "unknown sdpa status";
   }
 }

@@ -35,6 +35,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -56,7 +57,15 @@ struct Args {
   float scale_log2;  // scale * log2(e): scores are kept in base-2 units
   int32_t mask_vec8; // mask rows may be read 8 bytes at a time
   int32_t bottom_right;  // causal alignment: key j visible iff j <= i + (Lk - Lq)
+  float* ws_o;           // split keys only: normalised partial outputs [split][bh][Lq][D]
+  float* ws_lse;         // and their lse [split][bh][Lq] (fp32, natural log)
+  int32_t split_len;     // keys per split, a multiple of the key tile
 };
+
+// How a launch maps workgroups to rows: dense (b, h) heads, packed variable-length
+// sequences, or dense heads whose keys are split into chunks of split_len, one chunk per
+// workgroup, each writing a partial result that a second kernel merges.
+enum { kDense = 0, kVarlen = 1, kSplit = 2 };
 
 // The rows one work item serves: the element offsets of row 0 of its head in q, k, v, out
 // and the mask, the index of row 0's lse, its row counts, and the causal offset (key j is
@@ -70,10 +79,10 @@ struct Item {
   int Lq, Lk, coff;
 };
 
-template <bool VARLEN>
-__device__ inline Item item_of(const Args& a, int64_t bh) {
+template <int MODE>
+__device__ inline Item item_of(const Args& a, int64_t bh, int split) {
   Item it;
-  if (!VARLEN) {
+  if (MODE != kVarlen) {
     const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
     it.q = b * a.sq[0] + h * a.sq[1];
     it.k = b * a.sk[0] + h * a.sk[1];
@@ -97,7 +106,27 @@ __device__ inline Item item_of(const Args& a, int64_t bh) {
     it.Lk = k_hi - k_lo;
   }
   it.coff = a.bottom_right ? it.Lk - it.Lq : 0;
+  if (MODE == kSplit) {  // keys ks .. ks + split_len - 1, renumbered from 0
+    const int ks = split * a.split_len;
+    it.k += int64_t(ks) * a.sk[2];
+    it.v += int64_t(ks) * a.sv[2];
+    it.Lk = max(0, min(it.Lk - ks, a.split_len));
+    it.coff -= ks;
+  }
   return it;
+}
+
+// Work item (head, query tile) and key split of this workgroup.
+__device__ inline void decode_split(const Args& a, bool causal, int mode, int64_t* bh,
+                                    int64_t* qt, int* split) {
+  int64_t blk = blockIdx.x;
+  *split = 0;
+  if (mode == kSplit) {
+    const int64_t per = int64_t(a.bh_count) * a.q_tiles;
+    *split = int(blk / per);
+    blk -= int64_t(*split) * per;
+  }
+  decode_item(blk, a.bh_count, a.q_tiles, causal, bh, qt);
 }
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -180,7 +209,7 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-template <int D, bool CAUSAL, bool MASK, bool POS, bool VARLEN>
+template <int D, bool CAUSAL, bool MASK, bool POS, int MODE>
 __global__ __launch_bounds__(kThreadsBf16) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16(Args a) {
   constexpr int BN = kBlockNBf16;
@@ -206,11 +235,12 @@ void fwd_bf16(Args a) {
   const int hf = lane >> 5;
 
   int64_t bh, qt;
-  decode_item(blockIdx.x, a.bh_count, a.q_tiles, CAUSAL, &bh, &qt);
-  const Item it = item_of<VARLEN>(a, bh);
+  int split;
+  decode_split(a, CAUSAL, MODE, &bh, &qt, &split);
+  const Item it = item_of<MODE>(a, bh, split);
   const int Lq = it.Lq, Lk = it.Lk, coff = it.coff;
   const int q0 = int(qt) * kBlockMBf16;
-  if (VARLEN && q0 >= Lq) return;  // a tile past this sequence's rows (whole workgroup)
+  if (MODE == kVarlen && q0 >= Lq) return;  // a tile past this sequence's rows (whole workgroup)
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + it.q;
   const char* kb = static_cast<const char*>(a.k) + 2 * it.k;
   const char* vb = static_cast<const char*>(a.v) + 2 * it.v;
@@ -494,7 +524,22 @@ void fwd_bf16(Args a) {
   // ---- epilogue: normalise, safe-softmax zeros, store O and the LSE ----
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_ok) {
+  if (MODE == kSplit) {
+    if (q_ok) {
+      const int64_t prow = (int64_t(split) * a.bh_count + bh) * Lq + qi;
+      float* orow = a.ws_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 w = {o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
+                           o[dt][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * g + 4 * hf) = w;
+        }
+      if (hf == 0)
+        a.ws_lse[prow] = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+  } else if (q_ok) {
     uint16_t* orow = ob + int64_t(qi) * a.so[2];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -522,7 +567,7 @@ void fwd_bf16(Args a) {
 // fp32 kernel: fp32 MFMA 32x32x2 (true fp32 products, fp32 accumulation) for both
 // products; same decomposition as the bf16 kernel, probabilities stay fp32.
 // ---------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK, bool VARLEN>
+template <int D, bool CAUSAL, bool MASK, int MODE>
 __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   constexpr int DG = D / 4;                             // 16-byte groups per row
   constexpr int CH = kBlockNF32 * DG / kThreadsF32;           // chunks per thread per tile
@@ -540,11 +585,12 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   const int hf = lane >> 5;
 
   int64_t bh, qt;
-  decode_item(blockIdx.x, a.bh_count, a.q_tiles, CAUSAL, &bh, &qt);
-  const Item it = item_of<VARLEN>(a, bh);
+  int split;
+  decode_split(a, CAUSAL, MODE, &bh, &qt, &split);
+  const Item it = item_of<MODE>(a, bh, split);
   const int Lq = it.Lq, Lk = it.Lk, coff = it.coff;
   const int q0 = int(qt) * kBlockMF32;
-  if (VARLEN && q0 >= Lq) return;  // a tile past this sequence's rows (whole workgroup)
+  if (MODE == kVarlen && q0 >= Lq) return;  // a tile past this sequence's rows (whole workgroup)
   const float* qb = static_cast<const float*>(a.q) + it.q;
   const float* kb = static_cast<const float*>(a.k) + it.k;
   const float* vb = static_cast<const float*>(a.v) + it.v;
@@ -691,7 +737,23 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
 
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q_ok) {
+  if (MODE == kSplit) {
+    if (q_ok) {
+      const int64_t prow = (int64_t(split) * a.bh_count + bh) * Lq + qi;
+      float* orow = a.ws_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(o[dt][4 * g + e] * inv);
+          *reinterpret_cast<u32x4*>(orow + 32 * dt + 8 * g + 4 * hf) = w;
+        }
+      if (hf == 0)
+        a.ws_lse[prow] = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+  } else if (q_ok) {
     float* orow = ob + int64_t(qi) * a.so[2];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -708,27 +770,88 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   }
 }
 
-template <int D, bool CAUSAL, bool MASK, bool VARLEN>
+// ---------------------------------------------------------------------------------------
+// Merge of split-key partial results.  Split s of a row holds o_s = its softmax-weighted
+// sum of values over its keys, normalised by its own sum, and lse_s = log of that sum;
+// the row's result is the same quantity over all keys:
+//   lse = log sum_s exp(lse_s),   out = sum_s exp(lse_s - lse) o_s,
+// computed around m = max_s lse_s (splits with no visible key have lse_s = -inf and
+// weight 0; a row with none at all gets out = 0, lse = -inf).  One wave per row, lane l
+// holding head dims l, l + 64, ...
+// ---------------------------------------------------------------------------------------
+constexpr int kCombineRows = 4;  // rows (waves) per workgroup
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int nsplit) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = int64_t(a.bh_count) * a.Lq;
+  const int64_t row = int64_t(blockIdx.x) * kCombineRows + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t bh = row / a.Lq, i = row - bh * a.Lq;
+  float m = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, a.ws_lse[sp * rows + row]);
+  float acc[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float w = exp2_fast((a.ws_lse[sp * rows + row] - m) * kLog2e);
+      wsum += w;
+      const float* o = a.ws_o + (sp * rows + row) * D;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) acc[e] = __builtin_fmaf(w, o[lane + 64 * e], acc[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t b = bh / a.H, h = bh - b * a.H;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) {
+    const int64_t off = b * a.so[0] + h * a.so[1] + i * a.so[2] + lane + 64 * e;
+    if (BF16)
+      static_cast<__bf16*>(a.out)[off] = static_cast<__bf16>(acc[e] * inv);
+    else
+      static_cast<float*>(a.out)[off] = acc[e] * inv;
+  }
+  if (a.lse && lane == 0)
+    a.lse[row] = wsum > 0.f ? m + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
+}
+
+template <int D, bool CAUSAL, bool MASK, int MODE>
 hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Args*>(&a)};
   const void* fn;
   if (dtype == 1)
-    fn = a.scale_log2 > 0.f ? reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, true, VARLEN>)
-                            : reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, false, VARLEN>);
+    fn = a.scale_log2 > 0.f ? reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, true, MODE>)
+                            : reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, false, MODE>);
   else
-    fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK, VARLEN>);
+    fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK, MODE>);
   return hipLaunchKernel(fn, dim3(grid), dim3(block_threads(dtype)), args, 0, stream);
 }
 
 template <int D>
-hipError_t launch_d(const Args& a, int dtype, bool causal, bool varlen, unsigned grid,
+hipError_t launch_d(const Args& a, int dtype, bool causal, int mode, unsigned grid,
                     hipStream_t s) {
-  if (varlen)  // packed sequences take no mask
-    return causal ? launch<D, true, false, true>(a, dtype, grid, s)
-                  : launch<D, false, false, true>(a, dtype, grid, s);
+  if (mode == kVarlen)  // packed sequences take no mask
+    return causal ? launch<D, true, false, kVarlen>(a, dtype, grid, s)
+                  : launch<D, false, false, kVarlen>(a, dtype, grid, s);
+  if (mode == kSplit)  // neither do split keys
+    return causal ? launch<D, true, false, kSplit>(a, dtype, grid, s)
+                  : launch<D, false, false, kSplit>(a, dtype, grid, s);
   const bool m = a.mask != nullptr;
-  if (causal) return m ? launch<D, true, true, false>(a, dtype, grid, s) : launch<D, true, false, false>(a, dtype, grid, s);
-  return m ? launch<D, false, true, false>(a, dtype, grid, s) : launch<D, false, false, false>(a, dtype, grid, s);
+  if (causal) return m ? launch<D, true, true, kDense>(a, dtype, grid, s) : launch<D, true, false, kDense>(a, dtype, grid, s);
+  return m ? launch<D, false, true, kDense>(a, dtype, grid, s) : launch<D, false, false, kDense>(a, dtype, grid, s);
+}
+
+template <int D>
+hipError_t launch_combine(const Args& a, int dtype, int nsplit, hipStream_t s) {
+  const int64_t rows = int64_t(a.bh_count) * a.Lq;
+  const unsigned grid = unsigned((rows + kCombineRows - 1) / kCombineRows);
+  int ns = nsplit;
+  void* args[] = {const_cast<Args*>(&a), &ns};
+  const void* fn = dtype == 1 ? reinterpret_cast<const void*>(&splitkv_combine<D, true>)
+                              : reinterpret_cast<const void*>(&splitkv_combine<D, false>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(64 * kCombineRows), args, 0, s);
 }
 
 }  // namespace
@@ -761,9 +884,18 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
                 p.sm[1] % 8 == 0 && p.sm[2] % 8 == 0;
   a.bottom_right = p.causal == 2;
-  const unsigned grid = unsigned(int64_t(a.q_tiles) * a.bh_count);
-  if (p.D == 64) return launch_d<64>(a, p.dtype, p.causal != 0, p.varlen != 0, grid, stream);
-  return launch_d<128>(a, p.dtype, p.causal != 0, p.varlen != 0, grid, stream);
+  a.ws_o = p.ws_o;
+  a.ws_lse = p.ws_lse;
+  a.split_len = int32_t(p.split_len);
+  const int mode = p.varlen ? kVarlen : p.nsplit > 0 ? kSplit : kDense;
+  const unsigned grid =
+      unsigned(int64_t(a.q_tiles) * a.bh_count * (mode == kSplit ? p.nsplit : 1));
+  const bool causal = p.causal != 0;
+  hipError_t e = p.D == 64 ? launch_d<64>(a, p.dtype, causal, mode, grid, stream)
+                           : launch_d<128>(a, p.dtype, causal, mode, grid, stream);
+  if (e != hipSuccess || mode != kSplit) return e;
+  return p.D == 64 ? launch_combine<64>(a, p.dtype, int(p.nsplit), stream)
+                   : launch_combine<128>(a, p.dtype, int(p.nsplit), stream);
 }
 
 }  // namespace sdpa

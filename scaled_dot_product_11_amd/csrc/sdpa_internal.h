@@ -37,6 +37,11 @@ struct Problem {
   const int32_t* cu_k;
   int64_t B, H, Lq, Lk, D;
   int64_t nseq, max_seqlen_q;  // packed only
+  // split keys (dense, no mask): nsplit > 0 chunks of split_len keys, partial results in
+  // ws_o [nsplit][B*H][Lq][D] and ws_lse [nsplit][B*H][Lq] (fp32), merged by a second kernel
+  int64_t nsplit, split_len;
+  float* ws_o;
+  float* ws_lse;
   int64_t sq[4], sk[4], sv[4], so[4], sm[4];
   float scale;
   int causal;  // 0 none, 1 top-left (j <= i), 2 bottom-right (j <= i + Lk - Lq)
@@ -67,9 +72,30 @@ constexpr int64_t lds_bytes_f32(int D) {
   return 2 * (int64_t(kBlockNF32) * (D + 1) * 4 + int64_t(kBlockNF32) * D * 4);
 }
 
-// Launches the kernel matching p.dtype / p.D / p.causal / mask on `stream`.
-// p must already be validated.  Returns a hipError_t.
+// Launches the kernel matching p.dtype / p.D / p.causal / mask on `stream` (and, with
+// split keys, the merge kernel after it).  p must already be validated.  Returns a
+// hipError_t.
 hipError_t launch_fwd(const Problem& p, hipStream_t stream);
+
+// Split keys: the number of splits used for a requested count (0 = automatic: enough
+// workgroups to fill the chip, at least 512 keys per split, at most 64 splits) and the
+// keys per split (a multiple of the 64-key tile).
+inline void splitkv_plan(int64_t bh, int64_t q_tiles, int64_t Lk, int64_t requested,
+                         int64_t* nsplit, int64_t* split_len) {
+  int64_t want = requested;
+  if (want <= 0) {
+    const int64_t items = bh * q_tiles > 0 ? bh * q_tiles : 1;
+    want = (512 + items - 1) / items;
+    const int64_t by_keys = (Lk + 511) / 512;
+    if (want > by_keys) want = by_keys;
+    if (want > 64) want = 64;
+    if (want < 1) want = 1;
+  }
+  int64_t len = (Lk + want - 1) / want;
+  len = len < 64 ? 64 : (len + 63) / 64 * 64;
+  *split_len = len;
+  *nsplit = Lk > 0 ? (Lk + len - 1) / len : 1;
+}
 
 // ---- backward (bf16) ----
 // Two kernels of 8 waves (two per SIMD): the dQ kernel owns 256 query rows of one (b, h)

@@ -377,3 +377,54 @@ def test_varlen_check():
     big["strides"] = list(big["strides"])
     big["strides"][3] = 1024
     assert vcheck(**big) == SHAPE
+
+
+# ---- sdpa_fwd_splitkv_check / sdpa_fwd_splitkv_workspace ----------------------------------
+
+WORKSPACE_ERR = 11
+
+
+def sargs(B=2, H=3, Lq=4, Lk=5000, D=128, dtype=sd.SDPA_BF16, **over):
+    q = [H * Lq * D, Lq * D, D, 1]
+    k = [H * Lk * D, Lk * D, D, 1]
+    a = dict(ptrs=[A + i * 0x10000 for i in range(5)], rank=4, B=B, H=H, Lq=Lq, Lk=Lk, D=D,
+             strides=q + k + k + q, scale=0.1, causal=2, num_splits=0, workspace_ptr=A + 0x60000,
+             workspace_bytes=1 << 30, dtype=dtype)
+    a.update(over)
+    return a
+
+
+def test_splitkv_workspace_sizes():
+    ws = sd.sdpa_fwd_splitkv_workspace
+    # explicit splits: chunks are multiples of 64 keys, so 3 splits of 5000 keys -> 3 chunks
+    assert ws(2, 3, 4, 5000, 128, 3) == 3 * 6 * 4 * 129 * 4
+    # 100 splits of 5000 keys -> chunks of 64 keys -> 79 chunks
+    assert ws(2, 3, 4, 5000, 128, 100) == 79 * 6 * 4 * 129 * 4
+    # automatic: 6 work items -> ceil(512 / 6) = 86 wanted, capped by 512 keys a split (10)
+    assert ws(2, 3, 4, 5000, 64, 0) == 10 * 6 * 4 * 65 * 4
+    assert ws(1, 1, 1, 0, 64, 0) == 1 * 1 * 1 * 65 * 4
+    with pytest.raises(sd.SdpaError):
+        ws(1, 1, 1, 10, 96, 0)
+    with pytest.raises(sd.SdpaError):
+        ws(1, 1, 1, 10, 64, 5000)  # more than 1024 splits
+
+
+def test_splitkv_check():
+    c = sd.sdpa_fwd_splitkv_check
+    assert c(**sargs()) == OK
+    assert c(**sargs(dtype=sd.SDPA_F32, D=64, causal=0, num_splits=7)) == OK
+    assert c(**sargs(num_splits=-1)) == SHAPE
+    assert c(**sargs(causal=5)) == CAUSAL_ERR
+    assert c(**sargs(D=32)) == HEAD
+    need = sd.sdpa_fwd_splitkv_workspace(2, 3, 4, 5000, 128, 0)
+    assert c(**sargs(workspace_bytes=need)) == OK
+    assert c(**sargs(workspace_bytes=need - 1)) == WORKSPACE_ERR
+    assert c(**sargs(workspace_ptr=None)) == NULL
+    assert c(**sargs(workspace_ptr=A + 8)) == ALIGN
+    # empty problem: no workspace needed
+    assert c(**sargs(Lq=0, workspace_ptr=None, workspace_bytes=0)) == OK
+    a = sargs()
+    a["strides"] = list(a["strides"])
+    a["strides"][7] = 2  # k innermost stride
+    assert c(**a) == STRIDE
+    assert "workspace" in sd.sdpa_strerror(WORKSPACE_ERR)
