@@ -18,6 +18,11 @@ configurations, rank-3 vs rank-4) to PATH.
 log-uniform lengths in [128, 8192] (seeded), H=32, D=128, bf16, causal per document; work
 is 4*D per visible pair summed over the documents.
 
+`--pass decode` measures sdpa_fwd_splitkv on a decode step: B=8 x H=32 heads, one query
+each, against a 32768-key cache laid out [B,L,H,D], D=128, bf16, bottom-right causal (the
+query sees every key).  It is bound by HBM: `value` is algorithmic bytes (q, k, v, out,
+lse, each once) per second, against 8000 GB/s.
+
 `--pass bwd` measures the gradients instead: one step = one sdpa_bwd call (its dq and dk/dv
 kernels) on the same workload, with the forward's out and lse and an upstream gradient
 (N(0,1), same [B,L,H,D] layout) resident before the timed region, gradients written in the
@@ -42,6 +47,8 @@ PEAK_F32_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
 BWD_METRIC = "causal SDPA bwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
+DECODE_METRIC = ("decode SDPA (split keys) GB/s on 1 MI355X (% of HBM peak), B=8 H=32 Lq=1 "
+                 "Lk=32768 D=128")
 VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), "
                  "32768 tokens H=32 D=128")
 # HBM bytes per launch of the fused kernel on the default workload: FETCH_SIZE and
@@ -315,6 +322,112 @@ def main_varlen(args, props):
     print(json.dumps(line), flush=True)
 
 
+def decode_workload(device, heads=None):
+    """The decode step's inputs, i.i.d. N(0,1) bf16 drawn on `device` from a generator
+    seeded with 9: q [8,32,1,128] and the [8,32768,32,128] k and v buffers viewed as
+    [B,H,L,D].  heads=n draws a smaller problem of the same distribution, [1,n,1,128]
+    queries against [1,n,32768,128] keys, for the CPU sample."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(9)
+    B, H, L, D = (8, 32, 32768, 128) if heads is None else (1, heads, 32768, 128)
+
+    def draw(shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    q = draw((B, 1, H, D)).transpose(1, 2)
+    k, v = (draw((B, L, H, D)).transpose(1, 2) for _ in range(2))
+    return q, k, v
+
+
+def cpu_baseline_decode():
+    """The fp64 oracle on a bounded sample of the decode step: heads of the same shape and
+    distribution (one query row each, all 32768 keys), on the host cores; algorithmic bytes
+    of those rows (their q, k, v, out, lse) / time, in GB/s."""
+    import oracle
+    import torch
+
+    def run(n):
+        q, k, v = decode_workload("cpu", heads=n)
+        Lq, Lk, D = q.shape[2], k.shape[2], q.shape[3]
+        mask = torch.ones(Lq, Lk, dtype=torch.bool).tril(Lk - Lq)
+        t0 = time.perf_counter()
+        oracle.sdpa_oracle(q, k, v, mask=mask)
+        return time.perf_counter() - t0, n * (2 * Lk * D * 2 + 2 * D * 2 + 4)
+
+    # drawing the sample costs more than evaluating it, so its size is fixed
+    n = 64
+    dt, nb = run(n)
+    threads = oracle.default_threads()
+    return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} heads of the decode step's shape (one query against 32768 keys "
+                      f"each), fp64 oracle, {dt:.2f} s, {threads} OpenMP threads, host cpu: "
+                      f"{cpu_model()}"}
+
+
+def main_decode(args, props):
+    import torch
+    from scaled_dot_product_11_amd import sdpa_fwd, sdpa_fwd_splitkv, sdpa_fwd_splitkv_workspace
+    q, k, v = decode_workload("cuda")
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    need = sdpa_fwd_splitkv_workspace(B, H, Lq, Lk, D, 0, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def fn():
+        sdpa_fwd_splitkv(q, k, v, out, lse, is_causal=2, workspace=ws)
+    wall, per = time_kernel(fn, args.steps, args.warmup)
+
+    def dense():
+        sdpa_fwd(q, k, v, out, lse, is_causal=2)
+    _, per_dense = time_kernel(dense, max(5, args.steps // 5), 2)
+    # a small batch (one sequence of 8 heads): too few heads to fill the chip without splits
+    qs, ks, vs = q[:1, :8], k[:1, :8], v[:1, :8]
+    outs, lses = out[:1, :8].clone(), lse[:1, :8].clone()
+    ws_s = torch.empty(sdpa_fwd_splitkv_workspace(1, 8, Lq, Lk, D, 0, 1), dtype=torch.uint8,
+                       device="cuda")
+    _, per_small = time_kernel(lambda: sdpa_fwd_splitkv(qs, ks, vs, outs, lses, is_causal=2,
+                                                        workspace=ws_s), 10, 3)
+    _, per_small_dense = time_kernel(lambda: sdpa_fwd(qs, ks, vs, outs, lses, is_causal=2), 5, 2)
+    small_bytes = 2 * 8 * Lk * D * 2 + 2 * 8 * Lq * D * 2 + 8 * Lq * 4
+    nbytes = 2 * B * H * Lk * D * 2 + 2 * B * H * Lq * D * 2 + B * H * Lq * 4
+    flops = 4 * D * B * H * visible_pairs(Lq, Lk, False)
+    ms_per_step = wall / args.steps * 1e3
+    mean = statistics.fmean(per)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (mean * 1e-3) / 1e9
+    line = {
+        "metric": DECODE_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_bf16_b8_h32_lq1_lk32768_d128_blhd", "pass": "decode",
+                   "shape_q": [B, H, Lq, D], "shape_kv": [B, H, Lk, D],
+                   "layout": "[B,L,H,D] buffers viewed as [B,H,L,D]", "is_causal": "bottom-right",
+                   "bytes_per_step": nbytes, "tflops": round(flops / (mean * 1e-3) / 1e12, 3),
+                   "splits": need // (B * H * Lq * (D + 1) * 4),
+                   "dense_single_split_ms_mean": round(statistics.fmean(per_dense), 4),
+                   "small_batch_b1_h8": {
+                       "splitkv_ms_mean": round(statistics.fmean(per_small), 4),
+                       "splitkv_gbs": round(small_bytes / statistics.fmean(per_small) / 1e6, 1),
+                       "dense_ms_mean": round(statistics.fmean(per_small_dense), 4),
+                       "dense_gbs": round(small_bytes / statistics.fmean(per_small_dense) / 1e6, 1)},
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "device": props.name, "cus": props.multi_processor_count},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernels": "fwd_bf16 (split keys) + splitkv_combine",
+                     "kernel_ms_mean": round(mean, 4),
+                     "kernel_ms_median": round(statistics.median(per), 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode()
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+    print(json.dumps(line), flush=True)
+
+
 def main_bwd(args, props):
     import workloads as W
     wl = W.config4()
@@ -365,9 +478,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "varlen"), default="fwd",
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "varlen", "decode"),
+                    default="fwd",
                     help="fwd (default): the fused forward; bwd: its gradients; varlen: the "
-                         "forward over packed documents")
+                         "forward over packed documents; decode: split keys, one query per head")
     ap.add_argument("--report", default=None, help="write per-workload timings here")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one elementwise kernel reading and writing this many MiB "
@@ -387,6 +501,9 @@ def main():
         return
     if args.which == "varlen":
         main_varlen(args, props)
+        return
+    if args.which == "decode":
+        main_decode(args, props)
         return
 
     wl = W.config4()
