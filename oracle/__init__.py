@@ -32,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-_DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float64: 2}
+_DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float64: 2, torch.float16: 3}
 
 
 def _load():
@@ -87,7 +87,7 @@ def _check_qkv(q, k, v):
     if not (q.dim() == k.dim() == v.dim() and q.dim() in (3, 4)):
         raise ValueError("q, k, v must all be rank 3 or all rank 4")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
-        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float64")
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float16, float64")
     if q.dim() == 3:
         B, H, Lq, D = 1, q.shape[0], q.shape[1], q.shape[2]
         Lk = k.shape[1]
@@ -146,7 +146,7 @@ def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, n
     """Evaluate the plain definition in fp64.
 
     q: [N,Lq,D] or [B,H,Lq,D]; k, v: same rank with Lk rows; CPU tensors (or numpy) of one
-    dtype among float32 / bfloat16 / float64, any strides.  mask: optional bool or uint8
+    dtype among float32 / bfloat16 / float16 / float64, any strides.  mask: optional bool or uint8
     tensor broadcastable to [B,H,Lq,Lk] (rank 4) or [N,Lq,Lk] (rank 3); nonzero = visible.
     rows: optional int64 flat row ids (b*H + h)*Lq + i.
 
@@ -160,7 +160,7 @@ def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, n
     if not (q.dim() == k.dim() == v.dim() and q.dim() in (3, 4)):
         raise ValueError("q, k, v must all be rank 3 or all rank 4")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
-        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float64")
+        raise ValueError("q, k, v must share one dtype among float32, bfloat16, float16, float64")
     rank = q.dim()
     if rank == 3:
         B, H, Lq, D = 1, q.shape[0], q.shape[1], q.shape[2]

@@ -46,12 +46,25 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2, ORACLE_F16 = 3 };
+
+/* IEEE-754 binary16 from its fields: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent 0 holds zero and the subnormals frac * 2^-24; exponent 31 holds the
+ * infinities (frac 0) and NaNs; otherwise the value is (1024 + frac) * 2^(exp - 25). */
+static double decode_f16(uint16_t h) {
+  const int sign = h >> 15, ex = (h >> 10) & 0x1f, frac = h & 0x3ff;
+  double mag;
+  if (ex == 0) mag = ldexp((double)frac, -24);
+  else if (ex == 31) mag = frac == 0 ? INFINITY : NAN;
+  else mag = ldexp((double)(1024 + frac), ex - 25);
+  return sign ? -mag : mag;
+}
 
 /* Exact decode of one element of a q/k/v tensor to double. */
 static double load_elem(const void* base, int dtype, int64_t off) {
   if (dtype == ORACLE_F64) return ((const double*)base)[off];
   if (dtype == ORACLE_F32) return (double)((const float*)base)[off];
+  if (dtype == ORACLE_F16) return decode_f16(((const uint16_t*)base)[off]);
   /* bf16: the 16 stored bits are the high half of an IEEE-754 binary32. */
   uint32_t bits = (uint32_t)((const uint16_t*)base)[off] << 16;
   float f;
@@ -118,7 +131,8 @@ static void one_row(int dtype, int64_t Lk, int64_t D, const void* q, const int64
 /*
  * oracle_sdpa_fwd -- the whole forward, or a chosen subset of its rows.
  *
- *   dtype        ORACLE_F32 / ORACLE_BF16 (raw 16-bit patterns) / ORACLE_F64, shared by q,k,v
+ *   dtype        ORACLE_F32 / ORACLE_BF16 or ORACLE_F16 (raw 16-bit patterns) / ORACLE_F64,
+ *                shared by q, k, v
  *   B,H,Lq,Lk,D  sizes; q is [B,H,Lq,D], k and v are [B,H,Lk,D] through the strides below
  *   qs,ks,vs     four element strides each, in (b, h, row, d) order; any value allowed
  *   mask, ms     optional byte mask addressed as mask[b*ms0 + h*ms1 + i*ms2 + j*ms3]
@@ -138,7 +152,7 @@ int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
                     const void* v, const int64_t* vs, const uint8_t* mask, const int64_t* ms,
                     int is_causal, double scale, const int64_t* rows, int64_t nrows,
                     double* out, double* lse, int nthreads) {
-  if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return 1;
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return 1;
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || D < 0) return 1;
   if (!out || !lse || !qs || !ks || !vs || (mask && !ms)) return 1;
   const int64_t n = rows ? nrows : B * H * Lq;
@@ -201,7 +215,7 @@ int oracle_sdpa_bwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
                     const void* v, const int64_t* vs, const void* dout, const int64_t* dos,
                     const uint8_t* mask, const int64_t* ms, int is_causal, double scale,
                     double* dq, double* dk, double* dv, int nthreads) {
-  if (dtype < ORACLE_F32 || dtype > ORACLE_F64) return 1;
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return 1;
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || D < 0) return 1;
   if (!dq || !dk || !dv || !qs || !ks || !vs || !dos || (mask && !ms)) return 1;
   int status = 0;

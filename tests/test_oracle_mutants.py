@@ -25,6 +25,9 @@ MUTANTS = {
     "softmax_not_normalised": ("for (int64_t j = 0; j < Lk; ++j) p[j] /= l;", ""),
     "max_not_subtracted_wrongly": ("exp(s[j] - m)", "exp(s[j] + m)"),
     "bf16_decode_shift": ("<< 16", "<< 15"),
+    "f16_exponent_bias": ("ldexp((double)(1024 + frac), ex - 25)", "ldexp((double)(1024 + frac), ex - 24)"),
+    "f16_subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "f16_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
 }
 
 # backward: (anchor, replacement) in oracle_sdpa_bwd

@@ -279,3 +279,28 @@ def test_empty_key_set_and_empty_queries():
     assert np.all(out == 0.0) and np.all(lse == -np.inf)
     out, lse = sdpa_oracle(np.zeros((1, 2, 0, 4)), np.ones((1, 2, 5, 4)), np.ones((1, 2, 5, 4)))
     assert out.shape == (1, 2, 0, 4) and lse.shape == (1, 2, 0)
+
+
+def test_fp16_decode_is_exact_for_every_bit_pattern():
+    """One key gives weight exactly 1, so out = v: every finite and infinite IEEE binary16
+    bit pattern in v must come back as numpy's own float16 -> float64 value."""
+    bits = np.arange(65536, dtype=np.uint16)
+    halves = bits.view(np.float16)
+    keep = ~np.isnan(halves)
+    v = torch.from_numpy(halves[keep].copy()).reshape(1, 1, 1, -1)
+    D = v.shape[-1]
+    q = torch.zeros(1, 1, 1, D, dtype=torch.float16)
+    k = torch.zeros(1, 1, 1, D, dtype=torch.float16)
+    out, lse = sdpa_oracle(q, k, v)
+    want = halves[keep].astype(np.float64)
+    assert np.array_equal(out.reshape(-1), want)
+    assert lse.reshape(-1)[0] == 0.0
+
+
+def test_fp16_inputs_match_their_fp64_values():
+    g = torch.Generator().manual_seed(77)
+    q, k, v = (torch.randn(2, 3, 9, 16, generator=g).to(torch.float16) for _ in range(3))
+    a = sdpa_oracle(q, k, v, is_causal=True)
+    b = sdpa_oracle(q.double(), k.double(), v.double(), is_causal=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
