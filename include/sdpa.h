@@ -40,9 +40,12 @@ extern "C" {
 /* Element types of q, k, v and out (all four share one). */
 enum sdpa_dtype {
   SDPA_F32 = 0,  /* IEEE binary32; products and sums in fp32 (matrix cores, fp32 MFMA)   */
-  SDPA_BF16 = 1  /* bfloat16; bf16 products on matrix cores with fp32 accumulation, the
+  SDPA_BF16 = 1, /* bfloat16; bf16 products on matrix cores with fp32 accumulation, the
                     softmax in fp32, probabilities rounded to bf16 (nearest-even) before
                     the product with V                                                    */
+  SDPA_F16 = 2   /* IEEE binary16; as SDPA_BF16 with fp16 products and probabilities
+                    rounded to fp16 (nearest-even); outputs are finite when |v| is, since
+                    every output is a convex combination of value rows                   */
 };
 
 /* Status codes.  On any nonzero status nothing was launched and nothing was written. */
@@ -214,7 +217,7 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
                           const int64_t* strides, float scale, int causal, int dtype);
 
 /*
- * sdpa_bwd -- gradients dq, dk, dv of sdpa_fwd for an upstream gradient dout, bf16 only.
+ * sdpa_bwd -- gradients dq, dk, dv of sdpa_fwd for an upstream gradient dout, bf16 or fp16.
  *
  * The derivative of the forward above by the chain rule through its steps.  The pages
  * define no backward; it reuses the forward's exported lse, as the fused forward of
@@ -228,14 +231,15 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
  *   dS[i,j] = P[i,j] (dP[i,j] - delta[i])
  *   dq[i,:] = scale * sum_j dS[i,j] k[j,:],   dk[j,:] = scale * sum_i dS[i,j] q[i,:]
  *
- * P and dS are rounded to bf16 (nearest-even) before their products; every product
- * accumulates in fp32, and dq, dk, dv are rounded to bf16 once at the end.  Deterministic:
+ * P and dS are rounded to the input type (nearest-even) before their products; every
+ * product accumulates in fp32, and dq, dk, dv are rounded to the input type once at the
+ * end.  Deterministic:
  * no atomics, every output element is written by exactly one lane.  A query row with no
  * visible key gets dq = 0 and contributes nothing to dk, dv; a key seen by no query gets
  * dk = dv = 0.
  *
  *   q, k, v, out, dout, dq, dk, dv
- *                 device pointers to bf16.  q, out, dout, dq are [B,H,Lq,D] / [N,Lq,D];
+ *                 device pointers to the 16-bit dtype.  q, out, dout, dq are [B,H,Lq,D] / [N,Lq,D];
  *                 k, v, dk, dv are [B,H,Lk,D] / [N,Lk,D]; any layout with unit innermost
  *                 stride.  Bases and non-innermost strides (in bytes) multiples of 16.
  *                 dq, dk, dv must not overlap each other or any input.  q/out/dout/dq
@@ -252,7 +256,7 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
  *                 mask, each in its own axis order as in sdpa_fwd.
  *   scale, is_causal, mask
  *                 exactly as passed to sdpa_fwd (all three causal modes).
- *   dtype         SDPA_BF16 (anything else: SDPA_ERR_DTYPE).
+ *   dtype         SDPA_BF16 or SDPA_F16 (anything else: SDPA_ERR_DTYPE).
  *   stream        a hipStream_t (NULL = the null stream of the current device).
  *
  * Launches two kernels on `stream` (dq and delta first, then dk and dv); allocates,

@@ -4,7 +4,7 @@ The computation runs in hand-written HIP kernels for gfx950 behind the C ABI dec
 include/sdpa.h; this package is its thin Python binding (names mirror the C entry points).
 """
 from ._binding import (EXPORTS, LIB_PATH, SDPA_BF16, SDPA_CAUSAL_BOTTOM_RIGHT, SDPA_CAUSAL_NONE,
-                       SDPA_CAUSAL_TOP_LEFT, SDPA_F32, STATUS_NAMES, SdpaError, SdpaPlan,
+                       SDPA_CAUSAL_TOP_LEFT, SDPA_F16, SDPA_F32, STATUS_NAMES, SdpaError, SdpaPlan,
                        load_library, sdpa_bwd, sdpa_bwd_check, sdpa_check, sdpa_fwd,
                        sdpa_fwd_splitkv, sdpa_fwd_splitkv_check, sdpa_fwd_splitkv_workspace,
                        sdpa_fwd_varlen, sdpa_fwd_varlen_check, sdpa_plan, sdpa_plan_item,
@@ -13,5 +13,5 @@ from ._binding import (EXPORTS, LIB_PATH, SDPA_BF16, SDPA_CAUSAL_BOTTOM_RIGHT, S
 __all__ = ["sdpa_fwd", "sdpa_check", "sdpa_fwd_splitkv", "sdpa_fwd_splitkv_check",
            "sdpa_fwd_splitkv_workspace", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
            "sdpa_bwd_check", "SDPA_CAUSAL_NONE", "SDPA_CAUSAL_TOP_LEFT", "SDPA_CAUSAL_BOTTOM_RIGHT", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item", "SdpaError",
-           "SdpaPlan", "SDPA_F32", "SDPA_BF16", "STATUS_NAMES", "LIB_PATH", "EXPORTS",
+           "SdpaPlan", "SDPA_F32", "SDPA_BF16", "SDPA_F16", "STATUS_NAMES", "LIB_PATH", "EXPORTS",
            "load_library"]

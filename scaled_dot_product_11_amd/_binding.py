@@ -13,9 +13,9 @@ import torch  # must precede loading the library: it binds to torch's HIP runtim
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdpa_gfx950.so")
 
-SDPA_F32, SDPA_BF16 = 0, 1
+SDPA_F32, SDPA_BF16, SDPA_F16 = 0, 1, 2
 SDPA_CAUSAL_NONE, SDPA_CAUSAL_TOP_LEFT, SDPA_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
-_DTYPES = {torch.float32: SDPA_F32, torch.bfloat16: SDPA_BF16}
+_DTYPES = {torch.float32: SDPA_F32, torch.bfloat16: SDPA_BF16, torch.float16: SDPA_F16}
 
 STATUS_NAMES = {
     0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_RANK", 3: "SDPA_ERR_SHAPE",
@@ -171,7 +171,7 @@ def sdpa_fwd(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, mask=N
              stream=None, return_lse=True):
     """Fused SDPA forward through the C ABI `sdpa_fwd`.
 
-    q: [N,Lq,D] or [B,H,Lq,D]; k, v: [N,Lk,D] or [B,H,Lk,D]; bf16 or fp32 cuda tensors with
+    q: [N,Lq,D] or [B,H,Lq,D]; k, v: [N,Lk,D] or [B,H,Lk,D]; bf16, fp16 or fp32 cuda tensors with
     unit innermost stride (any other strides).  mask: optional bool/uint8 tensor
     broadcastable to q.shape[:-1] + (Lk,), True/nonzero = visible.  is_causal: False/True
     (top-left) or a mode 0 / 1 / 2 (2 = bottom-right).  scale defaults to 1/sqrt(D).  out/lse are allocated when not given (out contiguous, lse float32
@@ -309,7 +309,7 @@ def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None,
     """Fused forward over packed variable-length sequences through the C ABI
     `sdpa_fwd_varlen`.
 
-    q: [total_q, H, D], k, v: [total_k, H, D] (bf16 or fp32 cuda tensors, unit dim stride);
+    q: [total_q, H, D], k, v: [total_k, H, D] (bf16, fp16 or fp32 cuda tensors, unit dim stride);
     cu_seqlens_q / cu_seqlens_k: int32 cuda tensors of nseq + 1 offsets; max_seqlen_q: an
     int bound of the query lengths (it sizes the launch).  is_causal: False/True (top-left)
     or a mode 0 / 1 / 2, applied per sequence.  out ([total_q, H, D]) and lse ([H, total_q]

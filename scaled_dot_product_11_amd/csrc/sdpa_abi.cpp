@@ -59,7 +59,7 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
   if (Lq > kMaxDim || Lk > kMaxDim || B > kMaxDim || H > kMaxDim) return SDPA_ERR_SHAPE;
   if (B != 0 && H > kMaxDim / B) return SDPA_ERR_SHAPE;
   if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
-  if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
   if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
@@ -86,7 +86,7 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
   if (any_rows && (!q || !out)) return SDPA_ERR_NULL;
   if (reads_kv && (!k || !v)) return SDPA_ERR_NULL;
 
-  const int64_t esize = dtype == SDPA_BF16 ? 2 : 4;
+  const int64_t esize = dtype == SDPA_F32 ? 4 : 2;
   const void* bases[4] = {q, k, v, out};
   for (int t = 0; t < 4; ++t) {
     const bool used = (t == 1 || t == 2) ? reads_kv : any_rows;
@@ -140,7 +140,7 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
                   int is_causal, const uint8_t* mask, int dtype, sdpa::BwdProblem* p) {
   int st = check_sizes(rank, B, H, Lq, Lk, D, scale);
   if (st != SDPA_OK) return st;
-  if (dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+  if (dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t bh = B * H;
@@ -215,6 +215,7 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
     memcpy(p->sm, s4[M], sizeof p->sm);
     p->scale = scale;
     p->causal = is_causal;
+    p->dtype = dtype;
   }
   return SDPA_OK;
 }
@@ -231,7 +232,7 @@ int normalise_varlen(const void* q, const void* k, const void* v, const void* ou
     return SDPA_ERR_SHAPE;
   if (max_seqlen_q > total_q) return SDPA_ERR_SHAPE;
   if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
-  if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_DTYPE;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
   if (causal < SDPA_CAUSAL_NONE || causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
@@ -253,7 +254,7 @@ int normalise_varlen(const void* q, const void* k, const void* v, const void* ou
   }
   if (any_rows && (!q || !out || !cu_q || !cu_k)) return SDPA_ERR_NULL;
   if (any_rows && total_k != 0 && (!k || !v)) return SDPA_ERR_NULL;
-  const int64_t esize = dtype == SDPA_BF16 ? 2 : 4;
+  const int64_t esize = dtype == SDPA_F32 ? 4 : 2;
   const void* bases[4] = {q, k, v, out};
   for (int t = 0; t < 4; ++t) {
     if (!any_rows || (!bases[t] && (t == 1 || t == 2) && total_k == 0)) continue;
@@ -397,7 +398,7 @@ int64_t sdpa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
       Lk > kMaxDim || (B != 0 && H > kMaxDim / B))
     return -SDPA_ERR_SHAPE;
   if (D != 64 && D != 128) return -SDPA_ERR_HEAD_DIM;
-  if (dtype != SDPA_F32 && dtype != SDPA_BF16) return -SDPA_ERR_DTYPE;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return -SDPA_ERR_DTYPE;
   int64_t nsplit, split_len, need;
   const int st = splitkv_sizes(B, H, Lq, Lk, D, num_splits, dtype, &nsplit, &split_len, &need);
   return st != SDPA_OK ? -st : need;
@@ -482,7 +483,8 @@ const char* sdpa_strerror(int status) {
       return "negative size, a size beyond the supported maximum, or one head's k/v rows "
              "spanning 2 GiB or more";
     case SDPA_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
-    case SDPA_ERR_DTYPE: return "dtype must be SDPA_F32 or SDPA_BF16";
+    case SDPA_ERR_DTYPE:
+      return "dtype must be SDPA_F32, SDPA_BF16 or SDPA_F16 (the backward: SDPA_BF16 or SDPA_F16)";
     case SDPA_ERR_STRIDE: return "innermost strides must be 1 and no stride may be negative";
     case SDPA_ERR_ALIGN:
       return "q/k/v/out base pointers and outer strides must be 16-byte aligned, lse 4-byte";
@@ -513,7 +515,7 @@ int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
   plan->q_tiles = (Lq + plan->block_m - 1) / plan->block_m;
   plan->bh = B * H;
   plan->items = plan->bh * plan->q_tiles;
-  plan->lds_bytes = dtype == SDPA_BF16 ? sdpa::lds_bytes_bf16(int(D)) : sdpa::lds_bytes_f32(int(D));
+  plan->lds_bytes = dtype == SDPA_F32 ? sdpa::lds_bytes_f32(int(D)) : sdpa::lds_bytes_bf16(int(D));
   plan->is_causal = is_causal ? 1 : 0;
   return SDPA_OK;
 }

@@ -1,5 +1,5 @@
 // sdpa_bwd_gfx950.hip -- gradients of the fused scaled-dot-product attention for MI355X
-// (gfx950), bf16 inputs and outputs.
+// (gfx950), bf16 or fp16 inputs and outputs.
 //
 // The forward is out = P v with P the row softmax of S = scale * q.k^T over the visible
 // keys ("Profiling in PyTorch (part 3): attention", naive causal attention, five steps).
@@ -40,6 +40,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -97,10 +99,23 @@ __device__ inline int perm5(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 
 // visible key (lse = -inf) get +inf so that every probability of the row is 2^-inf = 0.
 __device__ inline float lse_base2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
-// Two fp32 values rounded to bf16 (nearest-even) and packed low-first.
-__device__ inline uint32_t pack_bf16(float lo, float hi) {
+// The 16-bit input types (bf16 or fp16): operand vectors, the 32x32x16 product of that
+// type, and two fp32 values rounded to it (nearest-even) and packed low-first.
+template <typename E> struct Vec16;
+template <> struct Vec16<__bf16> { typedef bf16x8 v8; typedef bf16x2 v2; };
+template <> struct Vec16<_Float16> { typedef f16x8 v8; typedef f16x2 v2; };
+
+__device__ inline f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x16 mfma16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+template <typename E>
+__device__ inline uint32_t pack2(float lo, float hi) {
   const f32x2 p = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, typename Vec16<E>::v2));
 }
 
 // The transposed operand of a 32x32x16 product from a row-major tile in LDS: rows are
@@ -111,12 +126,12 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 // address for row0 = 8 * (lane / 32), col0 = 16 * ((lane / 16) % 2); the operand of
 // reduction chunk c (rows 16c + 8h + 0..7 in half h) and output block dt (columns
 // 32dt + lane % 32) is two such reads, 4 rows apart.
-template <int PITCH>
-__device__ inline bf16x8 tr_operand(const char* tfrag, int c, int dt) {
+template <typename V, int PITCH>
+__device__ inline V tr_operand(const char* tfrag, int c, int dt) {
   const s16x4 lo = ds_read_tr(tfrag + (16 * c) * PITCH + 64 * dt);
   const s16x4 hi = ds_read_tr(tfrag + (16 * c + 4) * PITCH + 64 * dt);
   const s16x4 both[2] = {lo, hi};
-  return __builtin_bit_cast(bf16x8, both);
+  return __builtin_bit_cast(V, both);
 }
 
 __device__ inline int tr_lane_offset(int lane, int pitch) {
@@ -125,16 +140,17 @@ __device__ inline int tr_lane_offset(int lane, int pitch) {
 }
 
 // Stores a 32 x D accumulator block set (registers 4g..4g+3 of block dt hold columns
-// 32dt + 8g + 4h + 0..3 of the lane's row) as one bf16 row, multiplied by `mul`.
-template <int D>
-__device__ inline void store_row_bf16(uint16_t* row, const f32x16 (&acc)[D / 32], float mul,
-                                      int hf) {
+// 32dt + 8g + 4h + 0..3 of the lane's row) as one row of the 16-bit type E, multiplied by
+// `mul`.
+template <typename E, int D>
+__device__ inline void store_row(uint16_t* row, const f32x16 (&acc)[D / 32], float mul,
+                                 int hf) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t w0 = pack_bf16(acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul);
-      const uint32_t w1 = pack_bf16(acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul);
+      const uint32_t w0 = pack2<E>(acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul);
+      const uint32_t w1 = pack2<E>(acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul);
       *reinterpret_cast<u32x2*>(row + 32 * dt + 8 * g + 4 * hf) = u32x2{w0, w1};
     }
 }
@@ -148,12 +164,13 @@ __device__ inline void store_row_bf16(uint16_t* row, const f32x16 (&acc)[D / 32]
 //   S^T[kt]  = K[kt] Q^T        (K rows read in perm5 order: register r of half hf is key
 //   dP^T[kt] = V[kt] dO^T        32kt + 16(r/8) + 8hf + r%8)
 //   dS^T     = P^T * (dP^T - delta),  P^T = 2^(S^T scale log2e - lse2), hidden -> 0
-//   dQ^T    += K^T dS^T          (K^T by transposed reads, dS^T rounded to bf16)
+//   dQ^T    += K^T dS^T          (K^T by transposed reads, dS^T rounded to the input type)
 // LDS stage: K row copy | K transposed-read copy | V row copy.
 // ---------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK>
+template <typename E, int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreadsBwdQ) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_bf16(BwdArgs a) {
+void bwd_dq(BwdArgs a) {
+  typedef typename Vec16<E>::v8 v8;
   constexpr int BN = kBwdStep;
   constexpr int NT = kThreadsBwdQ;
   constexpr int DG = D / 8;           // 16-byte chunks per row
@@ -193,7 +210,7 @@ void bwd_dq_bf16(BwdArgs a) {
 
   // Q^T and dO^T operands (chunk c = head dims 16c..16c+15, half hf supplies 8 of them),
   // and delta = dO . out of this row from the same halves of dO and out.
-  bf16x8 qf[D / 16], dof[D / 16];
+  v8 qf[D / 16], dof[D / 16];
   float dpart = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
@@ -203,9 +220,9 @@ void bwd_dq_bf16(BwdArgs a) {
       wd = ld16(dob + int64_t(qi) * a.sdo[2] + 16 * c + 8 * hf);
       wo = ld16(ob + int64_t(qi) * a.so[2] + 16 * c + 8 * hf);
     }
-    qf[c] = __builtin_bit_cast(bf16x8, wq);
-    dof[c] = __builtin_bit_cast(bf16x8, wd);
-    const bf16x8 of = __builtin_bit_cast(bf16x8, wo);
+    qf[c] = __builtin_bit_cast(v8, wq);
+    dof[c] = __builtin_bit_cast(v8, wd);
+    const v8 of = __builtin_bit_cast(v8, wo);
 #pragma unroll
     for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf(float(dof[c][e]), float(of[e]), dpart);
   }
@@ -276,11 +293,11 @@ void bwd_dq_bf16(BwdArgs a) {
     // Products i = 4c + 2kt + {0: S, 1: dP}, their K or V operand read two products
     // ahead; the fences keep that order.
     constexpr int NP = 4 * (D / 16);
-    bf16x8 fa[3];
+    v8 fa[3];
     auto fread = [&](int i) {
       const int c = i >> 2, kt = (i >> 1) & 1;
       fa[i % 3] = __builtin_bit_cast(
-          bf16x8, ld16(st + ((i & 1) ? OFF_V : 0) + rfrag + kt * 32 * RP + 32 * c));
+          v8, ld16(st + ((i & 1) ? OFF_V : 0) + rfrag + kt * 32 * RP + 32 * c));
     };
     __builtin_amdgcn_sched_barrier(0);
     fread(0);
@@ -289,8 +306,8 @@ void bwd_dq_bf16(BwdArgs a) {
     for (int i = 0; i < NP; ++i) {
       if (i + 2 < NP) fread(i + 2);
       const int c = i >> 2, kt = (i >> 1) & 1;
-      if (i & 1) dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i % 3], dof[c], dp[kt], 0, 0, 0);
-      else s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i % 3], qf[c], s[kt], 0, 0, 0);
+      if (i & 1) dp[kt] = mfma16(fa[i % 3], dof[c], dp[kt]);
+      else s[kt] = mfma16(fa[i % 3], qf[c], s[kt]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -330,7 +347,7 @@ void bwd_dq_bf16(BwdArgs a) {
         }
     }
     // dS^T operand: chunk c = keys 16c + 8hf + 0..7 (registers 8(c%2) .. +7 of kt = c/2)
-    bf16x8 dsf[4];
+    v8 dsf[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4 w;
@@ -339,23 +356,23 @@ void bwd_dq_bf16(BwdArgs a) {
         const int kt = c >> 1, r = 8 * (c & 1) + 2 * e;
         const float d0 = exp2_fast(x[kt][r]) * (dp[kt][r] - delta);
         const float d1 = exp2_fast(x[kt][r + 1]) * (dp[kt][r + 1] - delta);
-        w[e] = pack_bf16(d0, d1);
+        w[e] = pack2<E>(d0, d1);
       }
-      dsf[c] = __builtin_bit_cast(bf16x8, w);
+      dsf[c] = __builtin_bit_cast(v8, w);
     }
     // dQ^T += K^T dS^T, operands two products ahead (i = c * (D / 32) + dt)
     const char* ktr = st + OFF_KT + tfrag;
     constexpr int NQ = 4 * (D / 32);
-    bf16x8 ta[3];
-    auto tread = [&](int i) { ta[i % 3] = tr_operand<TP>(ktr, i / (D / 32), i % (D / 32)); };
+    v8 ta[3];
+    auto tread = [&](int i) { ta[i % 3] = tr_operand<v8, TP>(ktr, i / (D / 32), i % (D / 32)); };
     __builtin_amdgcn_sched_barrier(0);
     tread(0);
     tread(1);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       if (i + 2 < NQ) tread(i + 2);
-      dq[i % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i % 3], dsf[i / (D / 32)],
-                                                                 dq[i % (D / 32)], 0, 0, 0);
+      dq[i % (D / 32)] = mfma16(ta[i % 3], dsf[i / (D / 32)],
+                                                                 dq[i % (D / 32)]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -370,7 +387,7 @@ void bwd_dq_bf16(BwdArgs a) {
     __syncthreads();
   }
 
-  if (q_ok) store_row_bf16<D>(dqb + int64_t(qi) * a.sdq[2], dq, a.scale, hf);
+  if (q_ok) store_row<E, D>(dqb + int64_t(qi) * a.sdq[2], dq, a.scale, hf);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -381,18 +398,19 @@ void bwd_dq_bf16(BwdArgs a) {
 //   both:     S[qs] = Q[qs] K^T         (Q rows read in perm5 order: register r of half hf
 //                                         is query 32qs + 16(r/8) + 8hf + r%8)
 //             P = 2^(S scale log2e - lse2[query]), hidden -> 0
-//   P wave:   dV^T += dO^T P             (dO^T by transposed reads, P in bf16)
+//   P wave:   dV^T += dO^T P             (dO^T by transposed reads, P in the input type)
 //   dS wave:  dP[qs] = dO[qs] V^T,  dS = P * (dP - delta[query]),
-//             dK^T += Q^T dS             (Q^T by transposed reads, dS in bf16)
+//             dK^T += Q^T dS             (Q^T by transposed reads, dS in the input type)
 // The scores are computed by both waves (a fifth product per pair instead of an exchange
 // of P through LDS, which holds the staged tiles); the dS wave carries three products and
 // the P wave two, and on each SIMD one wave's vector work runs under the other's products.
 // The P waves also stage the tiles.  LDS stage: Q row copy | Q transposed-read copy | dO row copy | dO transposed-read copy |
 // lse2[64] | delta[64].
 // ---------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK>
+template <typename E, int D, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(kThreadsBwdK) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_bf16(BwdArgs a) {
+void bwd_dkdv(BwdArgs a) {
+  typedef typename Vec16<E>::v8 v8;
   constexpr int BQ = kBwdStep;
   constexpr int NT = kThreadsBwdK / 2;  // the P waves stage the tiles
   constexpr int DG = D / 8;
@@ -440,7 +458,7 @@ void bwd_dkdv_bf16(BwdArgs a) {
 
   // K^T right operand of S (both waves) and V^T right operand of dP (dS wave): column =
   // this lane's key, half hf supplies head dims 16c + 8hf .. +7 of chunk c.
-  bf16x8 kf[D / 16], vf[D / 16];
+  v8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     u32x4 wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
@@ -448,8 +466,8 @@ void bwd_dkdv_bf16(BwdArgs a) {
       wk = ld16(kb + int64_t(kj) * a.sk[2] + 16 * c + 8 * hf);
       if (ds_wave) wv = ld16(vb + int64_t(kj) * a.sv[2] + 16 * c + 8 * hf);
     }
-    kf[c] = __builtin_bit_cast(bf16x8, wk);
-    vf[c] = __builtin_bit_cast(bf16x8, wv);
+    kf[c] = __builtin_bit_cast(v8, wk);
+    vf[c] = __builtin_bit_cast(v8, wv);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -519,7 +537,7 @@ void bwd_dkdv_bf16(BwdArgs a) {
     const float* lse2s = reinterpret_cast<const float*>(st + OFF_LSE);
     const float* dels = reinterpret_cast<const float*>(st + OFF_DEL);
     const bool edge = CAUSAL && qt0 + coff < kw + 31;
-    bf16x8 opf[4];  // P (P wave) or dS (dS wave): chunk c = queries 16c + 8hf + 0..7
+    v8 opf[4];  // P (P wave) or dS (dS wave): chunk c = queries 16c + 8hf + 0..7
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       f32x16 sc, dp;
@@ -528,19 +546,19 @@ void bwd_dkdv_bf16(BwdArgs a) {
       // Operands are read two chunks ahead of their products; the fences keep that order
       // (near the register limit the scheduler would otherwise read each operand just
       // before its product and wait out the full LDS latency every time).
-      bf16x8 qa[3], da[3];
+      v8 qa[3], da[3];
       auto read = [&](int c) {
-        qa[c % 3] = __builtin_bit_cast(bf16x8, ld16(st + rfrag + qs * 32 * RP + 32 * c));
+        qa[c % 3] = __builtin_bit_cast(v8, ld16(st + rfrag + qs * 32 * RP + 32 * c));
         if (DS)
-          da[c % 3] = __builtin_bit_cast(bf16x8, ld16(st + OFF_DR + rfrag + qs * 32 * RP + 32 * c));
+          da[c % 3] = __builtin_bit_cast(v8, ld16(st + OFF_DR + rfrag + qs * 32 * RP + 32 * c));
       };
       read(0);
       read(1);
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         if (c + 2 < D / 16) read(c + 2);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c % 3], kf[c], sc, 0, 0, 0);
-        if (DS) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[c % 3], vf[c], dp, 0, 0, 0);
+        sc = mfma16(qa[c % 3], kf[c], sc);
+        if (DS) dp = mfma16(da[c % 3], vf[c], dp);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -572,24 +590,24 @@ void bwd_dkdv_bf16(BwdArgs a) {
             const float p = exp2_fast(xv);
             o[u] = DS ? p * (dp[r] - (i < 4 ? d0[i] : d1[i - 4])) : p;
           }
-          w[e] = pack_bf16(o[0], o[1]);
+          w[e] = pack2<E>(o[0], o[1]);
         }
-        opf[c] = __builtin_bit_cast(bf16x8, w);
+        opf[c] = __builtin_bit_cast(v8, w);
       }
     }
     // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); operands two products ahead
     const char* ltr = st + (DS ? OFF_QT : OFF_DT) + tfrag;
     constexpr int NP = 4 * (D / 32);  // products, i = c * (D / 32) + dt
-    bf16x8 ta[3];
-    auto tread = [&](int i) { ta[i % 3] = tr_operand<TP>(ltr, i / (D / 32), i % (D / 32)); };
+    v8 ta[3];
+    auto tread = [&](int i) { ta[i % 3] = tr_operand<v8, TP>(ltr, i / (D / 32), i % (D / 32)); };
     __builtin_amdgcn_sched_barrier(0);
     tread(0);
     tread(1);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (i + 2 < NP) tread(i + 2);
-      acc[i % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i % 3], opf[i / (D / 32)],
-                                                                  acc[i % (D / 32)], 0, 0, 0);
+      acc[i % (D / 32)] = mfma16(ta[i % 3], opf[i / (D / 32)],
+                                                                  acc[i % (D / 32)]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -607,36 +625,36 @@ void bwd_dkdv_bf16(BwdArgs a) {
       store((t + 1) & 1);
       __syncthreads();
     }
-    if (k_ok) store_row_bf16<D>(dvb + int64_t(kj) * a.sdv[2], acc, 1.f, hf);
+    if (k_ok) store_row<E, D>(dvb + int64_t(kj) * a.sdv[2], acc, 1.f, hf);
   } else {
     __syncthreads();
     for (int t = tbeg; t < ntiles; ++t) {
       if (wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw)) compute(std::true_type{}, t);
       __syncthreads();
     }
-    if (k_ok) store_row_bf16<D>(dkb + int64_t(kj) * a.sdk[2], acc, a.scale, hf);
+    if (k_ok) store_row<E, D>(dkb + int64_t(kj) * a.sdk[2], acc, a.scale, hf);
   }
 }
 
-template <int D, bool CAUSAL, bool MASK>
+template <typename E, int D, bool CAUSAL, bool MASK>
 hipError_t launch_pair(const BwdArgs& a, unsigned grid_q, unsigned grid_k, hipStream_t s) {
   void* args[] = {const_cast<BwdArgs*>(&a)};
   if (grid_q) {
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_bf16<D, CAUSAL, MASK>),
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq<E, D, CAUSAL, MASK>),
                                          dim3(grid_q), dim3(kThreadsBwdQ), args, 0, s);
     if (e != hipSuccess) return e;
   }
   if (grid_k)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_bf16<D, CAUSAL, MASK>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv<E, D, CAUSAL, MASK>),
                            dim3(grid_k), dim3(kThreadsBwdK), args, 0, s);
   return hipSuccess;
 }
 
-template <int D>
+template <typename E, int D>
 hipError_t launch_bwd_d(const BwdArgs& a, bool causal, unsigned gq, unsigned gk, hipStream_t s) {
   const bool m = a.mask != nullptr;
-  if (causal) return m ? launch_pair<D, true, true>(a, gq, gk, s) : launch_pair<D, true, false>(a, gq, gk, s);
-  return m ? launch_pair<D, false, true>(a, gq, gk, s) : launch_pair<D, false, false>(a, gq, gk, s);
+  if (causal) return m ? launch_pair<E, D, true, true>(a, gq, gk, s) : launch_pair<E, D, true, false>(a, gq, gk, s);
+  return m ? launch_pair<E, D, false, true>(a, gq, gk, s) : launch_pair<E, D, false, false>(a, gq, gk, s);
 }
 
 }  // namespace
@@ -678,8 +696,12 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   a.coff = p.causal == 2 ? int32_t(p.Lk - p.Lq) : 0;
   const unsigned gq = unsigned(int64_t(a.q_items) * a.bh_count);
   const unsigned gk = unsigned(int64_t(a.k_items) * a.bh_count);
-  if (p.D == 64) return launch_bwd_d<64>(a, p.causal != 0, gq, gk, stream);
-  return launch_bwd_d<128>(a, p.causal != 0, gq, gk, stream);
+  const bool causal = p.causal != 0;
+  if (p.dtype == 2)
+    return p.D == 64 ? launch_bwd_d<_Float16, 64>(a, causal, gq, gk, stream)
+                     : launch_bwd_d<_Float16, 128>(a, causal, gq, gk, stream);
+  return p.D == 64 ? launch_bwd_d<__bf16, 64>(a, causal, gq, gk, stream)
+                   : launch_bwd_d<__bf16, 128>(a, causal, gq, gk, stream);
 }
 
 }  // namespace sdpa

@@ -10,8 +10,8 @@
 // diagonal are never computed, and a row with no visible key yields zeros (the math
 // backend's safe softmax).
 //
-// Work decomposition (bf16 and fp32 kernels alike):
-//   * a workgroup owns a tile of query rows of one (b, h): 256 rows in 8 waves (bf16) or
+// Work decomposition (16-bit and fp32 kernels alike):
+//   * a workgroup owns a tile of query rows of one (b, h): 256 rows in 8 waves (bf16, fp16) or
 //     128 rows in 4 waves (fp32); each wave owns 32 query rows;
 //   * lane l serves query row (l % 32) and half h = l / 32 of every key tile, so all
 //     per-row softmax state (running max, running sum, rescale factor) is a per-lane
@@ -166,7 +166,8 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ inline int perm5(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // ---------------------------------------------------------------------------------------
-// bf16 kernel: bf16 MFMA 32x32x16 for both products, fp32 accumulation and softmax.
+// 16-bit kernel (bf16 or fp16 inputs): 32x32x16 MFMA of that type for both products, fp32
+// accumulation and softmax, P rounded to the input type.
 //
 // A workgroup is 8 waves owning 256 query rows of one (b, h), 32 rows per wave; each
 // SIMD hosts two of its waves, one from each of two groups.  Per key tile t of 64 keys,
@@ -196,11 +197,27 @@ __device__ inline int perm5(int m) { return (m & 0x13) | ((m & 4) << 1) | ((m & 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit element types of the matrix-core kernel: bf16 (8 significand bits, fp32's
+// range) or IEEE fp16 (11 bits, range to 65504).  Both use the same 32x32x16 product shape
+// and operand layouts; only the product instruction and the rounding of P differ.
+template <typename E> struct Vec16;
+template <> struct Vec16<__bf16> { typedef bf16x8 v8; typedef bf16x2 v2; };
+template <> struct Vec16<_Float16> { typedef f16x8 v8; typedef f16x2 v2; };
+
+__device__ inline f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x16 mfma16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // The running max used as the exponent reference may lag the true row max by up to this
-// many base-2 units before O and l are rescaled: p = 2^(x - m_ref) then stays <= 256,
-// exact in fp32 accumulation and in bf16 (8 significand bits at every magnitude), and
+// many base-2 units before O and l are rescaled: p = 2^(x - m_ref) then stays <= 256, far
+// inside the range of fp32, bf16 and fp16 (whose largest finite value is 65504), and
 // the final O / l is unchanged because both carry the same reference.
 constexpr float kRescaleSlack = 8.0f;
 
@@ -209,9 +226,11 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-template <int D, bool CAUSAL, bool MASK, bool POS, int MODE>
+template <typename E, int D, bool CAUSAL, bool MASK, bool POS, int MODE>
 __global__ __launch_bounds__(kThreadsBf16) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_bf16(Args a) {
+void fwd_mfma(Args a) {
+  typedef typename Vec16<E>::v8 v8;
+  typedef typename Vec16<E>::v2 v2;
   constexpr int BN = kBlockNBf16;
   constexpr int NT = kThreadsBf16;
   constexpr int DG = D / 8;                // 16-byte chunks per row
@@ -254,12 +273,12 @@ void fwd_bf16(Args a) {
 
   // Q^T operand fragments, held for the whole key walk: chunk c covers head dims
   // 16c..16c+15, half hf supplies dims 16c+8hf..16c+8hf+7.
-  bf16x8 qf[D / 16];
+  v8 qf[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     u32x4 w = {0, 0, 0, 0};
     if (q_ok) w = ld16(qb + int64_t(qi) * a.sq[2] + 16 * c + 8 * hf);
-    qf[c] = __builtin_bit_cast(bf16x8, w);
+    qf[c] = __builtin_bit_cast(v8, w);
   }
   // Retire the Q loads here, on every path: left in flight, they would make the
   // memory-counter wait in the key loop cover the K/V prefetch as well.
@@ -332,8 +351,8 @@ void fwd_bf16(Args a) {
   float l_run = 0.f;        // sum of 2^(x - m_ref) over this lane's key half
   f32x16 s[2];              // scores of tile t; sub-tile kt, register r = key
                             // 32kt + 16(r/8) + 8hf + r%8
-  bf16x8 pf[4];             // P^T operand of tile t: chunk c = keys 16c + 8hf .. +7
-  bf16x8 kpre[KPRE];        // first K fragments of the next S, read ahead in the vector phase
+  v8 pf[4];             // P^T operand of tile t: chunk c = keys 16c + 8hf .. +7
+  v8 kpre[KPRE];        // first K fragments of the next S, read ahead in the vector phase
 
   // K operand fragment i of a tile's S, in the order the products consume them:
   // i = 2c + kt is head-dim chunk c (dims 16c..16c+15) of key sub-tile kt.
@@ -346,7 +365,7 @@ void fwd_bf16(Args a) {
     if (t >= wtiles) return;
     const char* kfp = lds + (t & 1) * KT + kfrag;
 #pragma unroll
-    for (int i = 0; i < KPRE; ++i) kpre[i] = __builtin_bit_cast(bf16x8, ld16(kfp + kfrag_off(i)));
+    for (int i = 0; i < KPRE; ++i) kpre[i] = __builtin_bit_cast(v8, ld16(kfp + kfrag_off(i)));
   };
 
   // Matrix phase M(t): S^T(t) = K(t) Q^T, then O^T += V^T(t-1) P^T(t-1).  It runs at
@@ -360,17 +379,17 @@ void fwd_bf16(Args a) {
     __builtin_amdgcn_s_setprio(1);
     if (t < wtiles) {
       const char* kfp = lds + (t & 1) * KT + kfrag;
-      bf16x8 kf[NKF];
+      v8 kf[NKF];
 #pragma unroll
       for (int i = 0; i < NKF; ++i)
-        kf[i] = i < KPRE ? kpre[i] : __builtin_bit_cast(bf16x8, ld16(kfp + kfrag_off(i)));
+        kf[i] = i < KPRE ? kpre[i] : __builtin_bit_cast(v8, ld16(kfp + kfrag_off(i)));
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
       for (int i = 0; i < NKF; ++i)
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+        s[i & 1] = mfma16(kf[i], qf[i >> 1], s[i & 1]);
       // Up to four reads first, then one product per read until the reads are issued,
       // then the remaining products.
       constexpr int R0 = NKF - KPRE < 4 ? NKF - KPRE : 4;
@@ -393,8 +412,8 @@ void fwd_bf16(Args a) {
           const s16x4 lo = ds_read_tr(vfp + (16 * c) * VP + 64 * dt);
           const s16x4 hi = ds_read_tr(vfp + (16 * c + 4) * VP + 64 * dt);
           const s16x4 both[2] = {lo, hi};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[dt], 0, 0, 0);
+          const v8 vf = __builtin_bit_cast(v8, both);
+          o[dt] = mfma16(vf, pf[c], o[dt]);
         }
       // Keep LDS reads ahead of the products: the first 8 reads, then one product per
       // two reads, then the remaining products.
@@ -470,7 +489,7 @@ void fwd_bf16(Args a) {
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
     const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-    // p = 2^(x - mu), rounded to bf16 two at a time into the P^T operand.  The row sum
+    // p = 2^(x - mu), rounded to the input type two at a time into the P^T operand.  The row sum
     // adds the fp32 values (the lse needs them unrounded) in two independent chains.
     float ps[2];
 #pragma unroll
@@ -482,9 +501,9 @@ void fwd_bf16(Args a) {
         const f32x2 pp = {exp2_fast(__builtin_fmaf(s[c >> 1][r], c2, -mu)),
                           exp2_fast(__builtin_fmaf(s[c >> 1][r + 1], c2, -mu))};
         ps[c & 1] = c < 2 && e == 0 ? pp[0] + pp[1] : ps[c & 1] + pp[0] + pp[1];
-        w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, bf16x2));
+        w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, v2));
       }
-      pf[c] = __builtin_bit_cast(bf16x8, w);
+      pf[c] = __builtin_bit_cast(v8, w);
     }
     l_run += ps[0] + ps[1];
   };
@@ -549,8 +568,8 @@ void fwd_bf16(Args a) {
         uint32_t w[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const __bf16 lo = static_cast<__bf16>(o[dt][4 * g + 2 * e] * inv);
-          const __bf16 hi = static_cast<__bf16>(o[dt][4 * g + 2 * e + 1] * inv);
+          const E lo = static_cast<E>(o[dt][4 * g + 2 * e] * inv);
+          const E hi = static_cast<E>(o[dt][4 * g + 2 * e + 1] * inv);
           w[e] = uint32_t(__builtin_bit_cast(uint16_t, lo)) |
                  (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
@@ -565,7 +584,7 @@ void fwd_bf16(Args a) {
 
 // ---------------------------------------------------------------------------------------
 // fp32 kernel: fp32 MFMA 32x32x2 (true fp32 products, fp32 accumulation) for both
-// products; same decomposition as the bf16 kernel, probabilities stay fp32.
+// products; same decomposition as the 16-bit kernel, probabilities stay fp32.
 // ---------------------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool MASK, int MODE>
 __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
@@ -781,7 +800,7 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
 // ---------------------------------------------------------------------------------------
 constexpr int kCombineRows = 4;  // rows (waves) per workgroup
 
-template <int D, bool BF16>
+template <int D, typename T>
 __global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int nsplit) {
   const int lane = threadIdx.x & 63;
   const int64_t rows = int64_t(a.bh_count) * a.Lq;
@@ -808,10 +827,7 @@ __global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) {
     const int64_t off = b * a.so[0] + h * a.so[1] + i * a.so[2] + lane + 64 * e;
-    if (BF16)
-      static_cast<__bf16*>(a.out)[off] = static_cast<__bf16>(acc[e] * inv);
-    else
-      static_cast<float*>(a.out)[off] = acc[e] * inv;
+    static_cast<T*>(a.out)[off] = static_cast<T>(acc[e] * inv);
   }
   if (a.lse && lane == 0)
     a.lse[row] = wsum > 0.f ? m + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
@@ -821,9 +837,13 @@ template <int D, bool CAUSAL, bool MASK, int MODE>
 hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Args*>(&a)};
   const void* fn;
+  const bool pos = a.scale_log2 > 0.f;
   if (dtype == 1)
-    fn = a.scale_log2 > 0.f ? reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, true, MODE>)
-                            : reinterpret_cast<const void*>(&fwd_bf16<D, CAUSAL, MASK, false, MODE>);
+    fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MASK, true, MODE>)
+             : reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MASK, false, MODE>);
+  else if (dtype == 2)
+    fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MASK, true, MODE>)
+             : reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MASK, false, MODE>);
   else
     fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK, MODE>);
   return hipLaunchKernel(fn, dim3(grid), dim3(block_threads(dtype)), args, 0, stream);
@@ -849,8 +869,9 @@ hipError_t launch_combine(const Args& a, int dtype, int nsplit, hipStream_t s) {
   const unsigned grid = unsigned((rows + kCombineRows - 1) / kCombineRows);
   int ns = nsplit;
   void* args[] = {const_cast<Args*>(&a), &ns};
-  const void* fn = dtype == 1 ? reinterpret_cast<const void*>(&splitkv_combine<D, true>)
-                              : reinterpret_cast<const void*>(&splitkv_combine<D, false>);
+  const void* fn = dtype == 1   ? reinterpret_cast<const void*>(&splitkv_combine<D, __bf16>)
+                   : dtype == 2 ? reinterpret_cast<const void*>(&splitkv_combine<D, _Float16>)
+                                : reinterpret_cast<const void*>(&splitkv_combine<D, float>);
   return hipLaunchKernel(fn, dim3(grid), dim3(64 * kCombineRows), args, 0, s);
 }
 

@@ -17,10 +17,11 @@ constexpr int kBlockNBf16 = 64;
 constexpr int kThreadsF32 = 256;
 constexpr int kBlockMF32 = 128;
 constexpr int kBlockNF32 = 64;
-// dtype: 1 = bf16, 0 = fp32 (the values of sdpa_dtype)
-constexpr int block_m(int dtype) { return dtype == 1 ? kBlockMBf16 : kBlockMF32; }
-constexpr int block_n(int dtype) { return dtype == 1 ? kBlockNBf16 : kBlockNF32; }
-constexpr int block_threads(int dtype) { return dtype == 1 ? kThreadsBf16 : kThreadsF32; }
+// dtype: 0 = fp32, 1 = bf16, 2 = fp16 (the values of sdpa_dtype); both 16-bit types run
+// the same matrix-core kernel and tiles
+constexpr int block_m(int dtype) { return dtype != 0 ? kBlockMBf16 : kBlockMF32; }
+constexpr int block_n(int dtype) { return dtype != 0 ? kBlockNBf16 : kBlockNF32; }
+constexpr int block_threads(int dtype) { return dtype != 0 ? kThreadsBf16 : kThreadsF32; }
 
 // Rank-3 [N,L,D] and rank-4 [B,H,L,D] inputs both become this (b, h, row, col) view;
 // every stride is in elements of the tensor's own type.  Packed variable-length inputs
@@ -133,6 +134,7 @@ struct BwdProblem {
   int64_t sq[4], sk[4], sv[4], so[4], sdo[4], sdq[4], sdk[4], sdv[4], sm[4];
   float scale;
   int causal;
+  int dtype;  // 1 bf16, 2 fp16
 };
 
 // Launches the dQ kernel (B*H*Lq > 0) and then the dK/dV kernel (B*H*Lk > 0) on

@@ -100,7 +100,8 @@ def test_shape_errors():
 def test_head_dim_and_dtype_errors():
     for D in (0, 32, 96, 256):
         assert check(**args4(D=D)) == HEAD
-    assert check(**args4(dtype=2)) == DTYPE
+    assert check(**args4(dtype=sd.SDPA_F16)) == OK
+    assert check(**args4(dtype=3)) == DTYPE
     assert check(**args4(dtype=-1)) == DTYPE
 
 
@@ -265,7 +266,8 @@ def test_bwd_check_valid_and_rank3():
 
 
 def test_bwd_check_errors():
-    assert bcheck(**bargs(dtype=sd.SDPA_F32)) == DTYPE  # the backward is bf16 only
+    assert bcheck(**bargs(dtype=sd.SDPA_F32)) == DTYPE  # the backward is 16-bit only
+    assert bcheck(**bargs(dtype=sd.SDPA_F16)) == OK
     assert bcheck(**bargs(D=96)) == HEAD
     assert bcheck(**bargs(rank=5)) == RANK
     assert bcheck(**bargs(Lq=-1)) == SHAPE
@@ -345,6 +347,7 @@ def test_varlen_check():
     assert vcheck(**vargs(dtype=sd.SDPA_F32, D=128)) == OK
     assert vcheck(**vargs(D=96)) == HEAD
     assert vcheck(**vargs(dtype=3)) == DTYPE
+    assert vcheck(**vargs(dtype=sd.SDPA_F16)) == OK
     assert vcheck(**vargs(causal=4)) == CAUSAL_ERR
     assert vcheck(**vargs(nseq=-1)) == SHAPE
     assert vcheck(**vargs(max_q=101)) == SHAPE  # longer than every token

@@ -1,6 +1,7 @@
 """GPU parity: the HIP kernel (through the C ABI) against the fp64 oracle.
 
-Tolerances (max-abs, element by element): out 1e-2 for bf16 and 2e-5 for fp32 inputs,
+Tolerances (max-abs, element by element): out 1e-2 for bf16 (and fp16, read the same way)
+and 2e-5 for fp32 inputs,
 LSE 1e-3 on finite rows; rows with no visible key must be exactly 0 with LSE -inf on
 both sides.  Small problems are compared on every output; the full-size workloads on
 sampled rows (the oracle evaluates them one by one) plus properties that hold at any
@@ -18,11 +19,11 @@ from scaled_dot_product_11_amd import SdpaError, sdpa_fwd
 
 pytestmark = pytest.mark.gpu
 
-OUT_TOL = {torch.bfloat16: 1e-2, torch.float32: 2e-5}
+OUT_TOL = {torch.bfloat16: 1e-2, torch.float16: 1e-2, torch.float32: 2e-5}
 LSE_TOL = 1e-3
 # significand bits of the output format: the bound applies to the value the kernel
 # computes, and storing it in the output dtype adds at most half a unit in the last place
-OUT_BITS = {torch.bfloat16: 8, torch.float32: 24}
+OUT_BITS = {torch.bfloat16: 8, torch.float16: 11, torch.float32: 24}
 DEV = "cuda"
 
 
@@ -101,7 +102,8 @@ def test_config1_full():
 SHAPES = [(1, 1), (33, 33), (64, 64), (127, 127), (129, 129), (200, 200), (77, 300), (300, 77)]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mode", ["none", "causal", "mask", "causal_mask", "bcast_mask"])
 def test_ragged_small(dtype, D, mode):
@@ -113,7 +115,8 @@ def test_ragged_small(dtype, D, mode):
         compare(out, lse, ro, rl, dtype, f"{mode} D={D} Lq={Lq} Lk={Lk}")
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
 def test_rank3_small_and_equals_rank4(dtype):
     q, k, v, mask = rand_inputs(7, 1, 3, 150, 150, 64, dtype, rank=3, mask_mode="full")
     out3, lse3, ro, rl = run_both(q, k, v, mask, True)
@@ -170,7 +173,7 @@ def test_invalid_arguments_raise():
     q = torch.randn(1, 1, 16, 96, device=DEV).to(torch.bfloat16)
     with pytest.raises(SdpaError):
         sdpa_fwd(q, q, q)
-    q = torch.randn(1, 1, 16, 64, device=DEV).to(torch.float16)
+    q = torch.randn(1, 1, 16, 64, device=DEV).to(torch.float64)
     with pytest.raises(SdpaError):
         sdpa_fwd(q, q, q)
 
@@ -214,6 +217,16 @@ def test_config2_full_oracle():
     out, lse = run_wl(wl)
     ro, rl = sdpa_oracle(wl.q, wl.k, wl.v, is_causal=True, scale=wl.scale)
     compare(out, lse, ro, rl, torch.bfloat16, wl.name)
+
+
+def test_config2_fp16_full_oracle():
+    """The c2 draws in fp16 (bf16 values are exact in fp16 at these magnitudes)."""
+    wl = W.config2()
+    q, k, v = (t.to(torch.float16) for t in (wl.q, wl.k, wl.v))
+    out, lse = sdpa_fwd(to_dev(q), to_dev(k), to_dev(v), is_causal=True, scale=wl.scale)
+    torch.cuda.synchronize()
+    ro, rl = sdpa_oracle(q, k, v, is_causal=True, scale=wl.scale)
+    compare(out, lse, ro, rl, torch.float16, wl.name + " fp16")
 
 
 def test_config3_rank3_equals_rank4_bitwise():

@@ -57,9 +57,9 @@ def compare_grads(got, ref, where="", names=("dq", "dk", "dv")):
     return errs
 
 
-def rand_inputs(seed, B, H, Lq, Lk, D, mask_mode=None, p_keep=0.3):
+def rand_inputs(seed, B, H, Lq, Lk, D, mask_mode=None, p_keep=0.3, dtype=torch.bfloat16):
     g = torch.Generator().manual_seed(seed)
-    q, k, v = W.draw_qkv(g, (B, H, Lq, D), (B, H, Lk, D))
+    q, k, v = W.draw_qkv(g, (B, H, Lq, D), (B, H, Lk, D), dtype=dtype)
     mask = None
     if mask_mode is not None:
         mask = torch.rand((B, 1 if mask_mode == "bcast" else H, Lq, Lk), generator=g) < p_keep
@@ -86,13 +86,14 @@ def gpu_grads(q, k, v, dout, mask, causal, scale=None, poison=True):
 SHAPES = [(1, 1), (33, 33), (64, 64), (127, 127), (129, 129), (200, 200), (77, 300), (300, 77)]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mode", ["none", "causal", "mask", "causal_mask", "bcast_mask"])
-def test_bwd_ragged_small(D, mode):
+def test_bwd_ragged_small(dtype, D, mode):
     causal = "causal" in mode
     mm = None if mode in ("none", "causal") else ("bcast" if mode == "bcast_mask" else "full")
     for n, (Lq, Lk) in enumerate(SHAPES):
-        q, k, v, mask = rand_inputs(1000 + 10 * n + D, 2, 3, Lq, Lk, D, mm)
+        q, k, v, mask = rand_inputs(1000 + 10 * n + D, 2, 3, Lq, Lk, D, mm, dtype=dtype)
         dout = W.upstream_grad(2000 + n, q)
         got = gpu_grads(q, k, v, dout, mask, causal)
         ref = sdpa_bwd_oracle(q, k, v, dout, mask=mask, is_causal=causal)
@@ -158,7 +159,7 @@ def test_bwd_invalid_arguments_raise():
     q, k, v, _ = rand_inputs(17, 1, 1, 8, 8, 64)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     out, lse = sdpa_fwd(qd, kd, vd)
-    with pytest.raises(SdpaError, match="SDPA_ERR_DTYPE"):
+    with pytest.raises(SdpaError, match="SDPA_ERR_DTYPE"):  # fp32 has no backward
         f = [t.float() for t in (qd, kd, vd, out)]
         sdpa_bwd(*f[:3], f[3], f[3], lse)
     with pytest.raises(SdpaError, match="SDPA_ERR_HEAD_DIM"):
@@ -169,12 +170,14 @@ def test_bwd_invalid_arguments_raise():
 # ---------------------------------------------------------------------------------------
 # full-size workloads
 
-def test_bwd_config2_full_oracle():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_bwd_config2_full_oracle(dtype):
     wl = W.config2()
-    dout = W.upstream_grad(21, wl.q)
-    got = gpu_grads(wl.q, wl.k, wl.v, dout, None, True, wl.scale)
-    compare_grads(got, sdpa_bwd_oracle(wl.q, wl.k, wl.v, dout, is_causal=True, scale=wl.scale),
-                  wl.name)
+    q, k, v = (t.to(dtype) for t in (wl.q, wl.k, wl.v))  # fp16: the bf16 draws, exactly
+    dout = W.upstream_grad(21, q)
+    got = gpu_grads(q, k, v, dout, None, True, wl.scale)
+    compare_grads(got, sdpa_bwd_oracle(q, k, v, dout, is_causal=True, scale=wl.scale),
+                  f"{wl.name} {dtype}")
 
 
 def test_bwd_config3_rank3_equals_rank4_and_heads():

@@ -57,7 +57,8 @@ CASES = [  # (Lq, Lk, num_splits)
 ]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [0, 1, 2], ids=["none", "top_left", "bottom_right"])
 def test_splitkv_decode_shapes(dtype, D, causal):

@@ -41,7 +41,8 @@ def rand4(seed, B, H, Lq, Lk, D, dtype):
 SHAPES = [(1, 1), (5, 300), (77, 300), (300, 77), (129, 129), (64, 200), (200, 64), (256, 1000)]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_bottom_right_forward(dtype, D):
     for n, (Lq, Lk) in enumerate(SHAPES):
@@ -131,7 +132,8 @@ Q_LENGTHS = [0, 1, 77, 256, 300, 5, 129]
 K_LENGTHS = [3, 1, 77, 300, 256, 0, 129]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [0, 1, 2], ids=["none", "top_left", "bottom_right"])
 def test_varlen_small(dtype, D, causal):
