@@ -51,6 +51,13 @@ def _load():
             ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
             ctypes.c_void_p, i64p,
             ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64, dp, dp, ctypes.c_int]
+        lib.oracle_sdpa_fwd_bias.restype = ctypes.c_int
+        lib.oracle_sdpa_fwd_bias.argtypes = [
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64,
+            ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
+            ctypes.c_void_p, i64p, dp, i64p,
+            ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64, dp, dp, ctypes.c_int]
         lib.oracle_sdpa_bwd.restype = ctypes.c_int
         lib.oracle_sdpa_bwd.argtypes = [
             ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -142,12 +149,15 @@ def sdpa_bwd_oracle(q, k, v, dout, *, mask=None, is_causal=False, scale=None, nt
     return dq.reshape(tuple(q.shape)), dk.reshape(tuple(k.shape)), dv.reshape(tuple(v.shape))
 
 
-def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, nthreads=0):
+def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, nthreads=0,
+                bias=None):
     """Evaluate the plain definition in fp64.
 
     q: [N,Lq,D] or [B,H,Lq,D]; k, v: same rank with Lk rows; CPU tensors (or numpy) of one
     dtype among float32 / bfloat16 / float16 / float64, any strides.  mask: optional bool or uint8
     tensor broadcastable to [B,H,Lq,Lk] (rank 4) or [N,Lq,Lk] (rank 3); nonzero = visible.
+    bias: optional float tensor of the same broadcast shapes, added to the scaled scores
+    (-inf hides a key), read exactly in fp64.
     rows: optional int64 flat row ids (b*H + h)*Lq + i.
 
     Returns (out, lse) as float64 numpy arrays: shaped like q and q.shape[:-1] when rows is
@@ -186,6 +196,13 @@ def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, n
         ms_arr = (ctypes.c_int64 * 4)(*ms)
         mptr = ctypes.c_void_p(mask_t.data_ptr())
 
+    bptr, bs_arr, bias_t = None, None, None
+    if bias is not None:
+        # converted in its own (unbroadcast) shape, then broadcast with zero strides
+        bias_t = _as_tensor(bias).to(torch.float64).expand(tuple(q.shape[:-1]) + (Lk,))
+        bs_arr = (ctypes.c_int64 * 4)(*_strides4(bias_t))
+        bptr = ctypes.cast(ctypes.c_void_p(bias_t.data_ptr()), ctypes.POINTER(ctypes.c_double))
+
     if rows is None:
         n = B * H * Lq
         rows_arr, rows_ptr = None, None
@@ -200,10 +217,10 @@ def sdpa_oracle(q, k, v, *, mask=None, is_causal=False, scale=None, rows=None, n
     ks = (ctypes.c_int64 * 4)(*_strides4(k))
     vs = (ctypes.c_int64 * 4)(*_strides4(v))
     lib = _load()
-    st = lib.oracle_sdpa_fwd(
+    st = lib.oracle_sdpa_fwd_bias(
         _DTYPE_CODE[q.dtype], B, H, Lq, Lk, D,
         ctypes.c_void_p(q.data_ptr()), qs, ctypes.c_void_p(k.data_ptr()), ks,
-        ctypes.c_void_p(v.data_ptr()), vs, mptr, ms_arr,
+        ctypes.c_void_p(v.data_ptr()), vs, mptr, ms_arr, bptr, bs_arr,
         1 if is_causal else 0, float(scale), rows_ptr, n,
         out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
         lse.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))

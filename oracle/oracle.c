@@ -86,9 +86,9 @@ static int allowed(int is_causal, const uint8_t* mask, const int64_t* ms, int64_
  */
 static void one_row(int dtype, int64_t Lk, int64_t D, const void* q, const int64_t* qs,
                     const void* k, const int64_t* ks, const void* v, const int64_t* vs,
-                    const uint8_t* mask, const int64_t* ms, int is_causal, double scale,
-                    int64_t b, int64_t h, int64_t i, double* s, double* p, double* out_row,
-                    double* lse_out) {
+                    const uint8_t* mask, const int64_t* ms, const double* bias,
+                    const int64_t* bs, int is_causal, double scale, int64_t b, int64_t h,
+                    int64_t i, double* s, double* p, double* out_row, double* lse_out) {
   const int64_t qrow = b * qs[0] + h * qs[1] + i * qs[2];
   int any = 0;
   double m = -INFINITY;
@@ -103,6 +103,10 @@ static void one_row(int dtype, int64_t Lk, int64_t D, const void* q, const int64
     for (int64_t d = 0; d < D; ++d)
       dot += load_elem(q, dtype, qrow + d * qs[3]) * load_elem(k, dtype, krow + d * ks[3]);
     s[j] = scale * dot;
+    if (bias) { /* additive mask: a value added to the scaled score; -inf hides the key */
+      s[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];
+      if (s[j] == -INFINITY) continue;
+    }
     if (!any || s[j] > m) m = s[j];
     any = 1;
   }
@@ -129,7 +133,8 @@ static void one_row(int dtype, int64_t Lk, int64_t D, const void* q, const int64
 }
 
 /*
- * oracle_sdpa_fwd -- the whole forward, or a chosen subset of its rows.
+ * oracle_sdpa_fwd_bias -- the whole forward, or a chosen subset of its rows, with an optional
+ * additive mask.
  *
  *   dtype        ORACLE_F32 / ORACLE_BF16 or ORACLE_F16 (raw 16-bit patterns) / ORACLE_F64,
  *                shared by q, k, v
@@ -137,6 +142,9 @@ static void one_row(int dtype, int64_t Lk, int64_t D, const void* q, const int64
  *   qs,ks,vs     four element strides each, in (b, h, row, d) order; any value allowed
  *   mask, ms     optional byte mask addressed as mask[b*ms0 + h*ms1 + i*ms2 + j*ms3]
  *                (0 = masked); strides may be 0 to broadcast; NULL = no mask
+ *   bias, bs     optional additive mask, doubles addressed as bias[b*bs0 + h*bs1 + i*bs2 +
+ *                j*bs3] (strides may be 0 to broadcast), added to the scaled score of every
+ *                visible key; -inf hides the key; NULL = none
  *   is_causal    nonzero: also hide keys j > i
  *   scale        multiplies q.k after the dot product
  *   rows, nrows  flat row ids r = (b*H + h)*Lq + i to evaluate; rows == NULL evaluates
@@ -147,14 +155,15 @@ static void one_row(int dtype, int64_t Lk, int64_t D, const void* q, const int64
  *
  * Returns 0 on success, 1 on a bad argument, 2 if scratch memory could not be allocated.
  */
-int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
-                    const void* q, const int64_t* qs, const void* k, const int64_t* ks,
-                    const void* v, const int64_t* vs, const uint8_t* mask, const int64_t* ms,
-                    int is_causal, double scale, const int64_t* rows, int64_t nrows,
-                    double* out, double* lse, int nthreads) {
+int oracle_sdpa_fwd_bias(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                         const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                         const void* v, const int64_t* vs, const uint8_t* mask,
+                         const int64_t* ms, const double* bias, const int64_t* bs,
+                         int is_causal, double scale, const int64_t* rows, int64_t nrows,
+                         double* out, double* lse, int nthreads) {
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return 1;
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || D < 0) return 1;
-  if (!out || !lse || !qs || !ks || !vs || (mask && !ms)) return 1;
+  if (!out || !lse || !qs || !ks || !vs || (mask && !ms) || (bias && !bs)) return 1;
   const int64_t n = rows ? nrows : B * H * Lq;
   if (n < 0) return 1;
   if (rows) {
@@ -182,13 +191,24 @@ int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
       const int64_t flat = rows ? rows[r] : r;
       const int64_t i = flat % Lq;
       const int64_t bh = flat / Lq;
-      one_row(dtype, Lk, D, q, qs, k, ks, v, vs, mask, ms, is_causal, scale, bh / H, bh % H, i,
+      one_row(dtype, Lk, D, q, qs, k, ks, v, vs, mask, ms, bias, bs, is_causal, scale, bh / H,
+              bh % H, i,
               s, p, out + r * D, lse + r);
     }
     free(s);
     free(p);
   }
   return status;
+}
+
+/* oracle_sdpa_fwd -- oracle_sdpa_fwd_bias without an additive mask. */
+int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                    const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                    const void* v, const int64_t* vs, const uint8_t* mask, const int64_t* ms,
+                    int is_causal, double scale, const int64_t* rows, int64_t nrows,
+                    double* out, double* lse, int nthreads) {
+  return oracle_sdpa_fwd_bias(dtype, B, H, Lq, Lk, D, q, qs, k, ks, v, vs, mask, ms, NULL, NULL,
+                              is_causal, scale, rows, nrows, out, lse, nthreads);
 }
 
 /*

@@ -28,6 +28,13 @@ MUTANTS = {
     "f16_exponent_bias": ("ldexp((double)(1024 + frac), ex - 25)", "ldexp((double)(1024 + frac), ex - 24)"),
     "f16_subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     "f16_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+    "bias_subtracted": ("s[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];",
+                        "s[j] -= bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];"),
+    "bias_transposed": ("s[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];",
+                        "s[j] += bias[b * bs[0] + h * bs[1] + j * bs[2] + i * bs[3]];"),
+    "bias_scaled": ("s[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];",
+                    "s[j] += scale * bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];"),
+    "bias_minus_inf_kept": ("      if (s[j] == -INFINITY) continue;\n    }", "    }"),
 }
 
 # backward: (anchor, replacement) in oracle_sdpa_bwd

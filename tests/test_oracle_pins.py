@@ -304,3 +304,62 @@ def test_fp16_inputs_match_their_fp64_values():
     b = sdpa_oracle(q.double(), k.double(), v.double(), is_causal=True)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ---- additive float mask (bias) -------------------------------------------------------
+
+def _bias_case(seed=90, B=2, H=3, Lq=11, Lk=13, D=8):
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = (torch.randn(B, H, n, D, generator=g, dtype=torch.float64) for n in (Lq, Lk, Lk))
+    bias = torch.randn(B, 1, Lq, Lk, generator=g, dtype=torch.float64) * 2
+    return q, k, v, bias
+
+
+def test_bias_zero_is_no_bias_bitwise():
+    q, k, v, bias = _bias_case()
+    a = sdpa_oracle(q, k, v, is_causal=True, bias=torch.zeros_like(bias))
+    b = sdpa_oracle(q, k, v, is_causal=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_bias_of_zero_and_minus_inf_is_the_bool_mask_bitwise():
+    q, k, v, bias = _bias_case()
+    m = bias > 0.5
+    m[0, 0, 4, :] = False  # an empty row
+    minf = torch.where(m, 0.0, float("-inf")).to(torch.float64)
+    a = sdpa_oracle(q, k, v, bias=minf)
+    b = sdpa_oracle(q, k, v, mask=m)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert np.all(a[0][0, :, 4] == 0) and np.all(a[1][0, :, 4] == -np.inf)
+
+
+def test_bias_constant_per_row_shifts_only_the_lse():
+    q, k, v, _ = _bias_case()
+    c = torch.randn(2, 3, 11, 1, generator=torch.Generator().manual_seed(91), dtype=torch.float64)
+    a = sdpa_oracle(q, k, v, bias=c.expand(2, 3, 11, 13))
+    b = sdpa_oracle(q, k, v)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1] + c[..., 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_bias_matches_library_math_backend_with_float_mask():
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    q, k, v, bias = _bias_case(D=16)
+    out, lse = sdpa_oracle(q, k, v, bias=bias, scale=0.37)
+    with sdpa_kernel(SDPBackend.MATH):
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=bias, scale=0.37)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-11, atol=1e-12)
+    s = (q @ k.transpose(-1, -2)) * 0.37 + bias
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_bias_with_causal_and_broadcast_strides():
+    q, k, v, bias = _bias_case(Lq=9, Lk=9)
+    out, lse = sdpa_oracle(q, k, v, bias=bias, is_causal=True)  # bias [B,1,L,L] over 3 heads
+    tri = torch.ones(9, 9, dtype=torch.bool).tril()
+    s = (q @ k.transpose(-1, -2)) / math.sqrt(8) + bias
+    s = s.masked_fill(~tri, float("-inf"))
+    np.testing.assert_allclose(out, (torch.softmax(s, -1) @ v).numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=1e-12, atol=1e-12)
