@@ -428,15 +428,25 @@ def main_decode(args, props):
     print(json.dumps(line), flush=True)
 
 
+def as_dtype(wl, name):
+    """The workload with its q, k, v cast to `name` ("bf16" leaves it as drawn; "f16" casts
+    the bf16 draws, exactly, keeping the strides)."""
+    import torch
+    if name == "f16":
+        wl.q, wl.k, wl.v = (t.to(torch.float16) for t in (wl.q, wl.k, wl.v))
+        wl.name = wl.name.replace("bf16", "f16")
+    return wl
+
+
 def main_bwd(args, props):
     import workloads as W
-    wl = W.config4()
+    wl = as_dtype(W.config4(), args.dtype)
     r = bench_bwd(wl, args.steps, args.warmup)
     ms_per_step = r["wall_s"] / args.steps * 1e3
     value = r["flops"] / (ms_per_step * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
     line = {
-        "metric": BWD_METRIC,
+        "metric": BWD_METRIC if args.dtype == "bf16" else BWD_METRIC.replace("bf16", "fp16"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -446,7 +456,7 @@ def main_bwd(args, props):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "pass": "bwd", "shape_bhld": [1, 32, 8192, 128],
                    "layout": "[B,L,H,D] buffers viewed as [B,H,L,D], gradients alike",
@@ -459,7 +469,8 @@ def main_bwd(args, props):
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(BWD_KERNEL_SOURCE, BWD_TRAFFIC_KERNEL_SHA256,
-                                                 BWD_TRAFFIC_BYTES),
+                                                 BWD_TRAFFIC_BYTES) if args.dtype == "bf16"
+                                else None,
                      "kernels": "bwd_dq_bf16 + bwd_dkdv_bf16",
                      "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
                      "kernel_ms_median": round(r["kernel_ms_median"], 4)},
@@ -478,6 +489,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
+                    help="input type of the fwd and bwd passes (default bf16, the metric's)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "varlen", "decode"),
                     default="fwd",
                     help="fwd (default): the fused forward; bwd: its gradients; varlen: the "
@@ -506,13 +519,13 @@ def main():
         main_decode(args, props)
         return
 
-    wl = W.config4()
+    wl = as_dtype(W.config4(), args.dtype)
     r = bench_workload(wl, args.steps, args.warmup)
     ms_per_step = r["wall_s"] / args.steps * 1e3
     value = r["flops"] / (ms_per_step * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.dtype == "bf16" else METRIC.replace("bf16", "fp16"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -522,7 +535,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "shape_bhld": [1, 32, 8192, 128],
                    "layout": "[B,L,H,D] buffers viewed as [B,H,L,D]", "is_causal": True,
@@ -533,7 +546,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic() if args.dtype == "bf16" else None,
                      "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
                      "kernel_ms_median": round(r["kernel_ms_median"], 4)},
         "cpu_baseline": None,

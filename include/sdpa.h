@@ -128,6 +128,34 @@ int sdpa_check(const void* q, const void* k, const void* v, const void* out, con
 const char* sdpa_strerror(int status);
 
 /*
+ * sdpa_fwd_bias -- sdpa_fwd with an additive float mask instead of the boolean one: the
+ * scores become scale * q_i.k_j + bias[b,h,i,j] before the softmax (a -inf entry hides the
+ * key; a row whose keys are all hidden returns zeros and lse = -inf, as in sdpa_fwd).  The
+ * naive module's masked_fill to -inf is this with entries 0 and -inf; the SDPA call the
+ * pages profile takes a mask and picks its kernel by dtype, head dim, mask and hardware
+ * (the Hungarian edition of "Profiling in PyTorch" part 3, section Scaled Dot Product
+ * Attention (SDPA) és backendes választás).
+ *
+ *   bias          NULL (then this is sdpa_fwd without a mask), or a device pointer to fp32
+ *                 values addressed through the fifth group of strides exactly as sdpa_fwd
+ *                 addresses its mask: innermost (key) stride 1, strides may be 0 to
+ *                 broadcast, 4-byte aligned (16-byte aligned base and row strides let rows
+ *                 be read 16 bytes at a time).  Entries must not be +inf or NaN.
+ *   everything else
+ *                 as in sdpa_fwd (is_causal combines with the bias).
+ */
+int sdpa_fwd_bias(const void* q, const void* k, const void* v, void* out, float* lse, int rank,
+                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                  const int64_t* strides, float scale, int is_causal, const float* bias,
+                  int dtype, void* stream);
+
+/* sdpa_fwd_bias_check -- the host-side validation of sdpa_fwd_bias alone. */
+int sdpa_fwd_bias_check(const void* q, const void* k, const void* v, const void* out,
+                        const float* lse, int rank, int64_t B, int64_t H, int64_t Lq,
+                        int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                        int is_causal, const float* bias, int dtype);
+
+/*
  * sdpa_fwd_splitkv -- sdpa_fwd (no mask) with the keys of every head split into chunks
  * that separate workgroups process in parallel, for problems with few query rows per head
  * and many keys (decoding: one or a few new queries against a long key sequence), where

@@ -23,7 +23,7 @@ STATUS_NAMES = {
     8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE", 10: "SDPA_ERR_CAUSAL", 11: "SDPA_ERR_WORKSPACE",
 }
 
-EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_fwd_splitkv", "sdpa_fwd_splitkv_check",
+EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_fwd_bias", "sdpa_fwd_bias_check", "sdpa_fwd_splitkv", "sdpa_fwd_splitkv_check",
            "sdpa_fwd_splitkv_workspace", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
            "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
 
@@ -73,6 +73,10 @@ def load_library():
     lib.sdpa_fwd_varlen.restype = ctypes.c_int
     lib.sdpa_fwd_varlen_check.argtypes = varlen_common
     lib.sdpa_fwd_varlen_check.restype = ctypes.c_int
+    lib.sdpa_fwd_bias.argtypes = common + [vp]  # the bias takes the mask's place
+    lib.sdpa_fwd_bias.restype = ctypes.c_int
+    lib.sdpa_fwd_bias_check.argtypes = common
+    lib.sdpa_fwd_bias_check.restype = ctypes.c_int
     split_common = [vp] * 5 + [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.POINTER(i64),
                                ctypes.c_float, ctypes.c_int, i64, vp, i64, ctypes.c_int]
     lib.sdpa_fwd_splitkv.argtypes = split_common + [vp]
@@ -250,6 +254,44 @@ def sdpa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, delta=None, *, 
             _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return dq, dk, dv
+
+
+def sdpa_fwd_bias(q, k, v, bias, out=None, lse=None, *, scale=None, is_causal=False,
+                  stream=None, return_lse=True):
+    """SDPA forward with an additive float mask (C ABI `sdpa_fwd_bias`): bias is a float32
+    cuda tensor broadcastable to q.shape[:-1] + (Lk,), added to the scaled scores (-inf
+    hides a key).  Otherwise as sdpa_fwd.  Returns (out, lse)."""
+    _check_shapes(q, k, v, out, lse, bias)
+    if bias.dtype != torch.float32:
+        raise TypeError("bias must be a float32 tensor")
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    B, H, Lq, Lk, D = _sizes(q, k)
+    b = bias.expand(*q.shape[:-1], Lk)
+    strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride(), *b.stride()]
+    arr = (ctypes.c_int64 * len(strides))(*strides)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        status = load_library().sdpa_fwd_bias(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), q.dim(), B, H, Lq, Lk, D, arr,
+            float(scale), causal_mode(is_causal), b.data_ptr(), _DTYPES.get(q.dtype, -1), handle)
+    _raise_on(status)
+    return out, lse
+
+
+def sdpa_fwd_bias_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, rank, B, H, Lq, Lk, D, strides,
+                        scale, is_causal, bias_ptr, dtype) -> int:
+    """The C ABI `sdpa_fwd_bias_check` on raw integers (as sdpa_check, with the bias pointer
+    in the mask's place).  Host-only."""
+    arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
+    return load_library().sdpa_fwd_bias_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, rank, B, H,
+                                              Lq, Lk, D, arr, float(scale), int(is_causal),
+                                              bias_ptr, int(dtype))
 
 
 def sdpa_fwd_splitkv_workspace(B, H, Lq, Lk, D, num_splits=0, dtype=SDPA_BF16) -> int:

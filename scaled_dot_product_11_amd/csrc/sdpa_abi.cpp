@@ -109,6 +109,7 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
     p->out = const_cast<void*>(out);
     p->lse = const_cast<float*>(lse);
     p->mask = mask;
+    p->bias = nullptr;
     p->B = B;
     p->H = H;
     p->Lq = Lq;
@@ -276,6 +277,7 @@ int normalise_varlen(const void* q, const void* k, const void* v, const void* ou
     p->out = const_cast<void*>(out);
     p->lse = const_cast<float*>(lse);
     p->mask = nullptr;
+    p->bias = nullptr;
     p->cu_q = cu_q;
     p->cu_k = cu_k;
     p->B = 1;
@@ -345,6 +347,24 @@ int normalise_splitkv(const void* q, const void* k, const void* v, const void* o
   return SDPA_OK;
 }
 
+// Additive mask: the dense forward's validation with the bias in the mask's place (its
+// strides follow the mask's rules: innermost 1, none negative, 0 to broadcast); fp32,
+// 4-byte aligned.
+int normalise_bias(const void* q, const void* k, const void* v, const void* out,
+                   const float* lse, int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                   int64_t D, const int64_t* strides, float scale, int is_causal,
+                   const float* bias, int dtype, sdpa::Problem* p) {
+  const int st = normalise(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal,
+                           reinterpret_cast<const uint8_t*>(bias), dtype, p);
+  if (st != SDPA_OK) return st;
+  if (bias && !aligned(bias, 4)) return SDPA_ERR_ALIGN;
+  if (p) {
+    p->mask = nullptr;
+    p->bias = bias;
+  }
+  return SDPA_OK;
+}
+
 // The code object holds gfx950 machine code only; refuse other devices up front.
 // Cached per device id (the only global state of the library).
 bool device_is_gfx950(hipStream_t stream) {
@@ -385,6 +405,28 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   sdpa::Problem p;
   const int st = normalise(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal,
                            mask, dtype, &p);
+  if (st != SDPA_OK) return st;
+  if (p.B * p.H * p.Lq == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
+int sdpa_fwd_bias_check(const void* q, const void* k, const void* v, const void* out,
+                        const float* lse, int rank, int64_t B, int64_t H, int64_t Lq,
+                        int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                        int is_causal, const float* bias, int dtype) {
+  return normalise_bias(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal,
+                        bias, dtype, nullptr);
+}
+
+int sdpa_fwd_bias(const void* q, const void* k, const void* v, void* out, float* lse, int rank,
+                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                  const int64_t* strides, float scale, int is_causal, const float* bias,
+                  int dtype, void* stream) {
+  sdpa::Problem p;
+  const int st = normalise_bias(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale,
+                                is_causal, bias, dtype, &p);
   if (st != SDPA_OK) return st;
   if (p.B * p.H * p.Lq == 0) return SDPA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);

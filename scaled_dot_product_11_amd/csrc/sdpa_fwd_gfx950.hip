@@ -50,12 +50,14 @@ struct Args {
   void* out;
   float* lse;
   const uint8_t* mask;
+  const float* bias;    // additive mask (fp32), addressed with the mask strides
   const int32_t* cu_q;  // variable-length only: sequence s owns query tokens cu_q[s] ..
   const int32_t* cu_k;  // cu_q[s+1]-1 and key tokens cu_k[s] .. cu_k[s+1]-1
   int64_t sq[3], sk[3], sv[3], so[3], sm[3];
   int32_t H, Lq, Lk, q_tiles, bh_count;
   float scale_log2;  // scale * log2(e): scores are kept in base-2 units
   int32_t mask_vec8; // mask rows may be read 8 bytes at a time
+  int32_t bias_vec4; // bias rows may be read 16 bytes at a time
   int32_t bottom_right;  // causal alignment: key j visible iff j <= i + (Lk - Lq)
   float* ws_o;           // split keys only: normalised partial outputs [split][bh][Lq][D]
   float* ws_lse;         // and their lse [split][bh][Lq] (fp32, natural log)
@@ -226,9 +228,13 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-template <typename E, int D, bool CAUSAL, bool MASK, bool POS, int MODE>
+// MK: 0 no mask, 1 boolean mask, 2 additive mask (POS is then false: the scale is applied
+// to the scores before the bias is added).
+template <typename E, int D, bool CAUSAL, int MK, bool POS, int MODE>
 __global__ __launch_bounds__(kThreadsBf16) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma(Args a) {
+  constexpr bool MASK = MK == 1, BIAS = MK == 2;
+  static_assert(!(BIAS && POS), "an additive mask needs the scores scaled first");
   typedef typename Vec16<E>::v8 v8;
   typedef typename Vec16<E>::v2 v2;
   constexpr int BN = kBlockNBf16;
@@ -236,7 +242,7 @@ void fwd_mfma(Args a) {
   constexpr int DG = D / 8;                // 16-byte chunks per row
   constexpr int CH = BN * DG / NT;         // chunks per thread per K (or V) tile
   constexpr int ROWS = NT / DG;            // tile rows covered by one chunk pass
-  constexpr int KPRE = MASK ? 2 : 4;     // K fragments read ahead of each matrix phase
+  constexpr int KPRE = MK ? 2 : 4;       // K fragments read ahead of each matrix phase
   constexpr int KP = k_pitch_bf16(D);      // K row pitch in LDS (bytes)
   constexpr int VP = v_pitch_bf16(D);      // V row pitch in LDS (bytes)
   constexpr int KT = BN * KP;              // bytes of one K stage
@@ -265,6 +271,7 @@ void fwd_mfma(Args a) {
   const char* vb = static_cast<const char*>(a.v) + 2 * it.v;
   uint16_t* ob = static_cast<uint16_t*>(a.out) + it.o;
   const uint8_t* mb = MASK ? a.mask + it.m : nullptr;
+  const float* bb = BIAS ? a.bias + it.m : nullptr;
 
   const int qw = q0 + 32 * slice;  // first query row of this wave
   const int qi = qw + li;          // this lane's query row
@@ -440,6 +447,31 @@ void fwd_mfma(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][r] *= a.scale_log2;
     }
+    if (BIAS && q_ok) {
+      // additive mask of this lane's keys (runs of 8 at k0 + 32kt + 16g + 8hf), in base-2
+      // units; keys past Lk are hidden below
+      const float* brow = bb + int64_t(qi) * a.sm[2];
+#pragma unroll
+      for (int run = 0; run < 4; ++run) {
+        const int key0 = k0 + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
+        float bv[8];
+        if (a.bias_vec4 && key0 + 8 <= Lk) {
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(brow + key0);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(brow + key0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bv[e] = lo[e];
+            bv[e + 4] = hi[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bv[e] = key0 + e < Lk ? brow[key0 + e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          s[run >> 1][8 * (run & 1) + e] = __builtin_fmaf(bv[e], kLog2e, s[run >> 1][8 * (run & 1) + e]);
+      }
+    }
     const bool edge = (CAUSAL && k0 + BN - 1 > qw + coff) || (k0 + BN > Lk);
     if (edge || MASK) {
       // Mask bytes of this lane's keys: runs of 8 at k0 + 32kt + 16g + 8hf.
@@ -586,8 +618,9 @@ void fwd_mfma(Args a) {
 // fp32 kernel: fp32 MFMA 32x32x2 (true fp32 products, fp32 accumulation) for both
 // products; same decomposition as the 16-bit kernel, probabilities stay fp32.
 // ---------------------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool MASK, int MODE>
+template <int D, bool CAUSAL, int MK, int MODE>
 __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
+  constexpr bool MASK = MK == 1, BIAS = MK == 2;
   constexpr int DG = D / 4;                             // 16-byte groups per row
   constexpr int CH = kBlockNF32 * DG / kThreadsF32;           // chunks per thread per tile
   constexpr int KROW = D + 1;                           // odd pitch: conflict-free column reads
@@ -615,6 +648,7 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   const float* vb = static_cast<const float*>(a.v) + it.v;
   float* ob = static_cast<float*>(a.out) + it.o;
   const uint8_t* mb = MASK ? a.mask + it.m : nullptr;
+  const float* bb = BIAS ? a.bias + it.m : nullptr;
 
   const int qw = q0 + wave * 32;
   const int qi = qw + li;
@@ -702,8 +736,10 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float xv = s[kt][r] * a.scale_log2;
+          const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (BIAS && q_ok && key < Lk)  // additive mask, in base-2 units
+            xv = __builtin_fmaf(bb[int64_t(qi) * a.sm[2] + key], kLog2e, xv);
           if (edge || MASK) {
-            const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * hf + (r & 3);
             bool hide = key >= Lk;
             if (CAUSAL) hide = hide || key > qi + coff;
             if (MASK && !hide && q_ok) hide = mb[int64_t(qi) * a.sm[2] + key] == 0;
@@ -833,19 +869,20 @@ __global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int
     a.lse[row] = wsum > 0.f ? m + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
 
-template <int D, bool CAUSAL, bool MASK, int MODE>
+template <int D, bool CAUSAL, int MK, int MODE>
 hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Args*>(&a)};
   const void* fn;
-  const bool pos = a.scale_log2 > 0.f;
+  constexpr bool POS_OK = MK != 2;  // an additive mask takes the explicitly scaled path
+  const bool pos = POS_OK && a.scale_log2 > 0.f;
   if (dtype == 1)
-    fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MASK, true, MODE>)
-             : reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MASK, false, MODE>);
+    fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, POS_OK, MODE>)
+             : reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, false, MODE>);
   else if (dtype == 2)
-    fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MASK, true, MODE>)
-             : reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MASK, false, MODE>);
+    fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MK, POS_OK, MODE>)
+             : reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MK, false, MODE>);
   else
-    fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MASK, MODE>);
+    fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MK, MODE>);
   return hipLaunchKernel(fn, dim3(grid), dim3(block_threads(dtype)), args, 0, stream);
 }
 
@@ -853,14 +890,16 @@ template <int D>
 hipError_t launch_d(const Args& a, int dtype, bool causal, int mode, unsigned grid,
                     hipStream_t s) {
   if (mode == kVarlen)  // packed sequences take no mask
-    return causal ? launch<D, true, false, kVarlen>(a, dtype, grid, s)
-                  : launch<D, false, false, kVarlen>(a, dtype, grid, s);
+    return causal ? launch<D, true, 0, kVarlen>(a, dtype, grid, s)
+                  : launch<D, false, 0, kVarlen>(a, dtype, grid, s);
   if (mode == kSplit)  // neither do split keys
-    return causal ? launch<D, true, false, kSplit>(a, dtype, grid, s)
-                  : launch<D, false, false, kSplit>(a, dtype, grid, s);
-  const bool m = a.mask != nullptr;
-  if (causal) return m ? launch<D, true, true, kDense>(a, dtype, grid, s) : launch<D, true, false, kDense>(a, dtype, grid, s);
-  return m ? launch<D, false, true, kDense>(a, dtype, grid, s) : launch<D, false, false, kDense>(a, dtype, grid, s);
+    return causal ? launch<D, true, 0, kSplit>(a, dtype, grid, s)
+                  : launch<D, false, 0, kSplit>(a, dtype, grid, s);
+  if (a.mask)
+    return causal ? launch<D, true, 1, kDense>(a, dtype, grid, s) : launch<D, false, 1, kDense>(a, dtype, grid, s);
+  if (a.bias)
+    return causal ? launch<D, true, 2, kDense>(a, dtype, grid, s) : launch<D, false, 2, kDense>(a, dtype, grid, s);
+  return causal ? launch<D, true, 0, kDense>(a, dtype, grid, s) : launch<D, false, 0, kDense>(a, dtype, grid, s);
 }
 
 template <int D>
@@ -885,6 +924,7 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.out = p.out;
   a.lse = p.lse;
   a.mask = p.mask;
+  a.bias = p.bias;
   a.cu_q = p.cu_q;
   a.cu_k = p.cu_k;
   for (int i = 0; i < 3; ++i) {
@@ -904,6 +944,8 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.scale_log2 = p.scale * kLog2e;
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
                 p.sm[1] % 8 == 0 && p.sm[2] % 8 == 0;
+  a.bias_vec4 = p.bias && (reinterpret_cast<uintptr_t>(p.bias) % 16 == 0) && p.sm[0] % 4 == 0 &&
+                p.sm[1] % 4 == 0 && p.sm[2] % 4 == 0;
   a.bottom_right = p.causal == 2;
   a.ws_o = p.ws_o;
   a.ws_lse = p.ws_lse;

@@ -34,6 +34,7 @@ struct Problem {
   void* out;
   float* lse;
   const uint8_t* mask;
+  const float* bias;  // additive mask (fp32) through the mask strides sm; never with mask
   const int32_t* cu_q;
   const int32_t* cu_k;
   int64_t B, H, Lq, Lk, D;

@@ -431,3 +431,18 @@ def test_splitkv_check():
     a["strides"][7] = 2  # k innermost stride
     assert c(**a) == STRIDE
     assert "workspace" in sd.sdpa_strerror(WORKSPACE_ERR)
+
+
+def test_bias_check():
+    c = sd.sdpa_fwd_bias_check
+    a = args4(mask=True)
+    a["bias_ptr"] = a.pop("mask_ptr")
+    assert c(**a) == OK
+    assert c(**dict(a, bias_ptr=None)) == OK            # no bias: plain sdpa_fwd
+    assert c(**dict(a, bias_ptr=A + 0x40002)) == ALIGN  # fp32 bias: 4-byte aligned
+    assert c(**dict(a, bias_ptr=A + 0x40004)) == OK
+    s = list(a["strides"])
+    s[19] = 2  # the bias's key stride
+    assert c(**dict(a, strides=s)) == STRIDE
+    assert c(**dict(a, dtype=sd.SDPA_F16)) == OK
+    assert c(**dict(a, is_causal=2)) == OK
