@@ -23,6 +23,10 @@ each, against a 32768-key cache laid out [B,L,H,D], D=128, bf16, bottom-right ca
 query sees every key).  It is bound by HBM: `value` is algorithmic bytes (q, k, v, out,
 lse, each once) per second, against 8000 GB/s.
 
+`--pass bias` measures sdpa_fwd_bias: q/k/v bf16 [2,8,4096,64], causal, an ALiBi-style
+fp32 bias [1,8,4096,4096] (per-head slope times the query-key distance) broadcast over the
+batch; 4*D flops per visible pair.
+
 `--pass bwd` measures the gradients instead: one step = one sdpa_bwd call (its dq and dk/dv
 kernels) on the same workload, with the forward's out and lse and an upstream gradient
 (N(0,1), same [B,L,H,D] layout) resident before the timed region, gradients written in the
@@ -49,6 +53,8 @@ METRIC = "causal SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=12
 BWD_METRIC = "causal SDPA bwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), L=8192 D=128"
 DECODE_METRIC = ("decode SDPA (split keys) GB/s on 1 MI355X (% of HBM peak), B=8 H=32 Lq=1 "
                  "Lk=32768 D=128")
+BIAS_METRIC = ("causal SDPA fwd with an additive mask TFLOP/s on 1 MI355X (% of bf16 MFMA peak), "
+               "B=2 H=8 L=4096 D=64")
 VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf16 MFMA peak), "
                  "32768 tokens H=32 D=128")
 # HBM bytes per launch of the fused kernel on the default workload: FETCH_SIZE and
@@ -363,6 +369,71 @@ def cpu_baseline_decode():
                       f"{cpu_model()}"}
 
 
+def main_bias(args, props):
+    import torch
+    import workloads as W
+    from scaled_dot_product_11_amd import sdpa_fwd_bias
+    g = torch.Generator().manual_seed(960)
+    q, k, v = (t.to("cuda") for t in W.draw_qkv(g, (2, 8, 4096, 64)))
+    i = torch.arange(4096, device="cuda")
+    slopes = 0.5 * 2.0 ** -torch.arange(8, dtype=torch.float32, device="cuda")
+    bias = (-slopes[:, None, None] * (i[:, None] - i[None, :]).abs()).unsqueeze(0)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+
+    def fn():
+        sdpa_fwd_bias(q, k, v, bias, out, lse, is_causal=True)
+    wall, per = time_kernel(fn, args.steps, args.warmup)
+    flops = 4 * 64 * 2 * 8 * visible_pairs(4096, 4096, True)
+    ms_per_step = wall / args.steps * 1e3
+    mean = statistics.fmean(per)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (mean * 1e-3) / 1e12
+    line = {
+        "metric": BIAS_METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bias_alibi_bf16_causal_b2_h8_l4096_d64", "pass": "bias",
+                   "bias": "fp32 [1,8,4096,4096], slope 0.5*2^-h times |i - j|",
+                   "flops_per_step": flops, "flop_convention": "4*D per visible (i,j) pair",
+                   "bias_bytes_read_per_step": 2 * 8 * visible_pairs(4096, 4096, True) * 4,
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "device": props.name, "cus": props.multi_processor_count},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_ms_mean": round(mean, 4),
+                     "kernel_ms_median": round(statistics.median(per), 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bias(q.cpu(), k.cpu(), v.cpu(), bias.cpu())
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_bias(q, k, v, bias, target_s=10.0):
+    """The fp64 oracle (bias path) on a bounded sample of query rows of the same workload."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    B, H, L, D = q.shape
+
+    def run(n):
+        rows = np.sort(rng.choice(B * H * L, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.sdpa_oracle(q, k, v, is_causal=True, bias=bias, rows=rows)
+        return time.perf_counter() - t0, int(4 * D * ((rows % L) + 1).sum()), n
+
+    dt, fl, n = run(256)
+    n = int(min(B * H * L, max(256, 256 * target_s / max(dt, 1e-3))))
+    dt, fl, n = run(n)
+    threads = oracle.default_threads()
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows of the same workload, fp64 oracle with the bias, "
+                      f"{dt:.2f} s, {threads} OpenMP threads, host cpu: {cpu_model()}"}
+
+
 def main_decode(args, props):
     import torch
     from scaled_dot_product_11_amd import sdpa_fwd, sdpa_fwd_splitkv, sdpa_fwd_splitkv_workspace
@@ -491,7 +562,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
                     help="input type of the fwd and bwd passes (default bf16, the metric's)")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "varlen", "decode"),
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "varlen", "decode", "bias"),
                     default="fwd",
                     help="fwd (default): the fused forward; bwd: its gradients; varlen: the "
                          "forward over packed documents; decode: split keys, one query per head")
@@ -517,6 +588,9 @@ def main():
         return
     if args.which == "decode":
         main_decode(args, props)
+        return
+    if args.which == "bias":
+        main_bias(args, props)
         return
 
     wl = as_dtype(W.config4(), args.dtype)
