@@ -61,12 +61,12 @@ VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf1
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
 # kernel source they were taken on (sha256 prefix below); reported as null otherwise.
-TRAFFIC_BYTES = 500121 * 1024
-TRAFFIC_KERNEL_SHA256 = "6634a2952f17f447"
+TRAFFIC_BYTES = 502484 * 1024
+TRAFFIC_KERNEL_SHA256 = "61c5999379ff88de"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 # The same for one backward call (dq and dk/dv kernels together).
-BWD_TRAFFIC_BYTES = 1647942 * 1024
-BWD_TRAFFIC_KERNEL_SHA256 = "a1ad613950f96445"
+BWD_TRAFFIC_BYTES = 1639553 * 1024
+BWD_TRAFFIC_KERNEL_SHA256 = "e3baeb8fff0ccf82"
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_bwd_gfx950.hip")
 
 
