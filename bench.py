@@ -61,8 +61,8 @@ VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf1
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
 # kernel source they were taken on (sha256 prefix below); reported as null otherwise.
-TRAFFIC_BYTES = 502484 * 1024
-TRAFFIC_KERNEL_SHA256 = "61c5999379ff88de"
+TRAFFIC_BYTES = 501880 * 1024
+TRAFFIC_KERNEL_SHA256 = "45ace130af550e4d"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 # The same for one backward call (dq and dk/dv kernels together).
 BWD_TRAFFIC_BYTES = 1639553 * 1024
@@ -566,6 +566,9 @@ def main():
                     default="fwd",
                     help="fwd (default): the fused forward; bwd: its gradients; varlen: the "
                          "forward over packed documents; decode: split keys, one query per head")
+    ap.add_argument("--head-dim", type=int, default=128, choices=(32, 64, 96, 128, 256),
+                    help="fwd pass: head dim of the [1,32,8192,D] causal workload (default 128, "
+                         "the metric's)")
     ap.add_argument("--report", default=None, help="write per-workload timings here")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one elementwise kernel reading and writing this many MiB "
@@ -593,13 +596,15 @@ def main():
         main_bias(args, props)
         return
 
-    wl = as_dtype(W.config4(), args.dtype)
+    D = args.head_dim
+    wl = as_dtype(W.config4(D=D), args.dtype)
     r = bench_workload(wl, args.steps, args.warmup)
     ms_per_step = r["wall_s"] / args.steps * 1e3
     value = r["flops"] / (ms_per_step * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms_mean"] * 1e-3) / 1e12
     line = {
-        "metric": METRIC if args.dtype == "bf16" else METRIC.replace("bf16", "fp16"),
+        "metric": (METRIC if args.dtype == "bf16" else METRIC.replace("bf16", "fp16")).replace(
+            "D=128", f"D={D}"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -611,7 +616,7 @@ def main():
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "shape_bhld": [1, 32, 8192, 128],
+        "config": {"workload": wl.name, "shape_bhld": [1, 32, 8192, D],
                    "layout": "[B,L,H,D] buffers viewed as [B,H,L,D]", "is_causal": True,
                    "scale": wl.scale, "flops_per_step": r["flops"],
                    "flop_convention": "4*D per visible (i,j) pair, causal-adjusted",
@@ -620,7 +625,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic() if args.dtype == "bf16" else None,
+                     "traffic": measured_traffic() if args.dtype == "bf16" and D == 128
+                     else None,
                      "kernel_ms_mean": round(r["kernel_ms_mean"], 4),
                      "kernel_ms_median": round(r["kernel_ms_median"], 4)},
         "cpu_baseline": None,

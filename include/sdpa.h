@@ -54,7 +54,8 @@ enum sdpa_status {
   SDPA_ERR_NULL = 1,     /* a required pointer is NULL (strides, or q/k/v/out when read) */
   SDPA_ERR_RANK = 2,     /* rank not 3 or 4, or rank 3 with B != 1                       */
   SDPA_ERR_SHAPE = 3,    /* negative size, or a size/extent beyond the supported maximum */
-  SDPA_ERR_HEAD_DIM = 4, /* D not in {64, 128}                                           */
+  SDPA_ERR_HEAD_DIM = 4, /* D not a supported head dim (forward: 32, 64, 96, 128, 256;
+                            backward: 64, 128)                                         */
   SDPA_ERR_DTYPE = 5,    /* dtype not an sdpa_dtype                                      */
   SDPA_ERR_STRIDE = 6,   /* innermost stride != 1, or a negative stride                  */
   SDPA_ERR_ALIGN = 7,    /* q/k/v/out base or row stride not 16-byte aligned, lse not 4  */
@@ -86,9 +87,12 @@ enum sdpa_causal {
  *                 [N,Lq]), 4-byte aligned, receiving the natural-log LSE (-inf for
  *                 rows with no visible key).
  *   rank          3 or 4.  Rank 3 requires B == 1 and H == N.
- *   B,H,Lq,Lk,D   sizes; D in {64, 128}; Lq, Lk and B*H below 2^31; (Lk + 64) times the
- *                 row stride of k (and of v) must stay below 2 GiB (one head's rows are
- *                 addressed with 32-bit offsets).  B*H*Lq == 0 is a no-op returning
+ *   B,H,Lq,Lk,D   sizes; D in {32, 64, 96, 128, 256} (the head dims an SDPA dispatcher
+ *                 routes by, "profiling attention in pytorch" (news.bpdata), section
+ *                 Scaled Dot Product Attention (SDPA) es backendes valasztas; every dtype,
+ *                 mask kind and causal mode takes every one of them); Lq, Lk and B*H
+ *                 below 2^31; (Lk + 64) times the row stride of k (and of v) must stay
+ *                 below 2 GiB (one head's rows are addressed with 32-bit offsets).  B*H*Lq == 0 is a no-op returning
  *                 SDPA_OK; Lk == 0 makes every row empty.
  *   strides       5*rank element strides, tensor-major: q, k, v, out, mask, each in its
  *                 own axis order ([N,L,D] / [B,H,L,D]; the mask is [N,Lq,Lk] /
@@ -222,8 +226,8 @@ int64_t sdpa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
  *   max_seqlen_q  an upper bound of every cu_seqlens_q[s+1] - cu_seqlens_q[s], at most
  *                 total_q (it sizes the launch; query rows past it are not written).
  *   total_q, total_k, H, D
- *                 sizes; D in {64, 128}; (total_k + 64) times the token stride of k (and of
- *                 v) must stay below 2 GiB.
+ *                 sizes; D in {32, 64, 96, 128, 256}; (total_k + 64) times the token
+ *                 stride of k (and of v) must stay below 2 GiB.
  *   strides       12 element strides: (token, head, dim) for q, k, v, out.
  *   scale, causal, dtype, stream
  *                 as in sdpa_fwd (causal: an sdpa_causal mode).

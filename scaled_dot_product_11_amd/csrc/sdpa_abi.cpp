@@ -36,7 +36,7 @@ int canon_strides(int rank, const int64_t* s, int64_t out[4]) {
   return SDPA_OK;
 }
 
-// Shared checks of the sizes, head dim and scale.
+// The backward's checks of the sizes, head dim (its kernels take 64 and 128) and scale.
 int check_sizes(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, float scale) {
   if (rank != 3 && rank != 4) return SDPA_ERR_RANK;
   if (rank == 3 && B != 1) return SDPA_ERR_RANK;
@@ -58,14 +58,14 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return SDPA_ERR_SHAPE;
   if (Lq > kMaxDim || Lk > kMaxDim || B > kMaxDim || H > kMaxDim) return SDPA_ERR_SHAPE;
   if (B != 0 && H > kMaxDim / B) return SDPA_ERR_SHAPE;
-  if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
+  if (!sdpa::fwd_head_dim_ok(D)) return SDPA_ERR_HEAD_DIM;
   if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
   if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
 
   const int64_t bh = B * H;
-  const int64_t bm = sdpa::block_m(dtype);
+  const int64_t bm = sdpa::block_m(dtype, int(D));
   const int64_t q_tiles = (Lq + bm - 1) / bm;
   if (bh != 0 && q_tiles > kMaxDim / bh) return SDPA_ERR_SHAPE;  // grid size
   const bool any_rows = bh * Lq != 0;
@@ -232,13 +232,14 @@ int normalise_varlen(const void* q, const void* k, const void* v, const void* ou
   if (nseq >= kMaxDim || H > kMaxDim || total_q > kMaxDim || total_k > kMaxDim)
     return SDPA_ERR_SHAPE;
   if (max_seqlen_q > total_q) return SDPA_ERR_SHAPE;
-  if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
+  if (!sdpa::fwd_head_dim_ok(D)) return SDPA_ERR_HEAD_DIM;
   if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
   if (causal < SDPA_CAUSAL_NONE || causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t heads = nseq * H;
-  const int64_t q_tiles = (max_seqlen_q + sdpa::block_m(dtype) - 1) / sdpa::block_m(dtype);
+  const int64_t bm = sdpa::block_m(dtype, int(D));
+  const int64_t q_tiles = (max_seqlen_q + bm - 1) / bm;
   if (heads != 0 && q_tiles > kMaxDim / heads) return SDPA_ERR_SHAPE;  // grid size
   const bool any_rows = heads != 0 && total_q != 0 && max_seqlen_q != 0;
 
@@ -311,7 +312,8 @@ int splitkv_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, int64
                   int dtype, int64_t* nsplit, int64_t* split_len, int64_t* need) {
   if (num_splits < 0 || num_splits > kMaxSplits) return SDPA_ERR_SHAPE;
   const int64_t bh = B * H;
-  const int64_t q_tiles = (Lq + sdpa::block_m(dtype) - 1) / sdpa::block_m(dtype);
+  const int64_t bm = sdpa::block_m(dtype, int(D));
+  const int64_t q_tiles = (Lq + bm - 1) / bm;
   sdpa::splitkv_plan(bh, q_tiles, Lk, num_splits, nsplit, split_len);
   if (bh != 0 && q_tiles > kMaxDim / bh / *nsplit) return SDPA_ERR_SHAPE;  // grid size
   *need = *nsplit * bh * Lq * (D + 1) * 4;
@@ -439,7 +441,7 @@ int64_t sdpa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || B > kMaxDim || H > kMaxDim || Lq > kMaxDim ||
       Lk > kMaxDim || (B != 0 && H > kMaxDim / B))
     return -SDPA_ERR_SHAPE;
-  if (D != 64 && D != 128) return -SDPA_ERR_HEAD_DIM;
+  if (!sdpa::fwd_head_dim_ok(D)) return -SDPA_ERR_HEAD_DIM;
   if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return -SDPA_ERR_DTYPE;
   int64_t nsplit, split_len, need;
   const int st = splitkv_sizes(B, H, Lq, Lk, D, num_splits, dtype, &nsplit, &split_len, &need);
@@ -524,7 +526,8 @@ const char* sdpa_strerror(int status) {
     case SDPA_ERR_SHAPE:
       return "negative size, a size beyond the supported maximum, or one head's k/v rows "
              "spanning 2 GiB or more";
-    case SDPA_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
+    case SDPA_ERR_HEAD_DIM:
+      return "head dim D must be 32, 64, 96, 128 or 256 (the backward: 64 or 128)";
     case SDPA_ERR_DTYPE:
       return "dtype must be SDPA_F32, SDPA_BF16 or SDPA_F16 (the backward: SDPA_BF16 or SDPA_F16)";
     case SDPA_ERR_STRIDE: return "innermost strides must be 1 and no stride may be negative";
@@ -551,9 +554,9 @@ int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
   const int st = normalise(dummy, dummy, dummy, dummy, nullptr, rank, B, H, Lq, Lk, D, strides,
                            1.0f, is_causal, nullptr, dtype, nullptr);
   if (st != SDPA_OK) return st;
-  plan->block_m = sdpa::block_m(dtype);
+  plan->block_m = sdpa::block_m(dtype, int(D));
   plan->block_n = sdpa::block_n(dtype);
-  plan->threads = sdpa::block_threads(dtype);
+  plan->threads = sdpa::block_threads(dtype, int(D));
   plan->q_tiles = (Lq + plan->block_m - 1) / plan->block_m;
   plan->bh = B * H;
   plan->items = plan->bh * plan->q_tiles;

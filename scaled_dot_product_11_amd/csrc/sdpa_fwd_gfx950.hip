@@ -231,31 +231,35 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
 // MK: 0 no mask, 1 boolean mask, 2 additive mask (POS is then false: the scale is applied
 // to the scores before the bias is added).
 template <typename E, int D, bool CAUSAL, int MK, bool POS, int MODE>
-__global__ __launch_bounds__(kThreadsBf16) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256 * groups_16(D))
+__attribute__((amdgpu_waves_per_eu(groups_16(D), groups_16(D))))
 void fwd_mfma(Args a) {
   constexpr bool MASK = MK == 1, BIAS = MK == 2;
   static_assert(!(BIAS && POS), "an additive mask needs the scores scaled first");
   typedef typename Vec16<E>::v8 v8;
   typedef typename Vec16<E>::v2 v2;
+  constexpr int G = groups_16(D);          // phase groups (waves per SIMD)
   constexpr int BN = kBlockNBf16;
-  constexpr int NT = kThreadsBf16;
+  constexpr int BM = block_m(1, D);        // query rows per workgroup
+  constexpr int NT = block_threads(1, D);
   constexpr int DG = D / 8;                // 16-byte chunks per row
-  constexpr int CH = BN * DG / NT;         // chunks per thread per K (or V) tile
-  constexpr int ROWS = NT / DG;            // tile rows covered by one chunk pass
-  constexpr int KPRE = MK ? 2 : 4;       // K fragments read ahead of each matrix phase
+  constexpr int CH = (BN * DG + NT - 1) / NT;  // chunks per thread per K (or V) tile
+  constexpr bool CH_FULL = CH * NT == BN * DG;  // every thread stages CH chunks
+  constexpr int NKF = 2 * (D / 16);        // K operand fragments of one tile's S
+  constexpr int KPRE = (MK ? 2 : 4) < NKF ? (MK ? 2 : 4) : NKF;  // read ahead of M(t)
   constexpr int KP = k_pitch_bf16(D);      // K row pitch in LDS (bytes)
   constexpr int VP = v_pitch_bf16(D);      // V row pitch in LDS (bytes)
   constexpr int KT = BN * KP;              // bytes of one K stage
   constexpr int VT = BN * VP;              // bytes of one V stage
-  static_assert(CH * NT == BN * DG, "tile must split evenly over the workgroup");
+  static_assert(D % 32 == 0 && BM == 32 * 4 * G && NT == 64 * 4 * G, "tile shape");
   static_assert(2 * KT + 2 * VT == lds_bytes_bf16(D), "plan and kernel disagree on LDS");
   __shared__ __attribute__((aligned(16))) char lds[2 * KT + 2 * VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;        // 0..7; SIMD = wave % 4
-  const int grp = wave >> 2;        // phase group
-  const int slice = 2 * (wave & 3) + grp;  // 32-row slice of the workgroup's rows
+  const int wave = tid >> 6;        // 0..4G-1; SIMD = wave % 4
+  const int grp = G == 2 ? wave >> 2 : 0;  // phase group
+  const int slice = G == 2 ? 2 * (wave & 3) + grp : wave;  // 32-row slice of the rows
   const int li = lane & 31;
   const int hf = lane >> 5;
 
@@ -264,7 +268,7 @@ void fwd_mfma(Args a) {
   decode_split(a, CAUSAL, MODE, &bh, &qt, &split);
   const Item it = item_of<MODE>(a, bh, split);
   const int Lq = it.Lq, Lk = it.Lk, coff = it.coff;
-  const int q0 = int(qt) * kBlockMBf16;
+  const int q0 = int(qt) * BM;
   if (MODE == kVarlen && q0 >= Lq) return;  // a tile past this sequence's rows (whole workgroup)
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + it.q;
   const char* kb = static_cast<const char*>(a.k) + 2 * it.k;
@@ -294,7 +298,7 @@ void fwd_mfma(Args a) {
   // Key tiles the workgroup stages (keys that can be visible to some stored row), and
   // the tiles this wave computes on (with a causal mask: tiles 0 .. (qw + 31 + coff) / 64).
   int kend = Lk;
-  if (CAUSAL) kend = max(0, min(kend, min(q0 + kBlockMBf16, Lq) + coff));
+  if (CAUSAL) kend = max(0, min(kend, min(q0 + BM, Lq) + coff));
   const int ntiles = (kend + BN - 1) / BN;
   const int wlast = qw + 31 + coff;  // last key any row of the wave may see (causal)
   const int wtiles = !wave_live ? 0 : CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
@@ -314,33 +318,62 @@ void fwd_mfma(Args a) {
   const int v_ext = Lk > 0 ? (Lk - 1) * v_rowb + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, k_ext, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, v_ext, kBufferFlags);
+  // Chunk p of this thread is chunk tid + p * NT of the tile (row-major, DG per row).  When
+  // the tile splits evenly (D = 64, 128, 256) chunk p sits ROWS rows below chunk 0;
+  // otherwise (D = 32, 96) each chunk's row and column are computed, and chunks past the
+  // tile's end are neither loaded nor stored -- a whole-wave condition, since BN * DG is a
+  // multiple of 64 there.
+  constexpr bool EVEN = CH_FULL && NT % DG == 0;
+  constexpr int ROWS = EVEN ? NT / DG : 0;   // tile rows covered by one chunk pass
+  auto chunk_ok = [&](int p) { return EVEN || tid + p * NT < BN * DG; };
   const int ld_row = tid / DG, ld_col = tid % DG;  // this thread's first chunk
   const int k_goff = ld_row * k_rowb + ld_col * 16;
   const int v_goff = ld_row * v_rowb + ld_col * 16;
   const int k_soff = ((ld_row & ~31) | perm5(ld_row & 31)) * KP + ld_col * 16;
   const int v_soff = ld_row * VP + ld_col * 16;
+  // byte offsets of chunk p within a tile: global (row stride rowb; chunk 0's offset is in
+  // the tile base when the tile splits evenly) and LDS (K or V layout)
+  auto g_off = [&](int p, int rowb) {
+    if (EVEN) return p * ROWS * rowb;
+    const int c = tid + p * NT;
+    return (c / DG) * rowb + (c % DG) * 16;
+  };
+  auto k_sto = [&](int p) {
+    // perm5 acts within 32-row sub-tiles: a chunk pass of a multiple of 32 rows leaves it
+    // unchanged (D = 64, 128); a pass of 8 rows (D = 256) does not
+    if (EVEN && ROWS % 32 == 0) return k_soff + p * ROWS * KP;
+    const int c = tid + p * NT, r = c / DG;
+    return ((r & ~31) | perm5(r & 31)) * KP + (c % DG) * 16;
+  };
+  auto v_sto = [&](int p) {
+    if (EVEN) return v_soff + p * ROWS * VP;
+    const int c = tid + p * NT;
+    return (c / DG) * VP + (c % DG) * 16;
+  };
   u32x4 kreg[CH], vreg[CH];
   auto load_k = [&](int t) {
-    const int base = k_goff + (t < ntiles ? t * BN * k_rowb : k_ext);
+    const int base = (EVEN ? k_goff : 0) + (t < ntiles ? t * BN * k_rowb : k_ext);
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + p * ROWS * k_rowb, 0, 0);
+      if (chunk_ok(p))
+        kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + g_off(p, k_rowb), 0, 0);
   };
   auto load_v = [&](int t) {
-    const int base = v_goff + (t < ntiles ? t * BN * v_rowb : v_ext);
+    const int base = (EVEN ? v_goff : 0) + (t < ntiles ? t * BN * v_rowb : v_ext);
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, base + p * ROWS * v_rowb, 0, 0);
+      if (chunk_ok(p))
+        vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, base + g_off(p, v_rowb), 0, 0);
   };
   auto store_k = [&](int st) {
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      *reinterpret_cast<u32x4*>(lds + st * KT + k_soff + p * ROWS * KP) = kreg[p];
+      if (chunk_ok(p)) *reinterpret_cast<u32x4*>(lds + st * KT + k_sto(p)) = kreg[p];
   };
   auto store_v = [&](int st) {
 #pragma unroll
     for (int p = 0; p < CH; ++p)
-      *reinterpret_cast<u32x4*>(lds + 2 * KT + st * VT + v_soff + p * ROWS * VP) = vreg[p];
+      if (chunk_ok(p)) *reinterpret_cast<u32x4*>(lds + 2 * KT + st * VT + v_sto(p)) = vreg[p];
   };
 
   // Per-lane operand addresses (stage and tile offsets are immediates).
@@ -362,8 +395,7 @@ void fwd_mfma(Args a) {
   v8 kpre[KPRE];        // first K fragments of the next S, read ahead in the vector phase
 
   // K operand fragment i of a tile's S, in the order the products consume them:
-  // i = 2c + kt is head-dim chunk c (dims 16c..16c+15) of key sub-tile kt.
-  constexpr int NKF = 2 * (D / 16);
+  // i = 2c + kt is head-dim chunk c (dims 16c..16c+15) of key sub-tile kt (NKF of them).
   auto kfrag_off = [](int i) { return (i & 1) * 32 * KP + (i >> 1) * 32; };
 
   // The first KPRE K fragments of tile t's S, read at the end of the vector phase that
@@ -550,26 +582,42 @@ void fwd_mfma(Args a) {
   load_k(0);
   store_k(0);
   __syncthreads();
-  if (grp == 0) prefetch_k(0);
-  for (int t = 0; t <= ntiles; ++t) {
-    load_k(t + 1);
-    load_v(t);
-    if (grp == 0) {
-      mphase(t);
-    } else {
-      vphase(t - 1);
+  if (G == 1) {
+    // One wave per SIMD (D = 256): each wave runs M(t) then V(t).  K(t+1) and V(t) go to
+    // the stages that held K(t-1) and V(t-2), whose last reader, M(t-1), every wave
+    // finished before the previous barrier; one barrier per step publishes them.
+    for (int t = 0; t <= ntiles; ++t) {
+      load_k(t + 1);
+      load_v(t);
       prefetch_k(t);
-    }
-    store_k((t + 1) & 1);
-    __syncthreads();
-    if (grp == 0) {
-      vphase(t);
-      prefetch_k(t + 1);
-    } else {
       mphase(t);
+      vphase(t);
+      store_k((t + 1) & 1);
+      store_v(t & 1);
+      __syncthreads();
     }
-    store_v(t & 1);
-    __syncthreads();
+  } else {
+    if (grp == 0) prefetch_k(0);
+    for (int t = 0; t <= ntiles; ++t) {
+      load_k(t + 1);
+      load_v(t);
+      if (grp == 0) {
+        mphase(t);
+      } else {
+        vphase(t - 1);
+        prefetch_k(t);
+      }
+      store_k((t + 1) & 1);
+      __syncthreads();
+      if (grp == 0) {
+        vphase(t);
+        prefetch_k(t + 1);
+      } else {
+        mphase(t);
+      }
+      store_v(t & 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: normalise, safe-softmax zeros, store O and the LSE ----
@@ -627,8 +675,10 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   constexpr int K_ELEMS = kBlockNF32 * KROW;
   constexpr int V_ELEMS = kBlockNF32 * D;
   constexpr int STAGE = K_ELEMS + V_ELEMS;
+  constexpr int NS = stages_f32(D);  // LDS stages: 2 (double-buffered) or 1 (D = 256)
   static_assert(CH * kThreadsF32 == kBlockNF32 * DG, "tile must split evenly over threads");
-  __shared__ __attribute__((aligned(16))) float lds[2 * STAGE];
+  static_assert(NS * STAGE * 4 == lds_bytes_f32(D), "plan and kernel disagree on LDS");
+  __shared__ __attribute__((aligned(16))) float lds[NS * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -705,8 +755,8 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    const int buf = NS == 2 ? t & 1 : 0;
+    if (NS == 2 && t + 1 < ntiles) load_tile(t + 1);
     const float* ks = lds + buf * STAGE;
     const float* vs = ks + K_ELEMS;
     const int k0 = t * kBlockNF32;
@@ -786,8 +836,15 @@ __global__ __launch_bounds__(kThreadsF32) void fwd_f32(Args a) {
           }
     }
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    if (NS == 2) {
+      if (t + 1 < ntiles) store_tile(buf ^ 1);
+      __syncthreads();
+    } else if (t + 1 < ntiles) {  // one stage: every wave is done with it before the refill
+      load_tile(t + 1);
+      __syncthreads();
+      store_tile(0);
+      __syncthreads();
+    }
   }
 
   const float l_tot = pair_sum(l_run);
@@ -845,9 +902,10 @@ __global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int
   const int64_t bh = row / a.Lq, i = row - bh * a.Lq;
   float m = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, a.ws_lse[sp * rows + row]);
-  float acc[D / 64];
+  constexpr int E = (D + 63) / 64;  // head dims per lane: lane + 64e for lane + 64e < D
+  float acc[E];
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (m != -INFINITY) {
     for (int sp = 0; sp < nsplit; ++sp) {
@@ -855,13 +913,15 @@ __global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int
       wsum += w;
       const float* o = a.ws_o + (sp * rows + row) * D;
 #pragma unroll
-      for (int e = 0; e < D / 64; ++e) acc[e] = __builtin_fmaf(w, o[lane + 64 * e], acc[e]);
+      for (int e = 0; e < E; ++e)
+        if (lane + 64 * e < D) acc[e] = __builtin_fmaf(w, o[lane + 64 * e], acc[e]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int64_t b = bh / a.H, h = bh - b * a.H;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) {
+  for (int e = 0; e < E; ++e) {
+    if (lane + 64 * e >= D) break;
     const int64_t off = b * a.so[0] + h * a.so[1] + i * a.so[2] + lane + 64 * e;
     static_cast<T*>(a.out)[off] = static_cast<T>(acc[e] * inv);
   }
@@ -883,7 +943,7 @@ hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
              : reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MK, false, MODE>);
   else
     fn = reinterpret_cast<const void*>(&fwd_f32<D, CAUSAL, MK, MODE>);
-  return hipLaunchKernel(fn, dim3(grid), dim3(block_threads(dtype)), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(block_threads(dtype, D)), args, 0, stream);
 }
 
 template <int D>
@@ -939,7 +999,8 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.Lk = int32_t(p.Lk);
   // dense: B*H heads of Lq rows; packed: nseq*H heads of up to max_seqlen_q rows
   const int64_t rows = p.varlen ? p.max_seqlen_q : p.Lq;
-  a.q_tiles = int32_t((rows + block_m(p.dtype) - 1) / block_m(p.dtype));
+  const int bm = block_m(p.dtype, int(p.D));
+  a.q_tiles = int32_t((rows + bm - 1) / bm);
   a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);
   a.scale_log2 = p.scale * kLog2e;
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
@@ -954,11 +1015,24 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   const unsigned grid =
       unsigned(int64_t(a.q_tiles) * a.bh_count * (mode == kSplit ? p.nsplit : 1));
   const bool causal = p.causal != 0;
-  hipError_t e = p.D == 64 ? launch_d<64>(a, p.dtype, causal, mode, grid, stream)
-                           : launch_d<128>(a, p.dtype, causal, mode, grid, stream);
+  hipError_t e;
+  switch (p.D) {
+    case 32: e = launch_d<32>(a, p.dtype, causal, mode, grid, stream); break;
+    case 64: e = launch_d<64>(a, p.dtype, causal, mode, grid, stream); break;
+    case 96: e = launch_d<96>(a, p.dtype, causal, mode, grid, stream); break;
+    case 128: e = launch_d<128>(a, p.dtype, causal, mode, grid, stream); break;
+    case 256: e = launch_d<256>(a, p.dtype, causal, mode, grid, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   if (e != hipSuccess || mode != kSplit) return e;
-  return p.D == 64 ? launch_combine<64>(a, p.dtype, int(p.nsplit), stream)
-                   : launch_combine<128>(a, p.dtype, int(p.nsplit), stream);
+  const int ns = int(p.nsplit);
+  switch (p.D) {
+    case 32: return launch_combine<32>(a, p.dtype, ns, stream);
+    case 64: return launch_combine<64>(a, p.dtype, ns, stream);
+    case 96: return launch_combine<96>(a, p.dtype, ns, stream);
+    case 128: return launch_combine<128>(a, p.dtype, ns, stream);
+    default: return launch_combine<256>(a, p.dtype, ns, stream);
+  }
 }
 
 }  // namespace sdpa

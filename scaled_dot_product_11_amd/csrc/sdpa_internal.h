@@ -7,9 +7,12 @@
 
 namespace sdpa {
 
-// Tile shapes.  bf16 kernel: a workgroup is 8 waves of 64 lanes, each wave owns 32 query
-// rows (256 per workgroup), keys advance 64 at a time; the waves form two groups that
-// alternate between matrix and vector phases.  fp32 kernel: 4 waves, 32 rows each (128
+// Tile shapes.  16-bit kernel: keys advance 64 at a time and each wave of 64 lanes owns
+// 32 query rows.  For D <= 128 a workgroup is 8 waves (256 rows) forming two groups that
+// alternate between matrix and vector phases, two waves per SIMD; at D = 256 a wave's
+// accumulators, Q fragments and staging registers need more than the 256 registers a wave
+// gets at two waves per SIMD, so the workgroup is 4 waves (128 rows), one per SIMD, each
+// running its matrix and vector work in turn.  fp32 kernel: 4 waves, 32 rows each (128
 // per workgroup), 64 keys at a time.
 constexpr int kThreadsBf16 = 512;
 constexpr int kBlockMBf16 = 256;
@@ -17,11 +20,19 @@ constexpr int kBlockNBf16 = 64;
 constexpr int kThreadsF32 = 256;
 constexpr int kBlockMF32 = 128;
 constexpr int kBlockNF32 = 64;
+// Head dims of the forward kernels (every dtype); the backward takes 64 and 128.
+constexpr bool fwd_head_dim_ok(int64_t D) {
+  return D == 32 || D == 64 || D == 96 || D == 128 || D == 256;
+}
+// Phase groups of the 16-bit kernel at head dim D (2: paired waves alternate phases).
+constexpr int groups_16(int D) { return D <= 128 ? 2 : 1; }
 // dtype: 0 = fp32, 1 = bf16, 2 = fp16 (the values of sdpa_dtype); both 16-bit types run
 // the same matrix-core kernel and tiles
-constexpr int block_m(int dtype) { return dtype != 0 ? kBlockMBf16 : kBlockMF32; }
+constexpr int block_m(int dtype, int D) { return dtype != 0 ? 128 * groups_16(D) : kBlockMF32; }
 constexpr int block_n(int dtype) { return dtype != 0 ? kBlockNBf16 : kBlockNF32; }
-constexpr int block_threads(int dtype) { return dtype != 0 ? kThreadsBf16 : kThreadsF32; }
+constexpr int block_threads(int dtype, int D) {
+  return dtype != 0 ? 256 * groups_16(D) : kThreadsF32;
+}
 
 // Rank-3 [N,L,D] and rank-4 [B,H,L,D] inputs both become this (b, h, row, col) view;
 // every stride is in elements of the tensor's own type.  Packed variable-length inputs
@@ -70,8 +81,11 @@ constexpr int v_pitch_bf16(int D) { return 2 * D + 64; }
 constexpr int64_t lds_bytes_bf16(int D) {
   return 2 * int64_t(kBlockNBf16) * (k_pitch_bf16(D) + v_pitch_bf16(D));
 }
+// The fp32 kernel double-buffers its K/V tiles up to D = 128; at D = 256 two stages would
+// exceed the 160 KiB of LDS, and it runs with one.
+constexpr int stages_f32(int D) { return D <= 128 ? 2 : 1; }
 constexpr int64_t lds_bytes_f32(int D) {
-  return 2 * (int64_t(kBlockNF32) * (D + 1) * 4 + int64_t(kBlockNF32) * D * 4);
+  return stages_f32(D) * (int64_t(kBlockNF32) * (D + 1) * 4 + int64_t(kBlockNF32) * D * 4);
 }
 
 // Launches the kernel matching p.dtype / p.D / p.causal / mask on `stream` (and, with

@@ -98,8 +98,10 @@ def test_shape_errors():
 
 
 def test_head_dim_and_dtype_errors():
-    for D in (0, 32, 96, 256):
+    for D in (0, -64, 16, 48, 80, 160, 192, 512):
         assert check(**args4(D=D)) == HEAD
+    for D in (32, 64, 96, 128, 256):
+        assert check(**args4(D=D)) == OK
     assert check(**args4(dtype=sd.SDPA_F16)) == OK
     assert check(**args4(dtype=3)) == DTYPE
     assert check(**args4(dtype=-1)) == DTYPE
@@ -168,10 +170,10 @@ def test_fwd_rejects_before_any_device_call():
     """Validation errors come back from sdpa_fwd itself, without touching a GPU."""
     import ctypes
     lib = sd.load_library()
-    a = args4(D=96)
+    a = args4(D=80)
     arr = (ctypes.c_int64 * 20)(*a["strides"])
     st = lib.sdpa_fwd(a["q_ptr"], a["k_ptr"], a["v_ptr"], a["out_ptr"], a["lse_ptr"], 4, 2, 3, 100,
-                      90, 96, arr, 0.125, 1, None, 1, None)
+                      90, 80, arr, 0.125, 1, None, 1, None)
     assert st == HEAD
     # an empty problem is a no-op returning success, also without a GPU
     st = lib.sdpa_fwd(None, None, None, None, None, 4, 2, 3, 0, 90, 64, arr, 0.125, 1, None, 1, None)
@@ -201,6 +203,25 @@ def test_plan_items_are_a_permutation(causal):
                 assert bh % 8 == i % 8
         with pytest.raises(sd.SdpaError):
             sd.sdpa_plan_item(plan, plan.items)
+
+
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_plan_tiles_per_head_dim(D, dtype):
+    """16-bit kernels: 8 waves and 256 rows up to D = 128, 4 waves and 128 rows at D = 256;
+    the fp32 kernel: 4 waves and 128 rows.  LDS always fits the 160 KiB of a CU."""
+    dt = {"f32": sd.SDPA_F32, "bf16": sd.SDPA_BF16, "f16": sd.SDPA_F16}[dtype]
+    plan = sd.sdpa_plan(4, 2, 3, 1000, 1000, D, 1, dt)
+    if dtype == "f32":
+        assert (plan.block_m, plan.threads) == (128, 256)
+        stages = 2 if D <= 128 else 1
+        assert plan.lds_bytes == stages * 64 * ((D + 1) + D) * 4
+    else:
+        assert (plan.block_m, plan.threads) == ((256, 512) if D <= 128 else (128, 256))
+        assert plan.lds_bytes == 2 * 64 * ((2 * D + 16) + (2 * D + 64))
+    assert plan.block_n == 64
+    assert plan.q_tiles == (1000 + plan.block_m - 1) // plan.block_m
+    assert plan.lds_bytes <= 160 * 1024
 
 
 def test_plan_rejects_bad_sizes():
@@ -345,7 +366,8 @@ def vcheck(**kw):
 def test_varlen_check():
     assert vcheck(**vargs()) == OK
     assert vcheck(**vargs(dtype=sd.SDPA_F32, D=128)) == OK
-    assert vcheck(**vargs(D=96)) == HEAD
+    assert vcheck(**vargs(D=80)) == HEAD
+    assert vcheck(**vargs(D=96)) == OK
     assert vcheck(**vargs(dtype=3)) == DTYPE
     assert vcheck(**vargs(dtype=sd.SDPA_F16)) == OK
     assert vcheck(**vargs(causal=4)) == CAUSAL_ERR
@@ -407,7 +429,7 @@ def test_splitkv_workspace_sizes():
     assert ws(2, 3, 4, 5000, 64, 0) == 10 * 6 * 4 * 65 * 4
     assert ws(1, 1, 1, 0, 64, 0) == 1 * 1 * 1 * 65 * 4
     with pytest.raises(sd.SdpaError):
-        ws(1, 1, 1, 10, 96, 0)
+        ws(1, 1, 1, 10, 80, 0)
     with pytest.raises(sd.SdpaError):
         ws(1, 1, 1, 10, 64, 5000)  # more than 1024 splits
 
@@ -418,7 +440,7 @@ def test_splitkv_check():
     assert c(**sargs(dtype=sd.SDPA_F32, D=64, causal=0, num_splits=7)) == OK
     assert c(**sargs(num_splits=-1)) == SHAPE
     assert c(**sargs(causal=5)) == CAUSAL_ERR
-    assert c(**sargs(D=32)) == HEAD
+    assert c(**sargs(D=48)) == HEAD
     need = sd.sdpa_fwd_splitkv_workspace(2, 3, 4, 5000, 128, 0)
     assert c(**sargs(workspace_bytes=need)) == OK
     assert c(**sargs(workspace_bytes=need - 1)) == WORKSPACE_ERR

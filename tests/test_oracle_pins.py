@@ -106,6 +106,33 @@ def test_library_math_backend_fp64():
         np.testing.assert_allclose(out[..., rows_ok, :], ref[..., rows_ok, :], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("D", [32, 96, 256])
+def test_brute_force_and_library_at_wide_head_dims(D):
+    """The head dims 32, 96 and 256 against the numpy five-step formulation and PyTorch's
+    fp64 math backend, causal and masked (the oracle's loops do not depend on D)."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+    rng = np.random.default_rng(D)
+    for causal, with_mask in [(True, False), (False, True)]:
+        q, k, v, mask = rand_case(rng, 1, 2, 9, 13, D, with_mask, empty_rows=1)
+        scale = 1 / math.sqrt(D)
+        out, lse = sdpa_oracle(q, k, v, mask=None if mask is None else torch.from_numpy(mask),
+                               is_causal=causal, scale=scale)
+        keep = visible(9, 13, causal, mask)
+        ref_out, ref_lse = naive_five_steps(q, k, v, keep, scale)
+        np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
+        fin = np.isfinite(ref_lse)
+        np.testing.assert_allclose(lse[fin], ref_lse[fin], rtol=0, atol=1e-12)
+        assert np.all(out[~fin] == 0.0) and np.all(lse[~fin] == -np.inf)
+        with sdpa_kernel(SDPBackend.MATH):
+            lib = F.scaled_dot_product_attention(
+                *(torch.from_numpy(x) for x in (q, k, v)),
+                attn_mask=torch.from_numpy(np.broadcast_to(keep, (1, 2, 9, 13)).copy()),
+                scale=scale).numpy()
+        rows_ok = keep.any(-1)
+        np.testing.assert_allclose(out[..., rows_ok, :], lib[..., rows_ok, :], rtol=0, atol=1e-12)
+
+
 def _load_golden():
     with open(GOLDEN) as f:
         return json.load(f)["cases"]

@@ -170,7 +170,7 @@ def test_fully_masked_rows_are_zero():
 
 
 def test_invalid_arguments_raise():
-    q = torch.randn(1, 1, 16, 96, device=DEV).to(torch.bfloat16)
+    q = torch.randn(1, 1, 16, 80, device=DEV).to(torch.bfloat16)
     with pytest.raises(SdpaError):
         sdpa_fwd(q, q, q)
     q = torch.randn(1, 1, 16, 64, device=DEV).to(torch.float64)

@@ -42,7 +42,7 @@ def run_split(q, k, v, causal, num_splits, scale=None):
     written, and the workspace's contents on entry must not matter."""
     out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
     lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device=DEV)
-    dt = 1 if q.dtype == torch.bfloat16 else 0
+    dt = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}[q.dtype]
     need = sdpa_fwd_splitkv_workspace(*sizes(q, k), num_splits, dt)
     ws = torch.full((need // 4 + 4,), float("nan"), dtype=torch.float32, device=DEV)
     out, lse = sdpa_fwd_splitkv(to_dev(q), to_dev(k), to_dev(v), out, lse, is_causal=causal,

@@ -113,14 +113,15 @@ def config3(device="cpu", rank=3):
                     1 / math.sqrt(128), f"rank-{rank} causal bf16 B*H=128 L=2048 D=128")
 
 
-def config4(device="cpu"):
+def config4(device="cpu", D=128):
     """Long-sequence causal, bf16, [1,32,8192,128], entries N(0,1)*0.5, each tensor a
-    [B,L,H,D] buffer viewed as [B,H,L,D] through a transpose (non-contiguous)."""
+    [B,L,H,D] buffer viewed as [B,H,L,D] through a transpose (non-contiguous).  Another head
+    dim D gives the same recipe at [1,32,8192,D] (scale 1/sqrt(D))."""
     g = torch.Generator().manual_seed(4)
-    bufs = [_randn(g, (1, 8192, 32, 128), torch.bfloat16, 0.5).to(device) for _ in range(3)]
+    bufs = [_randn(g, (1, 8192, 32, D), torch.bfloat16, 0.5).to(device) for _ in range(3)]
     q, k, v = (b.transpose(1, 2) for b in bufs)
-    return Workload("c4_rank4_bf16_causal_b1_h32_l8192_d128_strided", q, k, v, None, True,
-                    1 / math.sqrt(128), "rank-4 causal bf16 [1,32,8192,128], [B,L,H,D] strides")
+    return Workload(f"c4_rank4_bf16_causal_b1_h32_l8192_d{D}_strided", q, k, v, None, True,
+                    1 / math.sqrt(D), f"rank-4 causal bf16 [1,32,8192,{D}], [B,L,H,D] strides")
 
 
 def config5(device="cpu"):
