@@ -382,6 +382,58 @@ void fwd_mfma(Args a) {
   const int vfrag = (8 * (g16 >> 1) + e4) * VP + (16 * (g16 & 1) + 4 * q4) * 2;
   const float c2 = POS ? a.scale_log2 : 1.f;
 
+  // Mask bytes (boolean mask) and bias values (additive mask) of this lane's keys of key
+  // tile t: runs of 8 keys at 64t + 32kt + 16g + 8hf, run 2kt + g.  They are loaded ahead
+  // of the vector phase that uses them, so that the latency of the loads is covered by the
+  // phases in between: the mask bytes of tile t + 1 are loaded at the start of V(t) (eight
+  // registers), the bias values of tile t + 1 at the end of V(t), into the registers V(t)
+  // has just consumed (a second set of 32 would not fit beside the D = 128 accumulators,
+  // and measured no faster at D = 64).  Lanes past the last query row, and tiles past the
+  // wave's last one, load nothing (all keys visible, zero bias).
+  constexpr int NMB = MASK ? 4 : 1, NBV = BIAS ? 32 : 1;
+  uint64_t mcur[NMB];
+  float bcur[NBV];
+  auto load_mask = [&](uint64_t* m, int t) {
+    const uint8_t* mrow = mb + int64_t(qi) * a.sm[2];
+#pragma unroll
+    for (int run = 0; run < 4; ++run) {
+      const int key0 = t * BN + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
+      if (a.mask_vec8 && key0 + 8 <= Lk) {
+        m[run] = *reinterpret_cast<const uint64_t*>(mrow + key0);
+      } else {
+        uint64_t w = 0;
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e < Lk) w |= uint64_t(mrow[key0 + e]) << (8 * e);
+        m[run] = w;
+      }
+    }
+  };
+  auto load_bias = [&](float* bv, int t) {
+    const float* brow = bb + int64_t(qi) * a.sm[2];
+#pragma unroll
+    for (int run = 0; run < 4; ++run) {
+      const int key0 = t * BN + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
+      if (a.bias_vec4 && key0 + 8 <= Lk) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(brow + key0);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(brow + key0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bv[8 * run + e] = lo[e];
+          bv[8 * run + e + 4] = hi[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[8 * run + e] = key0 + e < Lk ? brow[key0 + e] : 0.f;
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NMB; ++i) mcur[i] = ~0ull;
+#pragma unroll
+  for (int i = 0; i < NBV; ++i) bcur[i] = 0.f;
+  if (MASK && q_ok && wtiles > 0) load_mask(mcur, 0);
+  if (BIAS && q_ok && wtiles > 0) load_bias(bcur, 0);
+
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -479,50 +531,29 @@ void fwd_mfma(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][r] *= a.scale_log2;
     }
-    if (BIAS && q_ok) {
-      // additive mask of this lane's keys (runs of 8 at k0 + 32kt + 16g + 8hf), in base-2
-      // units; keys past Lk are hidden below
-      const float* brow = bb + int64_t(qi) * a.sm[2];
+    const bool pre = q_ok && t + 1 < wtiles;  // this lane loads tile t + 1's mask / bias
+    uint64_t mnext[NMB];
+    if (MASK) {
 #pragma unroll
-      for (int run = 0; run < 4; ++run) {
-        const int key0 = k0 + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
-        float bv[8];
-        if (a.bias_vec4 && key0 + 8 <= Lk) {
-          const f32x4 lo = *reinterpret_cast<const f32x4*>(brow + key0);
-          const f32x4 hi = *reinterpret_cast<const f32x4*>(brow + key0 + 4);
+      for (int i = 0; i < NMB; ++i) mnext[i] = ~0ull;
+      if (pre) load_mask(mnext, t + 1);
+    }
+    if (BIAS) {
+      // additive mask of this lane's keys, in base-2 units; keys past Lk are hidden below
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            bv[e] = lo[e];
-            bv[e + 4] = hi[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bv[e] = key0 + e < Lk ? brow[key0 + e] : 0.f;
-        }
+      for (int run = 0; run < 4; ++run)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          s[run >> 1][8 * (run & 1) + e] = __builtin_fmaf(bv[e], kLog2e, s[run >> 1][8 * (run & 1) + e]);
-      }
+          s[run >> 1][8 * (run & 1) + e] =
+              __builtin_fmaf(bcur[8 * run + e], kLog2e, s[run >> 1][8 * (run & 1) + e]);
     }
+    // Hidden keys -> -inf: on the tiles that cross the causal diagonal or the end of the
+    // keys, by position (and mask byte); on the others, with a mask, by mask byte only.
+    auto mask_byte = [&](int kt, int r) {
+      return uint32_t(mcur[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xffu;
+    };
     const bool edge = (CAUSAL && k0 + BN - 1 > qw + coff) || (k0 + BN > Lk);
-    if (edge || MASK) {
-      // Mask bytes of this lane's keys: runs of 8 at k0 + 32kt + 16g + 8hf.
-      uint64_t mbits[4] = {~0ull, ~0ull, ~0ull, ~0ull};
-      if (MASK && q_ok) {
-        const uint8_t* mrow = mb + int64_t(qi) * a.sm[2];
-#pragma unroll
-        for (int run = 0; run < 4; ++run) {
-          const int key0 = k0 + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
-          if (a.mask_vec8 && key0 + 8 <= Lk) {
-            mbits[run] = *reinterpret_cast<const uint64_t*>(mrow + key0);
-          } else {
-            uint64_t w = 0;
-            for (int e = 0; e < 8; ++e)
-              if (key0 + e < Lk) w |= uint64_t(mrow[key0 + e]) << (8 * e);
-            mbits[run] = w;
-          }
-        }
-      }
+    if (edge) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -530,10 +561,21 @@ void fwd_mfma(Args a) {
           const int key = k0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
           bool hide = key >= Lk;
           if (CAUSAL) hide = hide || key > qi + coff;
-          if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
+          if (MASK) hide = hide || mask_byte(kt, r) == 0;
           if (hide) s[kt][r] = -INFINITY;
         }
+    } else if (MASK) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (mask_byte(kt, r) == 0) s[kt][r] = -INFINITY;
     }
+    if (MASK) {
+#pragma unroll
+      for (int i = 0; i < NMB; ++i) mcur[i] = mnext[i];
+    }
+    if (BIAS && pre) load_bias(bcur, t + 1);
     // Online softmax with a lagging reference: rescale O and l only when some row of the
     // wave sees its max grow by more than kRescaleSlack.  The lane's 32 scores are
     // reduced by a chain of 3-input maxima (v_max3_f32).
