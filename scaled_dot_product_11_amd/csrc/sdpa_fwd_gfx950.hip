@@ -291,9 +291,7 @@ void fwd_mfma(Args a) {
     if (q_ok) w = ld16(qb + int64_t(qi) * a.sq[2] + 16 * c + 8 * hf);
     qf[c] = __builtin_bit_cast(v8, w);
   }
-  // Retire the Q loads here, on every path: left in flight, they would make the
-  // memory-counter wait in the key loop cover the K/V prefetch as well.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // (the Q loads stay in flight with the first K tile's: both are retired before the key loop)
 
   // Key tiles the workgroup stages (keys that can be visible to some stored row), and
   // the tiles this wave computes on (with a causal mask: tiles 0 .. (qw + 31 + coff) / 64).
@@ -303,10 +301,10 @@ void fwd_mfma(Args a) {
   const int wlast = qw + 31 + coff;  // last key any row of the wave may see (causal)
   const int wtiles = !wave_live ? 0 : CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
 
-  // ---- global -> register -> LDS staging of K and V tiles.  All 512 threads stage: the
-  // loads of K(t+1) and V(t) are issued at the start of step t, K(t+1) is written to LDS
-  // at the end of phase A and V(t) at the end of phase B, so each phase carries half of
-  // the store traffic.  The loads are buffer loads whose whole byte offset (tile, row and
+  // ---- global -> register -> LDS staging of K and V tiles.  All threads stage: V(t) is
+  // loaded at the start of step t and written to LDS at the end of its phase B; K(t+1) is
+  // written at the end of phase A of step t and K(t+2) loaded right after, so each phase
+  // carries half of the store traffic and every K load has a whole step to arrive.  The loads are buffer loads whose whole byte offset (tile, row and
   // column) is in the per-lane offset, which the hardware checks against the buffer's
   // extent: rows past the end of the head read as zero, and tiles past the staged range
   // are given an offset beyond the extent, so they read zeros without touching memory.
@@ -617,31 +615,38 @@ void fwd_mfma(Args a) {
   // ---- two-phase pipeline over key tiles ----
   // Step t:  phase A: group 0 runs M(t); group 1 runs V(t-1) and reads ahead for its M(t);
   //                   then every thread writes K(t+1) to LDS
+  //                   and loads K(t+2)
   //          phase B: group 0 runs V(t) and reads ahead for M(t+1); group 1 runs M(t);
   //                   then every thread writes V(t) to LDS
   // M(t) reads K(t) (stage t&1) and V(t-1) (stage (t-1)&1); K(t+1) and V(t) go to the
   // other stages, whose previous tiles step t-1 finished with.
+  // Prologue: the Q, first mask / bias and K(0) loads are in flight together; retiring
+  // all of them here (on every path) leaves only K(1) outstanding at the loop's entry, so
+  // the memory-counter waits in the loop cover just the tiles they need.  Each K tile is
+  // then loaded right after its predecessor is written to LDS, a whole step before its own
+  // store.
   load_k(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   store_k(0);
+  load_k(1);
   __syncthreads();
   if (G == 1) {
     // One wave per SIMD (D = 256): each wave runs M(t) then V(t).  K(t+1) and V(t) go to
     // the stages that held K(t-1) and V(t-2), whose last reader, M(t-1), every wave
     // finished before the previous barrier; one barrier per step publishes them.
     for (int t = 0; t <= ntiles; ++t) {
-      load_k(t + 1);
       load_v(t);
       prefetch_k(t);
       mphase(t);
       vphase(t);
       store_k((t + 1) & 1);
+      load_k(t + 2);
       store_v(t & 1);
       __syncthreads();
     }
   } else {
     if (grp == 0) prefetch_k(0);
     for (int t = 0; t <= ntiles; ++t) {
-      load_k(t + 1);
       load_v(t);
       if (grp == 0) {
         mphase(t);
@@ -650,6 +655,7 @@ void fwd_mfma(Args a) {
         prefetch_k(t);
       }
       store_k((t + 1) & 1);
+      load_k(t + 2);
       __syncthreads();
       if (grp == 0) {
         vphase(t);

@@ -238,6 +238,37 @@ def test_config3_rank3_equals_rank4_bitwise():
     check_sampled(wl3, out3, lse3, seed=3)
 
 
+def test_config3_rank3_and_rank4_equal_speed():
+    """The rank-3 input and its rank-4 view reach the same kernel with the same arguments, so
+    their launch times agree: medians of interleaved blocks of launches within 3 %."""
+    import statistics
+    wl3, wl4 = W.config3(rank=3), W.config3(rank=4)
+    ins = {}
+    for name, wl in (("r3", wl3), ("r4", wl4)):
+        q, k, v = to_dev(wl.q), to_dev(wl.k), to_dev(wl.v)
+        ins[name] = (q, k, v, torch.empty_like(q), torch.empty(q.shape[:-1], device=DEV))
+
+    def times(name, n):
+        q, k, v, out, lse = ins[name]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            sdpa_fwd(q, k, v, out, lse, is_causal=True, scale=wl3.scale)
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    for name in ins:  # warm-up
+        times(name, 5)
+    t = {"r3": [], "r4": []}
+    for _ in range(8):
+        for name in ("r3", "r4"):
+            t[name] += times(name, 6)
+    m3, m4 = statistics.median(t["r3"]), statistics.median(t["r4"])
+    assert abs(m3 / m4 - 1) <= 0.03, f"rank-3 median {m3:.4f} ms vs rank-4 {m4:.4f} ms"
+
+
 def test_config4_strided_long_sequence():
     wl = W.config4()
     out, lse = run_wl(wl)
