@@ -253,6 +253,8 @@ void fwd_mfma(Args a) {
   constexpr int VT = BN * VP;              // bytes of one V stage
   static_assert(D % 32 == 0 && BM == 32 * 4 * G && NT == 64 * 4 * G, "tile shape");
   static_assert(2 * KT + 2 * VT == lds_bytes_bf16(D), "plan and kernel disagree on LDS");
+  static_assert(4 * G * 32 * KP <= 2 * KT + 2 * VT, "the epilogue's output tiles fit the LDS");
+  static_assert((32 * DG) % 64 == 0, "the epilogue's row chunks split evenly over a wave");
   __shared__ __attribute__((aligned(16))) char lds[2 * KT + 2 * VT];
 
   const int tid = threadIdx.x;
@@ -301,10 +303,10 @@ void fwd_mfma(Args a) {
   const int wlast = qw + 31 + coff;  // last key any row of the wave may see (causal)
   const int wtiles = !wave_live ? 0 : CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
 
-  // ---- global -> register -> LDS staging of K and V tiles.  All threads stage: V(t) is
-  // loaded at the start of step t and written to LDS at the end of its phase B; K(t+1) is
-  // written at the end of phase A of step t and K(t+2) loaded right after, so each phase
-  // carries half of the store traffic and every K load has a whole step to arrive.  The loads are buffer loads whose whole byte offset (tile, row and
+  // ---- global -> register -> LDS staging of K and V tiles.  All threads stage: K(t+1) is
+  // written to LDS at the end of phase A of step t and K(t+2) loaded right after; V(t) is
+  // written at the end of phase B and V(t+1) loaded right after.  Each phase carries half
+  // of the store traffic, and every load has a whole step to arrive.  The loads are buffer loads whose whole byte offset (tile, row and
   // column) is in the per-lane offset, which the hardware checks against the buffer's
   // extent: rows past the end of the head read as zero, and tiles past the staged range
   // are given an offset beyond the extent, so they read zeros without touching memory.
@@ -617,15 +619,16 @@ void fwd_mfma(Args a) {
   //                   then every thread writes K(t+1) to LDS
   //                   and loads K(t+2)
   //          phase B: group 0 runs V(t) and reads ahead for M(t+1); group 1 runs M(t);
-  //                   then every thread writes V(t) to LDS
+  //                   then every thread writes V(t) to LDS and loads V(t+1)
   // M(t) reads K(t) (stage t&1) and V(t-1) (stage (t-1)&1); K(t+1) and V(t) go to the
   // other stages, whose previous tiles step t-1 finished with.
-  // Prologue: the Q, first mask / bias and K(0) loads are in flight together; retiring
-  // all of them here (on every path) leaves only K(1) outstanding at the loop's entry, so
-  // the memory-counter waits in the loop cover just the tiles they need.  Each K tile is
-  // then loaded right after its predecessor is written to LDS, a whole step before its own
-  // store.
+  // Prologue: the Q, first mask / bias, K(0) and V(0) loads are in flight together;
+  // retiring all of them here (on every path) leaves only K(1) outstanding at the loop's
+  // entry, so the memory-counter waits in the loop cover just the tiles they need.  Each K
+  // and V tile is then loaded right after its predecessor is written to LDS, a whole step
+  // before its own store.
   load_k(0);
+  load_v(0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   store_k(0);
   load_k(1);
@@ -635,19 +638,18 @@ void fwd_mfma(Args a) {
     // the stages that held K(t-1) and V(t-2), whose last reader, M(t-1), every wave
     // finished before the previous barrier; one barrier per step publishes them.
     for (int t = 0; t <= ntiles; ++t) {
-      load_v(t);
       prefetch_k(t);
       mphase(t);
       vphase(t);
       store_k((t + 1) & 1);
       load_k(t + 2);
       store_v(t & 1);
+      load_v(t + 1);
       __syncthreads();
     }
   } else {
     if (grp == 0) prefetch_k(0);
     for (int t = 0; t <= ntiles; ++t) {
-      load_v(t);
       if (grp == 0) {
         mphase(t);
       } else {
@@ -664,6 +666,7 @@ void fwd_mfma(Args a) {
         mphase(t);
       }
       store_v(t & 1);
+      load_v(t + 1);
       __syncthreads();
     }
   }
@@ -686,8 +689,12 @@ void fwd_mfma(Args a) {
       if (hf == 0)
         a.ws_lse[prow] = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
-  } else if (q_ok) {
-    uint16_t* orow = ob + int64_t(qi) * a.so[2];
+  } else {
+    // The wave's 32 x D output tile goes through LDS (free after the key loop's last
+    // barrier; each wave uses its own 32 rows of pitch KP), so that the global stores write
+    // whole rows: lane l stores 16-byte chunks l, l + 64, ... of the tile in row-major order,
+    // four rows of D = 128 per instruction, instead of 8-byte pieces of 32 rows.
+    char* ot = lds + wave * 32 * KP;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -701,9 +708,17 @@ void fwd_mfma(Args a) {
           w[e] = uint32_t(__builtin_bit_cast(uint16_t, lo)) |
                  (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
         }
-        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * g + 4 * hf) = u32x2{w[0], w[1]};
+        *reinterpret_cast<u32x2*>(ot + li * KP + (32 * dt + 8 * g + 4 * hf) * 2) =
+            u32x2{w[0], w[1]};
       }
-    if (a.lse && hf == 0)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32 * DG / 64; ++i) {
+      const int c = i * 64 + lane, r = c / DG, col = c % DG;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(ot + r * KP + col * 16);
+      if (qw + r < Lq) *reinterpret_cast<u32x4*>(ob + int64_t(qw + r) * a.so[2] + col * 8) = w;
+    }
+    if (q_ok && a.lse && hf == 0)
       a.lse[it.lse + qi] =
           l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
