@@ -139,20 +139,34 @@ __device__ inline int tr_lane_offset(int lane, int pitch) {
   return (8 * (g16 >> 1) + e4) * pitch + (16 * (g16 & 1) + 4 * q4) * 2;
 }
 
-// Stores a 32 x D accumulator block set (registers 4g..4g+3 of block dt hold columns
-// 32dt + 8g + 4h + 0..3 of the lane's row) as one row of the 16-bit type E, multiplied by
-// `mul`.
-template <typename E, int D>
-__device__ inline void store_row(uint16_t* row, const f32x16 (&acc)[D / 32], float mul,
-                                 int hf) {
+// Stores a wave's 32 x D accumulator block set (registers 4g..4g+3 of block dt hold
+// columns 32dt + 8g + 4h + 0..3 of the lane's row), multiplied by `mul`, in the 16-bit type
+// E, through LDS so that the global stores cover whole rows: tile_to_lds puts the 32 rows
+// (pitch P bytes) into `ot`; after a workgroup barrier, rows_to_global stores them, lane l
+// taking 16-byte chunks l, l + 64, ... of the row-major tile, rows row0 + r < nrows only.
+template <typename E, int D, int P>
+__device__ inline void tile_to_lds(char* ot, const f32x16 (&acc)[D / 32], float mul, int li,
+                                   int hf) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t w0 = pack2<E>(acc[dt][4 * g] * mul, acc[dt][4 * g + 1] * mul);
       const uint32_t w1 = pack2<E>(acc[dt][4 * g + 2] * mul, acc[dt][4 * g + 3] * mul);
-      *reinterpret_cast<u32x2*>(row + 32 * dt + 8 * g + 4 * hf) = u32x2{w0, w1};
+      *reinterpret_cast<u32x2*>(ot + li * P + (32 * dt + 8 * g + 4 * hf) * 2) = u32x2{w0, w1};
     }
+}
+template <int D, int P>
+__device__ inline void rows_to_global(const char* ot, int lane, int row0, int nrows,
+                                      uint16_t* base, int64_t stride) {
+  constexpr int DG = D / 8;
+  static_assert((32 * DG) % 64 == 0, "row chunks split evenly over a wave");
+#pragma unroll
+  for (int i = 0; i < 32 * DG / 64; ++i) {
+    const int c = i * 64 + lane, r = c / DG, col = c % DG;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(ot + r * P + col * 16);
+    if (row0 + r < nrows) *reinterpret_cast<u32x4*>(base + int64_t(row0 + r) * stride + col * 8) = w;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -377,17 +391,24 @@ void bwd_dq(BwdArgs a) {
     }
   };
 
+  // Each tile is loaded right after its predecessor is written to LDS, a whole step
+  // before its own store.
   load(0);
   store(0);
+  load(1);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    load(t + 1);
     if (t < wtiles) compute(t);
     store((t + 1) & 1);
+    load(t + 2);
     __syncthreads();
   }
 
-  if (q_ok) store_row<E, D>(dqb + int64_t(qi) * a.sdq[2], dq, a.scale, hf);
+  static_assert(8 * 32 * RP <= 2 * STAGE, "the output tiles fit the LDS");
+  char* ot = lds + wave * 32 * RP;
+  tile_to_lds<E, D, RP>(ot, dq, a.scale, li, hf);
+  __syncthreads();
+  rows_to_global<D, RP>(ot, lane, qw, a.Lq, dqb, a.sdq[2]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -615,25 +636,34 @@ void bwd_dkdv(BwdArgs a) {
   // The two roles run separate loops with the same barriers, one per query tile, so that
   // the staging registers (P waves only) never count against the dS waves' products.  A
   // wave's keys are visible to some query of tile t iff the tile's last query + coff >= kw.
+  // The P waves load each tile right after its predecessor is written to LDS.
   if (!ds_wave) {
     load(tbeg);
     store(tbeg & 1);
+    load(tbeg + 1);
     __syncthreads();
     for (int t = tbeg; t < ntiles; ++t) {
-      load(t + 1);
       if (wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw)) compute(std::false_type{}, t);
       store((t + 1) & 1);
+      load(t + 2);
       __syncthreads();
     }
-    if (k_ok) store_row<E, D>(dvb + int64_t(kj) * a.sdv[2], acc, 1.f, hf);
   } else {
     __syncthreads();
     for (int t = tbeg; t < ntiles; ++t) {
       if (wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw)) compute(std::true_type{}, t);
       __syncthreads();
     }
-    if (k_ok) store_row<E, D>(dkb + int64_t(kj) * a.sdk[2], acc, a.scale, hf);
   }
+  // dV (P waves) and dK (dS waves) of the same 32 keys per SIMD, written as whole rows
+  static_assert(8 * 32 * RP <= 2 * STAGE, "the output tiles fit the LDS");
+  char* ot = lds + wave * 32 * RP;
+  tile_to_lds<E, D, RP>(ot, acc, ds_wave ? a.scale : 1.f, li, hf);
+  __syncthreads();
+  if (ds_wave)
+    rows_to_global<D, RP>(ot, lane, kw, a.Lk, dkb, a.sdk[2]);
+  else
+    rows_to_global<D, RP>(ot, lane, kw, a.Lk, dvb, a.sdv[2]);
 }
 
 template <typename E, int D, bool CAUSAL, bool MASK>
