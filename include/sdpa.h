@@ -55,7 +55,7 @@ enum sdpa_status {
   SDPA_ERR_RANK = 2,     /* rank not 3 or 4, or rank 3 with B != 1                       */
   SDPA_ERR_SHAPE = 3,    /* negative size, or a size/extent beyond the supported maximum */
   SDPA_ERR_HEAD_DIM = 4, /* D not a supported head dim (forward: 32, 64, 96, 128, 256;
-                            backward: 64, 128)                                         */
+                            backward: 32, 64, 96, 128)                                 */
   SDPA_ERR_DTYPE = 5,    /* dtype not an sdpa_dtype                                      */
   SDPA_ERR_STRIDE = 6,   /* innermost stride != 1, or a negative stride                  */
   SDPA_ERR_ALIGN = 7,    /* q/k/v/out base or row stride not 16-byte aligned, lse not 4  */
@@ -282,7 +282,7 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
  *   delta         device pointer to B*H*Lq contiguous floats of caller-owned scratch,
  *                 4-byte aligned; receives delta[i] above (fp32).  Required when
  *                 B*H*Lq > 0.
- *   rank, B..D    as in sdpa_fwd (D in {64, 128}); additionally (Lq + 64) times the row
+ *   rank, B..D    as in sdpa_fwd (D in {32, 64, 96, 128}); additionally (Lq + 64) times the row
  *                 stride of q (and of dout) must stay below 2 GiB.
  *   strides       9*rank element strides, tensor-major: q, k, v, out, dout, dq, dk, dv,
  *                 mask, each in its own axis order as in sdpa_fwd.

@@ -36,14 +36,15 @@ int canon_strides(int rank, const int64_t* s, int64_t out[4]) {
   return SDPA_OK;
 }
 
-// The backward's checks of the sizes, head dim (its kernels take 64 and 128) and scale.
+// The backward's checks of the sizes, head dim (its kernels take 32, 64, 96 and 128) and
+// scale.
 int check_sizes(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, float scale) {
   if (rank != 3 && rank != 4) return SDPA_ERR_RANK;
   if (rank == 3 && B != 1) return SDPA_ERR_RANK;
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return SDPA_ERR_SHAPE;
   if (Lq > kMaxDim || Lk > kMaxDim || B > kMaxDim || H > kMaxDim) return SDPA_ERR_SHAPE;
   if (B != 0 && H > kMaxDim / B) return SDPA_ERR_SHAPE;
-  if (D != 64 && D != 128) return SDPA_ERR_HEAD_DIM;
+  if (!sdpa::bwd_head_dim_ok(D)) return SDPA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
   return SDPA_OK;
 }
@@ -527,7 +528,7 @@ const char* sdpa_strerror(int status) {
       return "negative size, a size beyond the supported maximum, or one head's k/v rows "
              "spanning 2 GiB or more";
     case SDPA_ERR_HEAD_DIM:
-      return "head dim D must be 32, 64, 96, 128 or 256 (the backward: 64 or 128)";
+      return "head dim D must be 32, 64, 96, 128 or 256 (the backward: 32, 64, 96 or 128)";
     case SDPA_ERR_DTYPE:
       return "dtype must be SDPA_F32, SDPA_BF16 or SDPA_F16 (the backward: SDPA_BF16 or SDPA_F16)";
     case SDPA_ERR_STRIDE: return "innermost strides must be 1 and no stride may be negative";

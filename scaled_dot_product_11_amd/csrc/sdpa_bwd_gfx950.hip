@@ -169,6 +169,25 @@ __device__ inline void rows_to_global(const char* ot, int lane, int row0, int nr
   }
 }
 
+// Staging map of a streamed tile of R rows x DG 16-byte chunks over NT threads: chunk p of
+// thread tid is chunk tid + p * NT of the row-major tile, at byte offset off(p, pitch) for a
+// row pitch of `pitch` bytes (in global memory or LDS).  When the tile splits evenly
+// (NT a multiple of DG and of the tile) chunk p sits NT / DG rows below chunk 0; otherwise
+// (D = 32, 96) the chunks past the tile's end are skipped -- whole waves, since R * DG is a
+// multiple of 64.
+template <int R, int DG, int NT>
+struct StageMap {
+  static constexpr bool kEven = (R * DG) % NT == 0 && NT % DG == 0;
+  int tid, row0, col0;
+  __device__ explicit StageMap(int t) : tid(t), row0(t / DG), col0(t % DG) {}
+  __device__ bool ok(int p) const { return kEven || tid + p * NT < R * DG; }
+  __device__ int off(int p, int pitch) const {
+    if (kEven) return (row0 + p * (NT / DG)) * pitch + col0 * 16;
+    const int c = tid + p * NT;
+    return (c / DG) * pitch + (c % DG) * 16;
+  }
+};
+
 // ---------------------------------------------------------------------------------------
 // dq kernel.  Workgroup: 256 query rows of one (b, h) in 8 waves, two per SIMD, so that
 // one wave's vector work and operand reads overlap the other's products; wave w owns
@@ -188,14 +207,12 @@ void bwd_dq(BwdArgs a) {
   constexpr int BN = kBwdStep;
   constexpr int NT = kThreadsBwdQ;
   constexpr int DG = D / 8;           // 16-byte chunks per row
-  constexpr int CH = BN * DG / NT;    // chunks per thread per tile
-  constexpr int ROWS = NT / DG;       // tile rows covered by one chunk pass
+  constexpr int CH = (BN * DG + NT - 1) / NT;  // chunks per thread per tile
   constexpr int RP = k_pitch_bf16(D); // row-read pitch (bytes)
   constexpr int TP = v_pitch_bf16(D); // transposed-read pitch (bytes)
   constexpr int OFF_KT = BN * RP;
   constexpr int OFF_V = OFF_KT + BN * TP;
   constexpr int STAGE = OFF_V + BN * RP;
-  static_assert(CH * NT == BN * DG, "tile must split evenly over the workgroup");
   static_assert(2 * STAGE == lds_bytes_bwd_dq(D), "plan and kernel disagree on LDS");
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
@@ -261,29 +278,27 @@ void bwd_dq(BwdArgs a) {
   const int v_ext = a.Lk > 0 ? (a.Lk - 1) * v_rowb + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, k_ext, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, v_ext, kBufferFlags);
-  const int ld_row = tid / DG, ld_col = tid % DG;
-  const int k_goff = ld_row * k_rowb + ld_col * 16;
-  const int v_goff = ld_row * v_rowb + ld_col * 16;
-  const int r_soff = ld_row * RP + ld_col * 16;
-  const int t_soff = ld_row * TP + ld_col * 16;
+  const StageMap<BN, DG, NT> sm_(tid);
   u32x4 kreg[CH], vreg[CH];
   auto load = [&](int t) {
-    const int kbase = k_goff + (t < ntiles ? t * BN * k_rowb : k_ext);
-    const int vbase = v_goff + (t < ntiles ? t * BN * v_rowb : v_ext);
+    const int kbase = t < ntiles ? t * BN * k_rowb : k_ext;
+    const int vbase = t < ntiles ? t * BN * v_rowb : v_ext;
 #pragma unroll
-    for (int p = 0; p < CH; ++p) {
-      kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, kbase + p * ROWS * k_rowb, 0, 0);
-      vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vbase + p * ROWS * v_rowb, 0, 0);
-    }
+    for (int p = 0; p < CH; ++p)
+      if (sm_.ok(p)) {
+        kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, kbase + sm_.off(p, k_rowb), 0, 0);
+        vreg[p] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vbase + sm_.off(p, v_rowb), 0, 0);
+      }
   };
   auto store = [&](int st) {
     char* s = lds + st * STAGE;
 #pragma unroll
-    for (int p = 0; p < CH; ++p) {
-      *reinterpret_cast<u32x4*>(s + r_soff + p * ROWS * RP) = kreg[p];
-      *reinterpret_cast<u32x4*>(s + OFF_KT + t_soff + p * ROWS * TP) = kreg[p];
-      *reinterpret_cast<u32x4*>(s + OFF_V + r_soff + p * ROWS * RP) = vreg[p];
-    }
+    for (int p = 0; p < CH; ++p)
+      if (sm_.ok(p)) {
+        *reinterpret_cast<u32x4*>(s + sm_.off(p, RP)) = kreg[p];
+        *reinterpret_cast<u32x4*>(s + OFF_KT + sm_.off(p, TP)) = kreg[p];
+        *reinterpret_cast<u32x4*>(s + OFF_V + sm_.off(p, RP)) = vreg[p];
+      }
   };
 
   const int rfrag = perm5(li) * RP + hf * 16;  // left-operand row of this lane
@@ -435,8 +450,7 @@ void bwd_dkdv(BwdArgs a) {
   constexpr int BQ = kBwdStep;
   constexpr int NT = kThreadsBwdK / 2;  // the P waves stage the tiles
   constexpr int DG = D / 8;
-  constexpr int CH = BQ * DG / NT;
-  constexpr int ROWS = NT / DG;
+  constexpr int CH = (BQ * DG + NT - 1) / NT;
   constexpr int RP = k_pitch_bf16(D);
   constexpr int TP = v_pitch_bf16(D);
   constexpr int OFF_QT = BQ * RP;
@@ -445,7 +459,6 @@ void bwd_dkdv(BwdArgs a) {
   constexpr int OFF_LSE = OFF_DT + BQ * TP;
   constexpr int OFF_DEL = OFF_LSE + 4 * BQ;
   constexpr int STAGE = OFF_DEL + 4 * BQ;
-  static_assert(CH * NT == BQ * DG, "tile must split evenly over the workgroup");
   static_assert(2 * STAGE == lds_bytes_bwd_dkdv(D), "plan and kernel disagree on LDS");
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
 
@@ -503,22 +516,19 @@ void bwd_dkdv(BwdArgs a) {
   const int d_ext = a.Lq > 0 ? (a.Lq - 1) * d_rowb + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qb, 0, q_ext, kBufferFlags);
   const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, d_ext, kBufferFlags);
-  const int ld_row = tid / DG, ld_col = tid % DG;
-  const int q_goff = ld_row * q_rowb + ld_col * 16;
-  const int d_goff = ld_row * d_rowb + ld_col * 16;
-  const int r_soff = ld_row * RP + ld_col * 16;
-  const int t_soff = ld_row * TP + ld_col * 16;
+  const StageMap<BQ, DG, NT> sm_(tid);  // the P waves' threads, tid < NT
   u32x4 qreg[CH], dreg[CH];
   float rowval = 0.f;  // threads 0..63: lse2 of row tid; 64..127: delta of row tid - 64
   auto load = [&](int t) {
     const bool live = t < ntiles;
-    const int qbase = q_goff + (live ? t * BQ * q_rowb : q_ext);
-    const int dbase = d_goff + (live ? t * BQ * d_rowb : d_ext);
+    const int qbase = live ? t * BQ * q_rowb : q_ext;
+    const int dbase = live ? t * BQ * d_rowb : d_ext;
 #pragma unroll
-    for (int p = 0; p < CH; ++p) {
-      qreg[p] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qbase + p * ROWS * q_rowb, 0, 0);
-      dreg[p] = __builtin_amdgcn_raw_buffer_load_b128(drs, dbase + p * ROWS * d_rowb, 0, 0);
-    }
+    for (int p = 0; p < CH; ++p)
+      if (sm_.ok(p)) {
+        qreg[p] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qbase + sm_.off(p, q_rowb), 0, 0);
+        dreg[p] = __builtin_amdgcn_raw_buffer_load_b128(drs, dbase + sm_.off(p, d_rowb), 0, 0);
+      }
     if (tid < 2 * BQ) {
       const int row = t * BQ + (tid & (BQ - 1));
       const bool ok = live && row < a.Lq;
@@ -529,12 +539,13 @@ void bwd_dkdv(BwdArgs a) {
   auto store = [&](int st) {
     char* s = lds + st * STAGE;
 #pragma unroll
-    for (int p = 0; p < CH; ++p) {
-      *reinterpret_cast<u32x4*>(s + r_soff + p * ROWS * RP) = qreg[p];
-      *reinterpret_cast<u32x4*>(s + OFF_QT + t_soff + p * ROWS * TP) = qreg[p];
-      *reinterpret_cast<u32x4*>(s + OFF_DR + r_soff + p * ROWS * RP) = dreg[p];
-      *reinterpret_cast<u32x4*>(s + OFF_DT + t_soff + p * ROWS * TP) = dreg[p];
-    }
+    for (int p = 0; p < CH; ++p)
+      if (sm_.ok(p)) {
+        *reinterpret_cast<u32x4*>(s + sm_.off(p, RP)) = qreg[p];
+        *reinterpret_cast<u32x4*>(s + OFF_QT + sm_.off(p, TP)) = qreg[p];
+        *reinterpret_cast<u32x4*>(s + OFF_DR + sm_.off(p, RP)) = dreg[p];
+        *reinterpret_cast<u32x4*>(s + OFF_DT + sm_.off(p, TP)) = dreg[p];
+      }
     if (tid < 2 * BQ) reinterpret_cast<float*>(s + OFF_LSE)[tid] = rowval;
   };
 
@@ -728,10 +739,18 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const unsigned gk = unsigned(int64_t(a.k_items) * a.bh_count);
   const bool causal = p.causal != 0;
   if (p.dtype == 2)
-    return p.D == 64 ? launch_bwd_d<_Float16, 64>(a, causal, gq, gk, stream)
-                     : launch_bwd_d<_Float16, 128>(a, causal, gq, gk, stream);
-  return p.D == 64 ? launch_bwd_d<__bf16, 64>(a, causal, gq, gk, stream)
-                   : launch_bwd_d<__bf16, 128>(a, causal, gq, gk, stream);
+    switch (p.D) {
+      case 32: return launch_bwd_d<_Float16, 32>(a, causal, gq, gk, stream);
+      case 64: return launch_bwd_d<_Float16, 64>(a, causal, gq, gk, stream);
+      case 96: return launch_bwd_d<_Float16, 96>(a, causal, gq, gk, stream);
+      default: return launch_bwd_d<_Float16, 128>(a, causal, gq, gk, stream);
+    }
+  switch (p.D) {
+    case 32: return launch_bwd_d<__bf16, 32>(a, causal, gq, gk, stream);
+    case 64: return launch_bwd_d<__bf16, 64>(a, causal, gq, gk, stream);
+    case 96: return launch_bwd_d<__bf16, 96>(a, causal, gq, gk, stream);
+    default: return launch_bwd_d<__bf16, 128>(a, causal, gq, gk, stream);
+  }
 }
 
 }  // namespace sdpa

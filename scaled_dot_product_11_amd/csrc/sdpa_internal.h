@@ -20,10 +20,12 @@ constexpr int kBlockNBf16 = 64;
 constexpr int kThreadsF32 = 256;
 constexpr int kBlockMF32 = 128;
 constexpr int kBlockNF32 = 64;
-// Head dims of the forward kernels (every dtype); the backward takes 64 and 128.
+// Head dims of the forward kernels (every dtype) and of the backward kernels (at D = 256
+// the backward's accumulators and operands exceed two waves' registers per SIMD).
 constexpr bool fwd_head_dim_ok(int64_t D) {
   return D == 32 || D == 64 || D == 96 || D == 128 || D == 256;
 }
+constexpr bool bwd_head_dim_ok(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 // Phase groups of the 16-bit kernel at head dim D (2: paired waves alternate phases).
 constexpr int groups_16(int D) { return D <= 128 ? 2 : 1; }
 // dtype: 0 = fp32, 1 = bf16, 2 = fp16 (the values of sdpa_dtype); both 16-bit types run

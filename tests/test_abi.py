@@ -289,7 +289,10 @@ def test_bwd_check_valid_and_rank3():
 def test_bwd_check_errors():
     assert bcheck(**bargs(dtype=sd.SDPA_F32)) == DTYPE  # the backward is 16-bit only
     assert bcheck(**bargs(dtype=sd.SDPA_F16)) == OK
-    assert bcheck(**bargs(D=96)) == HEAD
+    assert bcheck(**bargs(D=96)) == OK
+    assert bcheck(**bargs(D=32)) == OK
+    assert bcheck(**bargs(D=256)) == HEAD  # the forward takes 256, the backward does not
+    assert bcheck(**bargs(D=80)) == HEAD
     assert bcheck(**bargs(rank=5)) == RANK
     assert bcheck(**bargs(Lq=-1)) == SHAPE
     assert bcheck(**bargs(scale=float("nan"))) == SCALE
@@ -326,9 +329,9 @@ def test_bwd_check_empty_sides():
 def test_bwd_rejects_before_any_device_call():
     import ctypes
     lib = sd.load_library()
-    a = bargs(D=96)
+    a = bargs(D=256)
     arr = (ctypes.c_int64 * 36)(*a["strides"])
-    st = lib.sdpa_bwd(*a["ptrs"], 4, 2, 3, 100, 90, 96, arr, 0.125, 1, None, 1, None)
+    st = lib.sdpa_bwd(*a["ptrs"], 4, 2, 3, 100, 90, 256, arr, 0.125, 1, None, 1, None)
     assert st == HEAD
     st = lib.sdpa_bwd(*([None] * 10), 4, 0, 3, 100, 90, 64, arr, 0.125, 1, None, 1, None)
     assert st == OK  # B == 0: nothing to do

@@ -87,7 +87,7 @@ SHAPES = [(1, 1), (33, 33), (64, 64), (127, 127), (129, 129), (200, 200), (77, 3
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
 @pytest.mark.parametrize("mode", ["none", "causal", "mask", "causal_mask", "bcast_mask"])
 def test_bwd_ragged_small(dtype, D, mode):
     causal = "causal" in mode
@@ -163,7 +163,7 @@ def test_bwd_invalid_arguments_raise():
         f = [t.float() for t in (qd, kd, vd, out)]
         sdpa_bwd(*f[:3], f[3], f[3], lse)
     with pytest.raises(SdpaError, match="SDPA_ERR_HEAD_DIM"):
-        z = torch.zeros(1, 1, 8, 32, dtype=torch.bfloat16, device=DEV)
+        z = torch.zeros(1, 1, 8, 256, dtype=torch.bfloat16, device=DEV)
         sdpa_bwd(z, z, z, z, z, lse)
 
 
