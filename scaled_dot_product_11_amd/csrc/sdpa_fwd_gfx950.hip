@@ -11,8 +11,9 @@
 // backend's safe softmax).
 //
 // Work decomposition (16-bit and fp32 kernels alike):
-//   * a workgroup owns a tile of query rows of one (b, h): 256 rows in 8 waves (bf16, fp16) or
-//     128 rows in 4 waves (fp32); each wave owns 32 query rows;
+//   * a workgroup owns a tile of query rows of one (b, h): 256 rows in 8 waves (bf16, fp16;
+//     128 rows in 4 waves at D = 256) or 128 rows in 4 waves (fp32); each wave owns 32 query
+//     rows;
 //   * lane l serves query row (l % 32) and half h = l / 32 of every key tile, so all
 //     per-row softmax state (running max, running sum, rescale factor) is a per-lane
 //     scalar;
@@ -20,9 +21,10 @@
 //     accumulator of a 32x32 tile gives each lane 16 keys of its own query row;
 //   * the output is accumulated transposed, O^T += V^T . P^T, so P^T comes straight from
 //     the score registers and each lane again owns its query's column;
-//   * K and V tiles of 64 keys are double-buffered through LDS: the global loads of the
-//     next tiles are issued before the matrix work on the current ones and written to
-//     the other LDS stage after it.
+//   * K and V tiles of 64 keys are double-buffered through LDS: each tile is loaded from
+//     global memory a whole key step before it is written to the other LDS stage;
+//   * the output tile of each wave goes through LDS at the end, so that its global stores
+//     cover whole rows.
 #include <math.h>
 
 
