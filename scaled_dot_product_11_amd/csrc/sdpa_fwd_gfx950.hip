@@ -232,18 +232,17 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
 
 // MK: 0 no mask, 1 boolean mask, 2 additive mask (POS is then false: the scale is applied
 // to the scores before the bias is added).
-template <typename E, int D, bool CAUSAL, int MK, bool POS, int MODE>
-__global__ __launch_bounds__(256 * groups_16(D))
-__attribute__((amdgpu_waves_per_eu(groups_16(D), groups_16(D))))
+template <typename E, int D, bool CAUSAL, int MK, bool POS, int MODE, int G = groups_16(D)>
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(waves_16(D), waves_16(D))))
 void fwd_mfma(Args a) {
   constexpr bool MASK = MK == 1, BIAS = MK == 2;
   static_assert(!(BIAS && POS), "an additive mask needs the scores scaled first");
   typedef typename Vec16<E>::v8 v8;
   typedef typename Vec16<E>::v2 v2;
-  constexpr int G = groups_16(D);          // phase groups (waves per SIMD)
+  static_assert(G == 1 || G == 2, "one or two phase groups");
   constexpr int BN = kBlockNBf16;
-  constexpr int BM = block_m(1, D);        // query rows per workgroup
-  constexpr int NT = block_threads(1, D);
+  constexpr int BM = 128 * G;              // query rows per workgroup
+  constexpr int NT = 256 * G;
   constexpr int DG = D / 8;                // 16-byte chunks per row
   constexpr int CH = (BN * DG + NT - 1) / NT;  // chunks per thread per K (or V) tile
   constexpr bool CH_FULL = CH * NT == BN * DG;  // every thread stages CH chunks
@@ -995,11 +994,23 @@ __global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int
 }
 
 template <int D, bool CAUSAL, int MK, int MODE>
-hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
+hipError_t launch(const Args& a, int dtype, int groups, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Args*>(&a)};
   const void* fn;
   constexpr bool POS_OK = MK != 2;  // an additive mask takes the explicitly scaled path
   const bool pos = POS_OK && a.scale_log2 > 0.f;
+  // the one-group tile for small causal problems (see fwd_groups)
+  if constexpr (CAUSAL && MK != 1 && MODE == kDense && D <= 128) {
+    if (groups == 1 && dtype != 0) {
+      if (dtype == 1)
+        fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, POS_OK, MODE, 1>)
+                 : reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, false, MODE, 1>);
+      else
+        fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MK, POS_OK, MODE, 1>)
+                 : reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MK, false, MODE, 1>);
+      return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream);
+    }
+  }
   if (dtype == 1)
     fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, POS_OK, MODE>)
              : reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, false, MODE>);
@@ -1012,19 +1023,19 @@ hipError_t launch(const Args& a, int dtype, unsigned grid, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t launch_d(const Args& a, int dtype, bool causal, int mode, unsigned grid,
+hipError_t launch_d(const Args& a, int dtype, int groups, bool causal, int mode, unsigned grid,
                     hipStream_t s) {
   if (mode == kVarlen)  // packed sequences take no mask
-    return causal ? launch<D, true, 0, kVarlen>(a, dtype, grid, s)
-                  : launch<D, false, 0, kVarlen>(a, dtype, grid, s);
+    return causal ? launch<D, true, 0, kVarlen>(a, dtype, groups, grid, s)
+                  : launch<D, false, 0, kVarlen>(a, dtype, groups, grid, s);
   if (mode == kSplit)  // neither do split keys
-    return causal ? launch<D, true, 0, kSplit>(a, dtype, grid, s)
-                  : launch<D, false, 0, kSplit>(a, dtype, grid, s);
+    return causal ? launch<D, true, 0, kSplit>(a, dtype, groups, grid, s)
+                  : launch<D, false, 0, kSplit>(a, dtype, groups, grid, s);
   if (a.mask)
-    return causal ? launch<D, true, 1, kDense>(a, dtype, grid, s) : launch<D, false, 1, kDense>(a, dtype, grid, s);
+    return causal ? launch<D, true, 1, kDense>(a, dtype, groups, grid, s) : launch<D, false, 1, kDense>(a, dtype, groups, grid, s);
   if (a.bias)
-    return causal ? launch<D, true, 2, kDense>(a, dtype, grid, s) : launch<D, false, 2, kDense>(a, dtype, grid, s);
-  return causal ? launch<D, true, 0, kDense>(a, dtype, grid, s) : launch<D, false, 0, kDense>(a, dtype, grid, s);
+    return causal ? launch<D, true, 2, kDense>(a, dtype, groups, grid, s) : launch<D, false, 2, kDense>(a, dtype, groups, grid, s);
+  return causal ? launch<D, true, 0, kDense>(a, dtype, groups, grid, s) : launch<D, false, 0, kDense>(a, dtype, groups, grid, s);
 }
 
 template <int D>
@@ -1064,7 +1075,10 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.Lk = int32_t(p.Lk);
   // dense: B*H heads of Lq rows; packed: nseq*H heads of up to max_seqlen_q rows
   const int64_t rows = p.varlen ? p.max_seqlen_q : p.Lq;
-  const int bm = block_m(p.dtype, int(p.D));
+  const int mode = p.varlen ? kVarlen : p.nsplit > 0 ? kSplit : kDense;
+  const int groups = fwd_groups(p.dtype, p.D, p.causal != 0, p.mask != nullptr, mode == kDense,
+                                p.B * p.H, p.Lq);
+  const int bm = p.dtype != 0 ? 128 * groups : kBlockMF32;
   a.q_tiles = int32_t((rows + bm - 1) / bm);
   a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);
   a.scale_log2 = p.scale * kLog2e;
@@ -1076,17 +1090,16 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   a.ws_o = p.ws_o;
   a.ws_lse = p.ws_lse;
   a.split_len = int32_t(p.split_len);
-  const int mode = p.varlen ? kVarlen : p.nsplit > 0 ? kSplit : kDense;
   const unsigned grid =
       unsigned(int64_t(a.q_tiles) * a.bh_count * (mode == kSplit ? p.nsplit : 1));
   const bool causal = p.causal != 0;
   hipError_t e;
   switch (p.D) {
-    case 32: e = launch_d<32>(a, p.dtype, causal, mode, grid, stream); break;
-    case 64: e = launch_d<64>(a, p.dtype, causal, mode, grid, stream); break;
-    case 96: e = launch_d<96>(a, p.dtype, causal, mode, grid, stream); break;
-    case 128: e = launch_d<128>(a, p.dtype, causal, mode, grid, stream); break;
-    case 256: e = launch_d<256>(a, p.dtype, causal, mode, grid, stream); break;
+    case 32: e = launch_d<32>(a, p.dtype, groups, causal, mode, grid, stream); break;
+    case 64: e = launch_d<64>(a, p.dtype, groups, causal, mode, grid, stream); break;
+    case 96: e = launch_d<96>(a, p.dtype, groups, causal, mode, grid, stream); break;
+    case 128: e = launch_d<128>(a, p.dtype, groups, causal, mode, grid, stream); break;
+    case 256: e = launch_d<256>(a, p.dtype, groups, causal, mode, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || mode != kSplit) return e;

@@ -14,8 +14,6 @@ namespace sdpa {
 // gets at two waves per SIMD, so the workgroup is 4 waves (128 rows), one per SIMD, each
 // running its matrix and vector work in turn.  fp32 kernel: 4 waves, 32 rows each (128
 // per workgroup), 64 keys at a time.
-constexpr int kThreadsBf16 = 512;
-constexpr int kBlockMBf16 = 256;
 constexpr int kBlockNBf16 = 64;
 constexpr int kThreadsF32 = 256;
 constexpr int kBlockMF32 = 128;
@@ -28,12 +26,31 @@ constexpr bool fwd_head_dim_ok(int64_t D) {
 constexpr bool bwd_head_dim_ok(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
 // Phase groups of the 16-bit kernel at head dim D (2: paired waves alternate phases).
 constexpr int groups_16(int D) { return D <= 128 ? 2 : 1; }
+// Waves per SIMD of a 16-bit workgroup of G groups: two (one per group, or one from each of
+// two co-resident one-group workgroups) up to D = 128, else one.
+constexpr int waves_16(int D) { return D <= 128 ? 2 : 1; }
 // dtype: 0 = fp32, 1 = bf16, 2 = fp16 (the values of sdpa_dtype); both 16-bit types run
 // the same matrix-core kernel and tiles
 constexpr int block_m(int dtype, int D) { return dtype != 0 ? 128 * groups_16(D) : kBlockMF32; }
 constexpr int block_n(int dtype) { return dtype != 0 ? kBlockNBf16 : kBlockNF32; }
 constexpr int block_threads(int dtype, int D) {
   return dtype != 0 ? 256 * groups_16(D) : kThreadsF32;
+}
+
+// Phase groups of a dense 16-bit launch.  A causal problem without a boolean mask (an
+// additive one is allowed) whose 256-row work items are no more than the chip's 256 CUs runs
+// one item per CU, and its time is that of
+// the last query tile of a head, which walks every key tile; with 128-row items of one group
+// (one wave per SIMD), there are twice as many shorter items and two workgroups share a CU,
+// their matrix and vector work overlapping unsynchronised.  Every other problem keeps the
+// two-group tile of groups_16(D).
+constexpr int64_t kSmallProblemItems = 256;
+constexpr int fwd_groups(int dtype, int64_t D, bool causal, bool masked, bool dense,
+                         int64_t bh, int64_t Lq) {
+  return dtype != 0 && causal && !masked && dense && D <= 128 &&
+                 bh * ((Lq + 255) / 256) <= kSmallProblemItems
+             ? 1
+             : (dtype != 0 ? groups_16(int(D)) : 1);
 }
 
 // Rank-3 [N,L,D] and rank-4 [B,H,L,D] inputs both become this (b, h, row, col) view;
