@@ -44,11 +44,16 @@ constexpr int block_threads(int dtype, int D) {
 // (one wave per SIMD), there are twice as many shorter items and two workgroups share a CU,
 // their matrix and vector work overlapping unsynchronised.  Every other problem keeps the
 // two-group tile of groups_16(D).
+// Split-key launches of decode shapes (at most 128 query rows) take the one-group tile too:
+// their workgroups stream K and V for a single live query tile, and two of them per CU keep
+// twice as many tile loads in flight.
 constexpr int64_t kSmallProblemItems = 256;
+constexpr int64_t kDecodeRows = 128;
 constexpr int fwd_groups(int dtype, int64_t D, bool causal, bool masked, bool dense,
-                         int64_t bh, int64_t Lq) {
-  return dtype != 0 && causal && !masked && dense && D <= 128 &&
-                 bh * ((Lq + 255) / 256) <= kSmallProblemItems
+                         int64_t bh, int64_t Lq, bool split = false) {
+  return dtype != 0 && D <= 128 && !masked &&
+                 ((causal && dense && bh * ((Lq + 255) / 256) <= kSmallProblemItems) ||
+                  (split && Lq <= kDecodeRows))
              ? 1
              : (dtype != 0 ? groups_16(int(D)) : 1);
 }
