@@ -194,6 +194,24 @@ def test_no_keys_and_no_queries():
     assert out.shape == (1, 2, 0, 64)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [1, 2], ids=["top_left", "bottom_right"])
+def test_causal_with_no_keys(dtype, causal):
+    """Causal problems with no keys (the one-group tile for 16-bit inputs): every row is
+    empty, so out = 0 and lse = -inf, also with an additive mask."""
+    q = torch.randn(2, 3, 70, 128, device=DEV).to(dtype)
+    kv = torch.empty(2, 3, 0, 128, device=DEV, dtype=dtype)
+    out = torch.full(q.shape, float("nan"), device=DEV, dtype=dtype)
+    out, lse = sdpa_fwd(q, kv, kv, out, is_causal=causal)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(lse == -math.inf)
+    bias = torch.zeros(1, 1, 70, 0, device=DEV)
+    out2, lse2 = sdpa_fwd_bias(q, kv, kv, bias, is_causal=causal)
+    torch.cuda.synchronize()
+    assert torch.all(out2 == 0) and torch.all(lse2 == -math.inf)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.3, 2.0])
 def test_unusual_scales(scale):
     q, k, v, _ = rand_inputs(31, 1, 2, 90, 90, 64, torch.bfloat16)
