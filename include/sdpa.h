@@ -308,13 +308,13 @@ int sdpa_bwd_check(const void* q, const void* k, const void* v, const void* out,
                    int is_causal, const uint8_t* mask, int dtype);
 
 /*
- * Launch plan (host-only introspection of the tile scheduler of sdpa_fwd, for a launch
- * without a boolean mask; sdpa_fwd_bias takes the same tiles).
+ * Launch plan (host-only introspection of the tile scheduler of sdpa_fwd; sdpa_fwd_bias
+ * takes the same tiles).
  *
  * A work item is one (b*H + h, query tile) pair: block_m query rows of one head, which
  * walk the key/value tiles of block_n keys.  16-bit inputs: 256 rows and 512 threads (two
  * waves per SIMD in alternating matrix / vector phases) up to D = 128, 128 rows and 256
- * threads at D = 256 and for causal problems with at most 256 items of 256 rows (then two
+ * threads at D = 256 and for problems with at most 256 items of 256 rows (then two
  * workgroups share a CU); fp32: 128 rows, 256 threads.  With is_causal the items are issued
  * heaviest-first (last query tile of every head first), so the long items start early
  * and the short ones fill the tail.  Without it the items are issued query-tile-major

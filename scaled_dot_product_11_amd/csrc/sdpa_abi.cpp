@@ -555,8 +555,8 @@ int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
   const int st = normalise(dummy, dummy, dummy, dummy, nullptr, rank, B, H, Lq, Lk, D, strides,
                            1.0f, is_causal, nullptr, dtype, nullptr);
   if (st != SDPA_OK) return st;
-  // the launch without a boolean mask: small causal 16-bit problems take the one-group tile
-  const int groups = sdpa::fwd_groups(dtype, D, is_causal != 0, false, true, B * H, Lq);
+  // small 16-bit problems take the one-group tile
+  const int groups = sdpa::fwd_groups(dtype, D, true, B * H, Lq, false);
   plan->block_m = dtype != SDPA_F32 ? 128 * groups : sdpa::block_m(dtype, int(D));
   plan->block_n = sdpa::block_n(dtype);
   plan->threads = dtype != SDPA_F32 ? 256 * groups : sdpa::block_threads(dtype, int(D));

@@ -999,8 +999,8 @@ hipError_t launch(const Args& a, int dtype, int groups, unsigned grid, hipStream
   const void* fn;
   constexpr bool POS_OK = MK != 2;  // an additive mask takes the explicitly scaled path
   const bool pos = POS_OK && a.scale_log2 > 0.f;
-  // the one-group tile for small causal problems and decode-shaped split keys (fwd_groups)
-  if constexpr (((CAUSAL && MK != 1 && MODE == kDense) || MODE == kSplit) && D <= 128) {
+  // the one-group tile for small dense problems and decode-shaped split keys (fwd_groups)
+  if constexpr ((MODE == kDense || MODE == kSplit) && D <= 128) {
     if (groups == 1 && dtype != 0) {
       if (dtype == 1)
         fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, POS_OK, MODE, 1>)
@@ -1076,8 +1076,7 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   // dense: B*H heads of Lq rows; packed: nseq*H heads of up to max_seqlen_q rows
   const int64_t rows = p.varlen ? p.max_seqlen_q : p.Lq;
   const int mode = p.varlen ? kVarlen : p.nsplit > 0 ? kSplit : kDense;
-  const int groups = fwd_groups(p.dtype, p.D, p.causal != 0, p.mask != nullptr, mode == kDense,
-                                p.B * p.H, p.Lq, mode == kSplit);
+  const int groups = fwd_groups(p.dtype, p.D, mode == kDense, p.B * p.H, p.Lq, mode == kSplit);
   const int bm = p.dtype != 0 ? 128 * groups : kBlockMF32;
   a.q_tiles = int32_t((rows + bm - 1) / bm);
   a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);

@@ -37,22 +37,20 @@ constexpr int block_threads(int dtype, int D) {
   return dtype != 0 ? 256 * groups_16(D) : kThreadsF32;
 }
 
-// Phase groups of a dense 16-bit launch.  A causal problem without a boolean mask (an
-// additive one is allowed) whose 256-row work items are no more than the chip's 256 CUs runs
-// one item per CU, and its time is that of
-// the last query tile of a head, which walks every key tile; with 128-row items of one group
-// (one wave per SIMD), there are twice as many shorter items and two workgroups share a CU,
-// their matrix and vector work overlapping unsynchronised.  Every other problem keeps the
-// two-group tile of groups_16(D).
-// Split-key launches of decode shapes (at most 128 query rows) take the one-group tile too:
-// their workgroups stream K and V for a single live query tile, and two of them per CU keep
-// twice as many tile loads in flight.
+// Phase groups of a 16-bit launch.  A dense problem whose 256-row work items are no more than
+// the chip's 256 CUs runs one item per CU, and its time is that of its longest item (under a
+// causal mask, the last query tile of a head, which walks every key tile).  With 128-row
+// items of one group (one wave per SIMD) there are twice as many shorter items and two
+// workgroups share a CU, their matrix and vector work overlapping unsynchronised.  Split-key
+// launches of decode shapes (at most 128 query rows) take that tile too: their workgroups
+// stream K and V for a single live query tile, and two of them per CU keep twice as many
+// tile loads in flight.  Every other launch keeps the two-group tile of groups_16(D).
 constexpr int64_t kSmallProblemItems = 256;
 constexpr int64_t kDecodeRows = 128;
-constexpr int fwd_groups(int dtype, int64_t D, bool causal, bool masked, bool dense,
-                         int64_t bh, int64_t Lq, bool split = false) {
-  return dtype != 0 && D <= 128 && !masked &&
-                 ((causal && dense && bh * ((Lq + 255) / 256) <= kSmallProblemItems) ||
+constexpr int fwd_groups(int dtype, int64_t D, bool dense, int64_t bh, int64_t Lq,
+                         bool split) {
+  return dtype != 0 && D <= 128 &&
+                 ((dense && bh * ((Lq + 255) / 256) <= kSmallProblemItems) ||
                   (split && Lq <= kDecodeRows))
              ? 1
              : (dtype != 0 ? groups_16(int(D)) : 1);

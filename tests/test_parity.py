@@ -117,28 +117,34 @@ def test_ragged_small(dtype, D, mode):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("D", [32, 64, 96, 128])
-def test_small_causal_tile_equals_two_group_tile(dtype, D):
-    """Causal problems (no boolean mask) with at most 256 items of 256 rows run 128-row,
-    one-group workgroups; larger ones the 256-row, two-group tile.  Both give each 32-row slice the same sequence of
+def test_small_problem_tile_equals_two_group_tile(dtype, D):
+    """Problems with at most 256 items of 256 rows run 128-row, one-group workgroups; larger
+    ones the 256-row, two-group tile.  Both give each 32-row slice the same sequence of
     operations, so heads 0..1 computed as a 2-head problem (one-group tile) and inside a
-    260-head problem (two-group tile) agree bit for bit, and both match the oracle."""
+    260-head problem (two-group tile) agree bit for bit, and both match the oracle: no mask,
+    both causal alignments, a boolean mask broadcast over heads, an additive mask."""
     for n, (Lq, Lk) in enumerate([(33, 33), (129, 200), (300, 77), (300, 300)]):
         g = torch.Generator().manual_seed(4100 + n + D)
         q, k, v = W.draw_qkv(g, (1, 260, Lq, D), (1, 260, Lk, D), dtype=dtype)
-        for mode in (1, 2):
-            big_o, big_l = sdpa_fwd(to_dev(q), to_dev(k), to_dev(v), is_causal=mode)
+        bmask = torch.rand((1, 1, Lq, Lk), generator=g) < 0.3
+        bmask[..., Lq // 2, :] = False  # one fully hidden row
+        for mode in (0, 1, 2, "mask"):
+            causal = 0 if mode == "mask" else mode
+            m = to_dev(bmask) if mode == "mask" else None
+            big_o, big_l = sdpa_fwd(to_dev(q), to_dev(k), to_dev(v), mask=m, is_causal=causal)
             small_o, small_l = sdpa_fwd(to_dev(q[:, :2].contiguous()), to_dev(k[:, :2].contiguous()),
-                                        to_dev(v[:, :2].contiguous()), is_causal=mode)
+                                        to_dev(v[:, :2].contiguous()), mask=m, is_causal=causal)
             torch.cuda.synchronize()
-            where = f"D={D} Lq={Lq} Lk={Lk} causal={mode}"
+            where = f"D={D} Lq={Lq} Lk={Lk} mode={mode}"
             assert torch.equal(big_o[:, :2], small_o) and torch.equal(big_l[:, :2], small_l), where
             heads = [0, 1, 131, 259]
             rows = np.concatenate([h * Lq + np.arange(Lq) for h in heads]).astype(np.int64)
-            if mode == 1:
-                ro, rl = sdpa_oracle(q, k, v, is_causal=True, rows=rows)
-            else:
+            if mode == 2:
                 tri = torch.ones(Lq, Lk, dtype=torch.bool).tril(Lk - Lq)
                 ro, rl = sdpa_oracle(q, k, v, mask=tri, rows=rows)
+            else:
+                ro, rl = sdpa_oracle(q, k, v, mask=bmask if mode == "mask" else None,
+                                     is_causal=mode == 1, rows=rows)
             idx = torch.from_numpy(rows).to(DEV)
             compare(big_o.reshape(-1, D)[idx], big_l.reshape(-1)[idx], ro, rl, dtype, where)
         # an additive mask broadcast over heads takes the same two tiles
