@@ -37,20 +37,23 @@ constexpr int block_threads(int dtype, int D) {
   return dtype != 0 ? 256 * groups_16(D) : kThreadsF32;
 }
 
-// Phase groups of a 16-bit launch.  A dense problem whose 256-row work items are no more than
-// the chip's 256 CUs runs one item per CU, and its time is that of its longest item (under a
-// causal mask, the last query tile of a head, which walks every key tile).  With 128-row
-// items of one group (one wave per SIMD) there are twice as many shorter items and two
-// workgroups share a CU, their matrix and vector work overlapping unsynchronised.  Split-key
-// launches of decode shapes (at most 128 query rows) take that tile too: their workgroups
-// stream K and V for a single live query tile, and two of them per CU keep twice as many
-// tile loads in flight.  Every other launch keeps the two-group tile of groups_16(D).
-constexpr int64_t kSmallProblemItems = 256;
+// Phase groups of a 16-bit launch.  The two-group tile (two waves per SIMD in alternating
+// matrix and vector phases, 256 rows) pays off where the matrix work is large and the key
+// walks long: D = 96 and 128 with more than two 256-row items per CU.  Elsewhere the one-group
+// tile (one wave per SIMD, 128 rows, two workgroups per CU whose matrix and vector work
+// overlap unsynchronised) is faster: at D <= 64 the vector work dominates and needs no
+// phase partner; with few items the launch takes as long as its longest item, which the
+// shorter 128-row items halve (measured: [1,32,8192,D] causal, 1024 items: D = 32 -12 %,
+// D = 64 -7 %, D = 96 +9 %, D = 128 +4 %; 512 and 256 items at D = 64 and 128: -4 % to -19 %).
+// Split-key launches of decode shapes (at most 128 query rows) take the one-group tile too:
+// their workgroups stream K and V for a single live query tile, and two of them per CU keep
+// twice as many tile loads in flight.
+constexpr int64_t kSmallProblemItems = 512;
 constexpr int64_t kDecodeRows = 128;
 constexpr int fwd_groups(int dtype, int64_t D, bool dense, int64_t bh, int64_t Lq,
                          bool split) {
   return dtype != 0 && D <= 128 &&
-                 ((dense && bh * ((Lq + 255) / 256) <= kSmallProblemItems) ||
+                 ((dense && (D <= 64 || bh * ((Lq + 255) / 256) <= kSmallProblemItems)) ||
                   (split && Lq <= kDecodeRows))
              ? 1
              : (dtype != 0 ? groups_16(int(D)) : 1);

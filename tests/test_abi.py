@@ -211,13 +211,13 @@ def test_plan_tiles_per_head_dim(D, dtype):
     """16-bit kernels: 8 waves and 256 rows up to D = 128, 4 waves and 128 rows at D = 256;
     the fp32 kernel: 4 waves and 128 rows.  LDS always fits the 160 KiB of a CU."""
     dt = {"f32": sd.SDPA_F32, "bf16": sd.SDPA_BF16, "f16": sd.SDPA_F16}[dtype]
-    plan = sd.sdpa_plan(4, 40, 8, 1000, 1000, D, 0, dt)  # 320 items of 256 rows
+    plan = sd.sdpa_plan(4, 40, 8, 1000, 1000, D, 0, dt)  # 1280 items of 256 rows
     if dtype == "f32":
         assert (plan.block_m, plan.threads) == (128, 256)
         stages = 2 if D <= 128 else 1
         assert plan.lds_bytes == stages * 64 * ((D + 1) + D) * 4
     else:
-        assert (plan.block_m, plan.threads) == ((256, 512) if D <= 128 else (128, 256))
+        assert (plan.block_m, plan.threads) == ((256, 512) if D in (96, 128) else (128, 256))
         assert plan.lds_bytes == 2 * 64 * ((2 * D + 16) + (2 * D + 64))
     assert plan.block_n == 64
     assert plan.q_tiles == (1000 + plan.block_m - 1) // plan.block_m
@@ -226,20 +226,20 @@ def test_plan_tiles_per_head_dim(D, dtype):
 
 @pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
 def test_plan_small_problems_take_the_one_group_tile(D):
-    """16-bit problems with at most 256 items of 256 rows run 128-row items of 4 waves, causal
-    or not; larger ones and fp32 keep their tiles."""
-    small = sd.sdpa_plan(4, 4, 16, 1024, 1024, D, 1, sd.SDPA_BF16)   # 64 heads x 4 = 256
-    small_nc = sd.sdpa_plan(4, 4, 16, 1024, 1024, D, 0, sd.SDPA_F16)
-    large = sd.sdpa_plan(4, 4, 16, 1025, 1025, D, 1, sd.SDPA_BF16)   # 64 heads x 5 = 320
-    large_nc = sd.sdpa_plan(4, 4, 16, 1025, 1025, D, 0, sd.SDPA_BF16)
-    f32 = sd.sdpa_plan(4, 4, 16, 1024, 1024, D, 1, sd.SDPA_F32)
+    """16-bit problems take 128-row items of 4 waves at D <= 64, or with at most 512 items of
+    256 rows, causal or not; D = 96 and 128 with more items, and fp32, keep their tiles."""
+    small = sd.sdpa_plan(4, 8, 16, 1024, 1024, D, 1, sd.SDPA_BF16)   # 128 heads x 4 = 512
+    small_nc = sd.sdpa_plan(4, 8, 16, 1024, 1024, D, 0, sd.SDPA_F16)
+    large = sd.sdpa_plan(4, 8, 16, 1025, 1025, D, 1, sd.SDPA_BF16)   # 128 heads x 5 = 640
+    large_nc = sd.sdpa_plan(4, 8, 16, 1025, 1025, D, 0, sd.SDPA_BF16)
+    f32 = sd.sdpa_plan(4, 8, 16, 1024, 1024, D, 1, sd.SDPA_F32)
     assert (small.block_m, small.threads, small.q_tiles) == (128, 256, 8)
     assert (small_nc.block_m, small_nc.threads) == (128, 256)
-    big = (256, 512) if D <= 128 else (128, 256)
+    big = (256, 512) if D in (96, 128) else (128, 256)
     assert (large.block_m, large.threads) == big
     assert (large_nc.block_m, large_nc.threads) == big
     assert (f32.block_m, f32.threads) == (128, 256)
-    assert small.items == 64 * 8
+    assert small.items == 128 * 8
 
 
 def test_plan_rejects_bad_sizes():

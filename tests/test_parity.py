@@ -118,14 +118,15 @@ def test_ragged_small(dtype, D, mode):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("D", [32, 64, 96, 128])
 def test_small_problem_tile_equals_two_group_tile(dtype, D):
-    """Problems with at most 256 items of 256 rows run 128-row, one-group workgroups; larger
-    ones the 256-row, two-group tile.  Both give each 32-row slice the same sequence of
-    operations, so heads 0..1 computed as a 2-head problem (one-group tile) and inside a
-    260-head problem (two-group tile) agree bit for bit, and both match the oracle: no mask,
-    both causal alignments, a boolean mask broadcast over heads, an additive mask."""
+    """Problems with at most 512 items of 256 rows (and every problem at D <= 64) run 128-row,
+    one-group workgroups; larger ones at D = 96 and 128 the 256-row, two-group tile.  Both give
+    each 32-row slice the same sequence of operations, so heads 0..1 computed as a 2-head
+    problem (one-group tile) and inside a 520-head problem (two-group tile at D = 96, 128)
+    agree bit for bit, and both match the oracle: no mask, both causal alignments, a boolean
+    mask broadcast over heads, an additive mask."""
     for n, (Lq, Lk) in enumerate([(33, 33), (129, 200), (300, 77), (300, 300)]):
         g = torch.Generator().manual_seed(4100 + n + D)
-        q, k, v = W.draw_qkv(g, (1, 260, Lq, D), (1, 260, Lk, D), dtype=dtype)
+        q, k, v = W.draw_qkv(g, (1, 520, Lq, D), (1, 520, Lk, D), dtype=dtype)
         bmask = torch.rand((1, 1, Lq, Lk), generator=g) < 0.3
         bmask[..., Lq // 2, :] = False  # one fully hidden row
         for mode in (0, 1, 2, "mask"):
@@ -137,7 +138,7 @@ def test_small_problem_tile_equals_two_group_tile(dtype, D):
             torch.cuda.synchronize()
             where = f"D={D} Lq={Lq} Lk={Lk} mode={mode}"
             assert torch.equal(big_o[:, :2], small_o) and torch.equal(big_l[:, :2], small_l), where
-            heads = [0, 1, 131, 259]
+            heads = [0, 1, 263, 519]
             rows = np.concatenate([h * Lq + np.arange(Lq) for h in heads]).astype(np.int64)
             if mode == 2:
                 tri = torch.ones(Lq, Lk, dtype=torch.bool).tril(Lk - Lq)
@@ -156,7 +157,7 @@ def test_small_problem_tile_equals_two_group_tile(dtype, D):
         torch.cuda.synchronize()
         where = f"bias D={D} Lq={Lq} Lk={Lk}"
         assert torch.equal(big_o[:, :2], small_o) and torch.equal(big_l[:, :2], small_l), where
-        rows = np.concatenate([h * Lq + np.arange(Lq) for h in (0, 259)]).astype(np.int64)
+        rows = np.concatenate([h * Lq + np.arange(Lq) for h in (0, 519)]).astype(np.int64)
         ro, rl = sdpa_oracle(q, k, v, is_causal=True, bias=bias, rows=rows)
         idx = torch.from_numpy(rows).to(DEV)
         compare(big_o.reshape(-1, D)[idx], big_l.reshape(-1)[idx], ro, rl, dtype, where)
