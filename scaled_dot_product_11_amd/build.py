@@ -18,9 +18,15 @@ LIB = os.path.join(HERE, "libsdpa_gfx950.so")
 # products accumulator-register (AGPR) destinations and then copies every accumulator
 # between the two register files on each loop iteration.  Forcing the VGPR form of the
 # products keeps the accumulators in place.
+#
+# The kernels never create a NaN from finite inputs; without NaN semantics the row maxima
+# lower to 3-input v_max3 instead of canonicalise + max pairs.  The host validation in
+# sdpa_abi.cpp rejects a NaN scale with isfinite(), which needs NaN semantics, so it is
+# compiled without that flag.
+KERNEL_FLAGS = ["-fno-honor-nans"]
 SOURCES = {
-    "sdpa_fwd_gfx950.hip": [],
-    "sdpa_bwd_gfx950.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "sdpa_fwd_gfx950.hip": KERNEL_FLAGS,
+    "sdpa_bwd_gfx950.hip": KERNEL_FLAGS + ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "sdpa_abi.cpp": [],
 }
 ARCH = "gfx950"
@@ -28,9 +34,6 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # the kernels never create a NaN from finite inputs; without NaN semantics the
-    # row maxima lower to 3-input v_max3 instead of canonicalise + max pairs
-    "-fno-honor-nans",
     "-Wall", "-Wno-unused-function",
 ]
 
@@ -41,26 +44,40 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def _run(cmd, verbose):
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
+
+
+def _finish(cmd, proc, verbose):
+    out, _ = proc.communicate()
+    msgs = [ln for ln in out.splitlines() if NOISE not in ln]
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed: " + " ".join(cmd) + "\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
 
 
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    _finish(cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                  text=True), verbose)
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
-    objs = []
+    """Compile every source to its own object (in parallel) and link the shared library."""
+    objs, jobs = [], []
     with tempfile.TemporaryDirectory(prefix="sdpa_build_") as tmpdir:
         for src, flags in SOURCES.items():
             obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
-            _run([hipcc(), *HIPCC_FLAGS, *flags, *extra_flags, "-c", "-x", "hip",
-                  os.path.join(CSRC, src), "-o", obj], verbose)
+            cmd = [hipcc(), *HIPCC_FLAGS, *flags, *extra_flags, "-c", "-x", "hip",
+                   os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            jobs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                               stderr=subprocess.STDOUT, text=True)))
             objs.append(obj)
+        for cmd, proc in jobs:
+            _finish(cmd, proc, verbose)
         tmp = LIB + ".tmp"
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
         os.replace(tmp, LIB)

@@ -224,6 +224,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // inside the range of fp32, bf16 and fp16 (whose largest finite value is 65504), and
 // the final O / l is unchanged because both carry the same reference.
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleBound = 256.0f;  // 2^kRescaleSlack
 
 
 __device__ inline s16x4 ds_read_tr(const char* p) {
@@ -577,42 +578,59 @@ void fwd_mfma(Args a) {
       for (int i = 0; i < NMB; ++i) mcur[i] = mnext[i];
     }
     if (BIAS && pre) load_bias(bcur, t + 1);
-    // Online softmax with a lagging reference: rescale O and l only when some row of the
-    // wave sees its max grow by more than kRescaleSlack.  The lane's 32 scores are
-    // reduced by a chain of 3-input maxima (v_max3_f32).
-    float mx = fmaxf(s[0][0], s[0][1]);
+    // Online softmax with a lagging reference.  p = 2^(x - m_ref), rounded to the input type
+    // two at a time into the P^T operand; the row sum adds the fp32 values (the lse needs
+    // them unrounded) in two independent chains.
+    auto exps = [&](float mu, float* psum) {
+      float ps[2];
 #pragma unroll
-    for (int i = 2; i < 32; i += 2)
-      mx = fmaxf(fmaxf(mx, s[i >> 4][i & 15]), s[i >> 4][(i + 1) & 15]);
-    mx = pair_max(mx) * c2;  // base-2 units
-    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_ref == -INFINITY ? 0.f : exp2_fast(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
+      for (int c = 0; c < 4; ++c) {
+        u32x4 w;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-    // p = 2^(x - mu), rounded to the input type two at a time into the P^T operand.  The row sum
-    // adds the fp32 values (the lse needs them unrounded) in two independent chains.
-    float ps[2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * (c & 1) + 2 * e;
-        const f32x2 pp = {exp2_fast(__builtin_fmaf(s[c >> 1][r], c2, -mu)),
-                          exp2_fast(__builtin_fmaf(s[c >> 1][r + 1], c2, -mu))};
-        ps[c & 1] = c < 2 && e == 0 ? pp[0] + pp[1] : ps[c & 1] + pp[0] + pp[1];
-        w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, v2));
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * (c & 1) + 2 * e;
+          const f32x2 pp = {exp2_fast(__builtin_fmaf(s[c >> 1][r], c2, -mu)),
+                            exp2_fast(__builtin_fmaf(s[c >> 1][r + 1], c2, -mu))};
+          ps[c & 1] = c < 2 && e == 0 ? pp[0] + pp[1] : ps[c & 1] + pp[0] + pp[1];
+          w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pp, v2));
+        }
+        pf[c] = __builtin_bit_cast(v8, w);
       }
-      pf[c] = __builtin_bit_cast(v8, w);
+      *psum = ps[0] + ps[1];
+    };
+    // Fast path: the exponentials against the current reference, no row max.  A lane whose
+    // 32 values sum to at most 2^kRescaleSlack has every p <= 2^kRescaleSlack, i.e. no score
+    // above the reference by more than the slack, so no rescale is due.  Otherwise (and
+    // while a row has no reference yet, or with a boolean mask, whose empty rows keep none)
+    // the wave takes the slow path: the row maxima (a chain of 3-input maxima and one
+    // permlane32 swap), the rescale of O and l where some row's max grew by more than the
+    // slack, and the exponentials again.  Both paths make the same rescale decisions as
+    // always computing the maxima, so the result does not depend on which path ran.
+    float lt;
+    bool slow = true;
+    if (!MASK && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
+      exps(m_ref, &lt);
+      slow = !(lt <= kRescaleBound);
     }
-    l_run += ps[0] + ps[1];
+    if (__builtin_amdgcn_ballot_w64(slow)) {
+      float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+      for (int i = 2; i < 32; i += 2)
+        mx = fmaxf(fmaxf(mx, s[i >> 4][i & 15]), s[i >> 4][(i + 1) & 15]);
+      mx = pair_max(mx) * c2;  // base-2 units
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_ref == -INFINITY ? 0.f : exp2_fast(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      exps(m_ref == -INFINITY ? 0.f : m_ref, &lt);
+    }
+    l_run += lt;
   };
 
   // ---- two-phase pipeline over key tiles ----

@@ -13,9 +13,11 @@ import numpy as np
 import pytest
 import torch
 
+import parity_log
 import workloads as W
 from oracle import sdpa_oracle
-from scaled_dot_product_11_amd import SdpaError, sdpa_fwd, sdpa_fwd_bias
+from scaled_dot_product_11_amd import (SDPA_BF16, SDPA_F16, SdpaError, sdpa_fwd, sdpa_fwd_bias,
+                                      sdpa_fwd_varlen, sdpa_plan)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,9 +50,13 @@ def half_ulp(x, bits):
     return np.where(ax > 0, np.exp2(e - bits), 0.0)
 
 
-def compare(out, lse, ref_out, ref_lse, dtype, where=""):
-    """Element-wise gate: |out - oracle| <= tol + half an output ulp; returns the raw
-    max-abs error."""
+def compare(out, lse, ref_out, ref_lse, dtype, where="", literal=False):
+    """Element-wise gate: |out - oracle| <= tol + half an output ulp (the bound applies to the
+    value the kernel computes; storing it in the output dtype adds at most half an ulp).  With
+    literal=True (the five configurations the 1e-2 / 2e-5 criterion is stated for) the raw
+    error must also be within tol itself.  Every comparison records the raw max-abs error and
+    the number of elements beyond the literal tolerance (printed at the end of the session);
+    returns the raw max-abs error."""
     out = out.float().cpu().double().numpy()
     lse = lse.cpu().double().numpy()
     assert out.shape == ref_out.shape and lse.shape == ref_lse.shape
@@ -59,13 +65,18 @@ def compare(out, lse, ref_out, ref_lse, dtype, where=""):
     assert np.all(lse[~fin] == -np.inf), f"{where}: empty rows need lse = -inf"
     assert np.all(out[~fin] == 0.0), f"{where}: empty rows need out = 0"
     diff = np.abs(out - ref_out)
-    bound = OUT_TOL[dtype] + half_ulp(np.maximum(np.abs(out), np.abs(ref_out)), OUT_BITS[dtype])
+    mag = np.maximum(np.abs(out), np.abs(ref_out))
+    bound = OUT_TOL[dtype] + half_ulp(mag, OUT_BITS[dtype])
     worst = np.max(diff - bound) if out.size else -1.0
-    err = np.max(diff) if out.size else 0.0
+    err = float(np.max(diff)) if out.size else 0.0
+    beyond = int(np.count_nonzero(diff > OUT_TOL[dtype]))
+    lerr = float(np.max(np.abs(lse[fin] - ref_lse[fin]))) if fin.any() else 0.0
+    parity_log.record(where, str(dtype).replace("torch.", ""), out.size, err, beyond, lerr,
+                      literal)
     assert worst <= 0, f"{where}: out error {err:.3e} exceeds tol + half ulp by {worst:.3e}"
-    if fin.any():
-        lerr = np.max(np.abs(lse[fin] - ref_lse[fin]))
-        assert lerr <= LSE_TOL, f"{where}: lse max-abs error {lerr:.3e}"
+    if literal:
+        assert err <= OUT_TOL[dtype], f"{where}: out error {err:.3e} beyond {OUT_TOL[dtype]}"
+    assert lerr <= LSE_TOL, f"{where}: lse max-abs error {lerr:.3e}"
     return err
 
 
@@ -96,7 +107,7 @@ def run_both(q, k, v, mask, causal, scale=None):
 def test_config1_full():
     wl = W.config1()
     out, lse, ro, rl = run_both(wl.q, wl.k, wl.v, None, True, wl.scale)
-    compare(out, lse, ro, rl, torch.float32, "c1")
+    compare(out, lse, ro, rl, torch.float32, "c1", literal=True)
 
 
 SHAPES = [(1, 1), (33, 33), (64, 64), (127, 127), (129, 129), (200, 200), (77, 300), (300, 77)]
@@ -118,17 +129,25 @@ def test_ragged_small(dtype, D, mode):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("D", [32, 64, 96, 128])
 def test_small_problem_tile_equals_two_group_tile(dtype, D):
-    """Problems with at most 512 items of 256 rows (and every problem at D <= 64) run 128-row,
-    one-group workgroups; larger ones at D = 96 and 128 the 256-row, two-group tile.  Both give
-    each 32-row slice the same sequence of operations, so heads 0..1 computed as a 2-head
-    problem (one-group tile) and inside a 520-head problem (two-group tile at D = 96, 128)
-    agree bit for bit, and both match the oracle: no mask, both causal alignments, a boolean
-    mask broadcast over heads, an additive mask."""
+    """The one-group tile (128 rows, 4 waves) and the two-group tile (256 rows, 8 waves in
+    alternating phases) give each 32-row slice the same sequence of operations, so they agree
+    bit for bit.  Which tile a launch takes is asserted through sdpa_plan.  At D = 96 and 128
+    a 2-head problem runs the one-group tile and a 520-head problem the two-group tile; their
+    shared heads are compared with no mask, both causal alignments, a boolean mask broadcast
+    over heads and an additive mask.  At D <= 64 every dense problem runs the one-group tile
+    (the 520-head comparison is then a determinism check), and the two-group side is the same
+    two heads packed as one sequence through sdpa_fwd_varlen, which always takes the
+    two-group tile (no mask, both causal alignments).  Everything is also checked against the
+    oracle."""
+    code = {torch.bfloat16: SDPA_BF16, torch.float16: SDPA_F16}[dtype]
     for n, (Lq, Lk) in enumerate([(33, 33), (129, 200), (300, 77), (300, 300)]):
         g = torch.Generator().manual_seed(4100 + n + D)
         q, k, v = W.draw_qkv(g, (1, 520, Lq, D), (1, 520, Lk, D), dtype=dtype)
         bmask = torch.rand((1, 1, Lq, Lk), generator=g) < 0.3
         bmask[..., Lq // 2, :] = False  # one fully hidden row
+        assert sdpa_plan(4, 1, 2, Lq, Lk, D, 1, code).threads == 256, "2 heads: one-group tile"
+        big_threads = sdpa_plan(4, 1, 520, Lq, Lk, D, 1, code).threads
+        assert big_threads == (512 if D >= 96 else 256), (D, Lq, big_threads)
         for mode in (0, 1, 2, "mask"):
             causal = 0 if mode == "mask" else mode
             m = to_dev(bmask) if mode == "mask" else None
@@ -138,6 +157,15 @@ def test_small_problem_tile_equals_two_group_tile(dtype, D):
             torch.cuda.synchronize()
             where = f"D={D} Lq={Lq} Lk={Lk} mode={mode}"
             assert torch.equal(big_o[:, :2], small_o) and torch.equal(big_l[:, :2], small_l), where
+            if D <= 64 and mode != "mask":
+                # the same two heads packed as one sequence: the two-group tile
+                pq, pk, pv = (to_dev(t[0, :2].transpose(0, 1).contiguous()) for t in (q, k, v))
+                cq = torch.tensor([0, Lq], dtype=torch.int32, device=DEV)
+                ck = torch.tensor([0, Lk], dtype=torch.int32, device=DEV)
+                vo, vl = sdpa_fwd_varlen(pq, pk, pv, cq, ck, Lq, is_causal=causal)
+                torch.cuda.synchronize()
+                assert torch.equal(vo.transpose(0, 1), small_o[0]), where + " varlen"
+                assert torch.equal(vl, small_l[0]), where + " varlen lse"
             heads = [0, 1, 263, 519]
             rows = np.concatenate([h * Lq + np.arange(Lq) for h in heads]).astype(np.int64)
             if mode == 2:
@@ -268,7 +296,7 @@ def check_sampled(wl, out, lse, n_random=300, seed=0, extra_rows=None):
                          rows=rows)
     go = out.reshape(-1, D)[torch.from_numpy(rows).to(out.device)]
     gl = lse.reshape(-1)[torch.from_numpy(rows).to(lse.device)]
-    return compare(go, gl, ro, rl, wl.q.dtype, wl.name)
+    return compare(go, gl, ro, rl, wl.q.dtype, wl.name, literal=True)
 
 
 def run_wl(wl):
@@ -282,7 +310,7 @@ def test_config2_full_oracle():
     wl = W.config2()
     out, lse = run_wl(wl)
     ro, rl = sdpa_oracle(wl.q, wl.k, wl.v, is_causal=True, scale=wl.scale)
-    compare(out, lse, ro, rl, torch.bfloat16, wl.name)
+    compare(out, lse, ro, rl, torch.bfloat16, wl.name, literal=True)
 
 
 def test_config2_fp16_full_oracle():
