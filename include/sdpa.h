@@ -25,8 +25,10 @@
  * [1,N,L,D], bit for bit.
  *
  * The library launches exactly one kernel per sdpa_fwd call on the caller's stream,
- * allocates nothing, frees nothing, never synchronises, and keeps no per-call state (the
- * only global is a per-device cache of the architecture check).  Calls are thread-safe.
+ * allocates nothing, frees nothing, never synchronises, and keeps no per-call state (its
+ * globals are a per-device cache of the architecture check and the static split-key
+ * workspace of sdpa_fwd_splitkv_noalloc).  Calls are thread-safe, except that calls of
+ * sdpa_fwd_splitkv_noalloc that overlap in time on one device share that workspace.
  */
 #ifndef SDPA_MI355X_H_
 #define SDPA_MI355X_H_
@@ -62,7 +64,9 @@ enum sdpa_status {
   SDPA_ERR_SCALE = 8,    /* scale is NaN or infinite                                     */
   SDPA_ERR_DEVICE = 9,   /* the stream's device is not gfx950, or the launch failed      */
   SDPA_ERR_CAUSAL = 10,  /* causal mode not an sdpa_causal value                         */
-  SDPA_ERR_WORKSPACE = 11 /* workspace smaller than sdpa_fwd_splitkv_workspace() bytes   */
+  SDPA_ERR_WORKSPACE = 11, /* workspace smaller than sdpa_fwd_splitkv_workspace() bytes  */
+  SDPA_ERR_STATIC_WORKSPACE = 12 /* sdpa_fwd_splitkv_noalloc: the problem needs more than
+                                    SDPA_STATIC_WORKSPACE_BYTES of split-key workspace    */
 };
 
 /* Causal modes (the is_causal / causal arguments). */
@@ -201,6 +205,34 @@ int sdpa_fwd_splitkv_check(const void* q, const void* k, const void* v, const vo
  * Returns minus an sdpa_status for invalid sizes. */
 int64_t sdpa_fwd_splitkv_workspace(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
                                    int64_t num_splits, int dtype);
+
+/* Bytes of the static split-key workspace of sdpa_fwd_splitkv_noalloc (per device). */
+#define SDPA_STATIC_WORKSPACE_BYTES (16ll << 20)
+
+/*
+ * sdpa_fwd_splitkv_noalloc -- sdpa_fwd_splitkv for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace argument; the partial outputs and lse go to a static
+ * device array of SDPA_STATIC_WORKSPACE_BYTES (16 MiB) that the library holds on every
+ * device it runs on until the process ends.  The library allocates and frees nothing; the
+ * array's device address is looked up once per device, on the first call there.
+ *
+ *   arguments     as sdpa_fwd_splitkv, without workspace / workspace_bytes.
+ *   limit         problems needing more than SDPA_STATIC_WORKSPACE_BYTES (that is,
+ *                 sdpa_fwd_splitkv_workspace(B, H, Lq, Lk, D, num_splits, dtype) bytes) are
+ *                 rejected with SDPA_ERR_STATIC_WORKSPACE before anything is launched.
+ *   sharing       every call on one device uses that device's one array, whose contents
+ *                 each call overwrites (nothing in it needs to start at zero): calls that
+ *                 overlap in time on one device race, e.g. calls on two streams that are not
+ *                 ordered by an event; calls on one stream are ordered and safe.
+ *
+ * Two launches on `stream` (chunks, then the merge); the result is the same as
+ * sdpa_fwd_splitkv's for the same num_splits, bit for bit.
+ */
+int sdpa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                             const int64_t* strides, float scale, int is_causal,
+                             int64_t num_splits, int dtype, void* stream);
 
 /*
  * sdpa_fwd_varlen -- the fused forward over a batch of sequences of different lengths

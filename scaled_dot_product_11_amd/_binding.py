@@ -21,10 +21,12 @@ STATUS_NAMES = {
     0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_RANK", 3: "SDPA_ERR_SHAPE",
     4: "SDPA_ERR_HEAD_DIM", 5: "SDPA_ERR_DTYPE", 6: "SDPA_ERR_STRIDE", 7: "SDPA_ERR_ALIGN",
     8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_DEVICE", 10: "SDPA_ERR_CAUSAL", 11: "SDPA_ERR_WORKSPACE",
+    12: "SDPA_ERR_STATIC_WORKSPACE",
 }
+SDPA_STATIC_WORKSPACE_BYTES = 16 << 20
 
 EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_fwd_bias", "sdpa_fwd_bias_check", "sdpa_fwd_splitkv", "sdpa_fwd_splitkv_check",
-           "sdpa_fwd_splitkv_workspace", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
+           "sdpa_fwd_splitkv_workspace", "sdpa_fwd_splitkv_noalloc", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
            "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
 
 
@@ -83,6 +85,10 @@ def load_library():
     lib.sdpa_fwd_splitkv.restype = ctypes.c_int
     lib.sdpa_fwd_splitkv_check.argtypes = split_common
     lib.sdpa_fwd_splitkv_check.restype = ctypes.c_int
+    lib.sdpa_fwd_splitkv_noalloc.argtypes = [vp] * 5 + [ctypes.c_int, i64, i64, i64, i64, i64,
+                                                        ctypes.POINTER(i64), ctypes.c_float,
+                                                        ctypes.c_int, i64, ctypes.c_int, vp]
+    lib.sdpa_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.sdpa_fwd_splitkv_workspace.argtypes = [i64] * 6 + [ctypes.c_int]
     lib.sdpa_fwd_splitkv_workspace.restype = i64
     lib.sdpa_strerror.argtypes = [ctypes.c_int]
@@ -332,6 +338,32 @@ def sdpa_fwd_splitkv(q, k, v, out=None, lse=None, *, scale=None, is_causal=False
             None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr, float(scale),
             causal_mode(is_causal), int(num_splits), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), dtype, handle)
+    _raise_on(status)
+    return out, lse
+
+
+def sdpa_fwd_splitkv_noalloc(q, k, v, out, lse=None, *, scale=None, is_causal=False,
+                             num_splits=0, stream=None):
+    """sdpa_fwd_splitkv without a workspace argument (C ABI `sdpa_fwd_splitkv_noalloc`): the
+    partial results go to the library's static per-device workspace of
+    SDPA_STATIC_WORKSPACE_BYTES, for callers that cannot allocate.  out (and lse, if wanted)
+    must be given: this call allocates nothing.  Calls that overlap in time on one device
+    share the workspace.  Returns (out, lse)."""
+    _check_shapes(q, k, v, out, lse, None)
+    if out is None:
+        raise ValueError("sdpa_fwd_splitkv_noalloc allocates nothing: pass out (and lse)")
+    rank = q.dim()
+    B, H, Lq, Lk, D = _sizes(q, k)
+    strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride()]
+    arr = (ctypes.c_int64 * len(strides))(*strides)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        status = load_library().sdpa_fwd_splitkv_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr, float(scale),
+            causal_mode(is_causal), int(num_splits), _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return out, lse
 

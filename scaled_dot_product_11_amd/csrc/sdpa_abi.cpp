@@ -6,6 +6,7 @@
 // the rank-4 problem [1,N,L,D] (batch stride 0) before anything else happens, and both
 // ranks reach the same fused kernel with the same arguments.
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <mutex>
@@ -16,6 +17,8 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+static_assert(SDPA_STATIC_WORKSPACE_BYTES == sdpa::kStaticWorkspaceBytes,
+              "header and library disagree on the static workspace size");
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -368,15 +371,19 @@ int normalise_bias(const void* q, const void* k, const void* v, const void* out,
   return SDPA_OK;
 }
 
+// The device `stream` runs on (the current device for the null stream); false on failure.
+bool stream_device(hipStream_t stream, int* dev) {
+  *dev = 0;
+  if (stream) return hipStreamGetDevice(stream, dev) == hipSuccess;
+  return hipGetDevice(dev) == hipSuccess;
+}
+
 // The code object holds gfx950 machine code only; refuse other devices up front.
-// Cached per device id (the only global state of the library).
+// Cached per device id (the only global state of the library besides the static split-key
+// workspace of sdpa_fwd_splitkv_noalloc).
 bool device_is_gfx950(hipStream_t stream) {
   int dev = 0;
-  if (stream) {
-    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return false;
-  } else if (hipGetDevice(&dev) != hipSuccess) {
-    return false;
-  }
+  if (!stream_device(stream, &dev)) return false;
   constexpr int kMaxDevices = 64;
   static std::mutex mu;
   static signed char verdict[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
@@ -472,6 +479,33 @@ int sdpa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, flo
   return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
 }
 
+int sdpa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                             const int64_t* strides, float scale, int is_causal,
+                             int64_t num_splits, int dtype, void* stream) {
+  // sdpa_fwd_splitkv's validation with a stand-in workspace that is large enough, then the
+  // bytes this problem needs against the static workspace
+  alignas(16) static const char stand_in[16] = {0};
+  sdpa::Problem p;
+  int st = normalise_splitkv(q, k, v, out, lse, rank, B, H, Lq, Lk, D, strides, scale, is_causal,
+                             num_splits, stand_in, INT64_MAX, dtype, &p);
+  if (st != SDPA_OK) return st;
+  int64_t nsplit, split_len, need;
+  st = splitkv_sizes(B, H, Lq, Lk, D, num_splits, dtype, &nsplit, &split_len, &need);
+  if (st != SDPA_OK) return st;
+  if (need > sdpa::kStaticWorkspaceBytes) return SDPA_ERR_STATIC_WORKSPACE;
+  if (p.B * p.H * p.Lq == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  int dev = 0;
+  void* ws = nullptr;
+  if (!stream_device(s, &dev) || sdpa::static_workspace(dev, &ws) != hipSuccess)
+    return SDPA_ERR_DEVICE;
+  p.ws_o = static_cast<float*>(ws);
+  p.ws_lse = p.ws_o + p.nsplit * p.B * p.H * p.Lq * p.D;
+  return sdpa::launch_fwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
 int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const void* out,
                           const float* lse, const int32_t* cu_seqlens_q,
                           const int32_t* cu_seqlens_k, int64_t nseq, int64_t max_seqlen_q,
@@ -540,6 +574,9 @@ const char* sdpa_strerror(int status) {
       return "causal mode must be 0 (none), 1 (top-left) or 2 (bottom-right)";
     case SDPA_ERR_WORKSPACE:
       return "workspace smaller than sdpa_fwd_splitkv_workspace() bytes";
+    case SDPA_ERR_STATIC_WORKSPACE:
+      return "the split-key workspace this problem needs exceeds the 16 MiB static workspace "
+             "of sdpa_fwd_splitkv_noalloc";
     default: return "unknown sdpa status";
   }
 }

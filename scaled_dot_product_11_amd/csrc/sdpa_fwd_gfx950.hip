@@ -27,6 +27,7 @@
 //     cover whole rows.
 #include <math.h>
 
+#include <mutex>
 
 #include "sdpa_internal.h"
 
@@ -606,7 +607,7 @@ void fwd_mfma(Args a) {
     // permlane32 swap), the rescale of O and l where some row's max grew by more than the
     // slack, and the exponentials again.  Both paths make the same rescale decisions as
     // always computing the maxima, so the result does not depend on which path ran.
-    float lt;
+    float lt = 0.f;
     bool slow = true;
     if (!MASK && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
       exps(m_ref, &lt);
@@ -1069,6 +1070,42 @@ hipError_t launch_combine(const Args& a, int dtype, int nsplit, hipStream_t s) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Split-key workspace of sdpa_fwd_splitkv_noalloc, for callers that cannot allocate: a
+// file-scope device array of kStaticWorkspaceBytes, held by every device the library runs
+// on until the process ends.  In host code the array's name is only a host-side stand-in;
+// its address on a device comes from hipGetSymbolAddress with that device current, taken
+// once per device and kept, and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------------------
+namespace {
+static __device__ __align__(256) char scratch[kStaticWorkspaceBytes];
+}  // namespace
+
+hipError_t static_workspace(int device, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int current = 0;
+    hipError_t e = hipGetDevice(&current);
+    if (e != hipSuccess) return e;
+    if (current != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (current != device) {
+      const hipError_t back = hipSetDevice(current);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   Args a;

@@ -138,6 +138,14 @@ inline void splitkv_plan(int64_t bh, int64_t q_tiles, int64_t Lk, int64_t reques
   *nsplit = Lk > 0 ? (Lk + len - 1) / len : 1;
 }
 
+// sdpa_fwd_splitkv_noalloc: the split-key workspace lives in a static device array of this
+// many bytes per device (partial outputs and their lse, nsplit * B*H * Lq * (D + 1) * 4).
+constexpr int64_t kStaticWorkspaceBytes = int64_t(16) << 20;
+
+// The device address of that array on `device` (looked up once per device, with the device
+// made current for the lookup).  Returns a hipError_t.
+hipError_t static_workspace(int device, void** ptr);
+
 // ---- backward (bf16) ----
 // Two kernels of 8 waves (two per SIMD): the dQ kernel owns 256 query rows of one (b, h)
 // and walks key tiles of 64; the dK/dV kernel owns 128 keys and walks query tiles of 64.

@@ -489,3 +489,32 @@ def test_bias_check():
     assert c(**dict(a, strides=s)) == STRIDE
     assert c(**dict(a, dtype=sd.SDPA_F16)) == OK
     assert c(**dict(a, is_causal=2)) == OK
+
+
+def test_splitkv_noalloc_rejects_before_any_device_call():
+    """sdpa_fwd_splitkv_noalloc validates like sdpa_fwd_splitkv and refuses problems whose
+    split-key workspace exceeds the static one, all before touching a GPU."""
+    import ctypes
+    lib = sd.load_library()
+    B, H, Lq, Lk, D = 8, 32, 64, 65536, 128
+    q = [H * Lq * D, Lq * D, D, 1]
+    k = [H * Lk * D, Lk * D, D, 1]
+    arr = (ctypes.c_int64 * 16)(*(q + k + k + q))
+    ptrs = (A, A + 0x10000, A + 0x20000, A + 0x30000, A + 0x40000)
+    need = sd.sdpa_fwd_splitkv_workspace(B, H, Lq, Lk, D, 64, sd.SDPA_BF16)
+    assert need > sd.SDPA_STATIC_WORKSPACE_BYTES == 16 << 20
+    st = lib.sdpa_fwd_splitkv_noalloc(*ptrs, 4, B, H, Lq, Lk, D, arr, 0.125, 2, 64, sd.SDPA_BF16,
+                                      None)
+    assert st == 12 and sd.STATUS_NAMES[st] == "SDPA_ERR_STATIC_WORKSPACE"
+    assert "16 MiB" in sd.sdpa_strerror(12)
+    # the splitkv validation runs first
+    st = lib.sdpa_fwd_splitkv_noalloc(*ptrs, 4, B, H, Lq, Lk, 80, arr, 0.125, 2, 64, sd.SDPA_BF16,
+                                      None)
+    assert st == HEAD
+    st = lib.sdpa_fwd_splitkv_noalloc(*ptrs, 4, B, H, Lq, Lk, D, arr, 0.125, 2, 5000,
+                                      sd.SDPA_BF16, None)
+    assert st == SHAPE
+    # an empty problem is a no-op returning success, without a GPU
+    st = lib.sdpa_fwd_splitkv_noalloc(None, None, None, None, None, 4, B, H, 0, Lk, D, arr, 0.125,
+                                      2, 0, sd.SDPA_BF16, None)
+    assert st == OK
