@@ -22,6 +22,22 @@ static_assert(SDPA_STATIC_WORKSPACE_BYTES == sdpa::kStaticWorkspaceBytes,
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// A one-dimensional launch of `blocks` workgroups of `threads` work-items fits HIP's limits:
+// at most 2^31 - 1 workgroups and fewer than 2^32 work-items in the dimension.
+bool launch_fits(int64_t blocks, int64_t threads) {
+  return blocks <= kMaxDim && blocks * threads <= int64_t(UINT32_MAX);
+}
+
+// Workgroups and threads of the forward kernel for `rows` query rows per head: the tile
+// sdpa::fwd_groups picks for this problem (dense, split-key or packed).
+void fwd_tile(int dtype, int64_t D, bool dense, bool split, int64_t bh, int64_t rows,
+              int64_t* q_tiles, int64_t* threads) {
+  const int groups = sdpa::fwd_groups(dtype, D, dense, bh, rows, split);
+  const int64_t bm = dtype != SDPA_F32 ? 128 * groups : sdpa::kBlockMF32;
+  *q_tiles = (rows + bm - 1) / bm;
+  *threads = dtype != SDPA_F32 ? 256 * groups : sdpa::kThreadsF32;
+}
+
 // One tensor's `rank` strides as canonical (b, h, row, col) strides: rank 3 [N,L,*] is
 // [1,N,L,*] with batch stride 0.  No stride may be negative; the innermost must be 1.
 int canon_strides(int rank, const int64_t* s, int64_t out[4]) {
@@ -69,9 +85,10 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
   if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
 
   const int64_t bh = B * H;
-  const int64_t bm = sdpa::block_m(dtype, int(D));
-  const int64_t q_tiles = (Lq + bm - 1) / bm;
-  if (bh != 0 && q_tiles > kMaxDim / bh) return SDPA_ERR_SHAPE;  // grid size
+  int64_t q_tiles, threads;
+  fwd_tile(dtype, D, true, false, bh, Lq, &q_tiles, &threads);
+  if (bh != 0 && (q_tiles > kMaxDim / bh || !launch_fits(bh * q_tiles, threads)))
+    return SDPA_ERR_SHAPE;  // grid size
   const bool any_rows = bh * Lq != 0;
   const bool reads_kv = any_rows && Lk != 0;
 
@@ -149,9 +166,12 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
   if (!strides) return SDPA_ERR_NULL;
   if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t bh = B * H;
-  if (bh != 0 && ((Lq + sdpa::kBwdBlockQ - 1) / sdpa::kBwdBlockQ > kMaxDim / bh ||
-                  (Lk + sdpa::kBwdBlockK - 1) / sdpa::kBwdBlockK > kMaxDim / bh))
-    return SDPA_ERR_SHAPE;  // grid size
+  const int64_t tq = (Lq + sdpa::kBwdBlockQ - 1) / sdpa::kBwdBlockQ;
+  const int64_t tk = (Lk + sdpa::kBwdBlockK - 1) / sdpa::kBwdBlockK;
+  if (bh != 0 && (tq > kMaxDim / bh || tk > kMaxDim / bh ||
+                  !launch_fits(bh * tq, sdpa::kThreadsBwdQ) ||
+                  !launch_fits(bh * tk, sdpa::kThreadsBwdK)))
+    return SDPA_ERR_SHAPE;  // grid sizes
   const bool rows = bh * Lq != 0;  // the dq kernel runs (and reads q, out, dout, lse)
   const bool keys = bh * Lk != 0;  // the dkdv kernel runs (and reads k, v, writes dk, dv)
 
@@ -242,9 +262,10 @@ int normalise_varlen(const void* q, const void* k, const void* v, const void* ou
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
   if (causal < SDPA_CAUSAL_NONE || causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t heads = nseq * H;
-  const int64_t bm = sdpa::block_m(dtype, int(D));
-  const int64_t q_tiles = (max_seqlen_q + bm - 1) / bm;
-  if (heads != 0 && q_tiles > kMaxDim / heads) return SDPA_ERR_SHAPE;  // grid size
+  int64_t q_tiles, threads;
+  fwd_tile(dtype, D, false, false, heads, max_seqlen_q, &q_tiles, &threads);
+  if (heads != 0 && (q_tiles > kMaxDim / heads || !launch_fits(heads * q_tiles, threads)))
+    return SDPA_ERR_SHAPE;  // grid size
   const bool any_rows = heads != 0 && total_q != 0 && max_seqlen_q != 0;
 
   int64_t s4[4][4];
@@ -317,9 +338,13 @@ int splitkv_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, int64
   if (num_splits < 0 || num_splits > kMaxSplits) return SDPA_ERR_SHAPE;
   const int64_t bh = B * H;
   const int64_t bm = sdpa::block_m(dtype, int(D));
-  const int64_t q_tiles = (Lq + bm - 1) / bm;
-  sdpa::splitkv_plan(bh, q_tiles, Lk, num_splits, nsplit, split_len);
-  if (bh != 0 && q_tiles > kMaxDim / bh / *nsplit) return SDPA_ERR_SHAPE;  // grid size
+  sdpa::splitkv_plan(bh, (Lq + bm - 1) / bm, Lk, num_splits, nsplit, split_len);
+  int64_t q_tiles, threads;
+  fwd_tile(dtype, D, false, true, bh, Lq, &q_tiles, &threads);
+  // the chunk launch, and the merge launch of one 64-lane wave per query row
+  if (bh != 0 && (q_tiles > kMaxDim / bh / *nsplit || !launch_fits(bh * q_tiles * *nsplit, threads) ||
+                  !launch_fits((bh * Lq + 3) / 4, 256)))
+    return SDPA_ERR_SHAPE;  // grid sizes
   *need = *nsplit * bh * Lq * (D + 1) * 4;
   return SDPA_OK;
 }

@@ -518,3 +518,34 @@ def test_splitkv_noalloc_rejects_before_any_device_call():
     st = lib.sdpa_fwd_splitkv_noalloc(None, None, None, None, None, 4, B, H, 0, Lk, D, arr, 0.125,
                                       2, 0, sd.SDPA_BF16, None)
     assert st == OK
+
+
+def test_grid_limits_follow_the_launched_tile():
+    """Problems are refused when the launch that would run exceeds HIP's grid limits (fewer
+    than 2^32 work-items in the dimension): the count uses the tile fwd_groups picks, 128
+    rows / 256 threads or 256 rows / 512 threads, and also bounds the merge launch of the
+    split-key path (one 64-lane wave per query row)."""
+    def dense(B, H, Lq, D):
+        return check(**args4(B=B, H=H, Lq=Lq, Lk=64, D=D, strides=[H * Lq * D, Lq * D, D, 1,
+                                                                   H * 64 * D, 64 * D, D, 1,
+                                                                   H * 64 * D, 64 * D, D, 1,
+                                                                   H * Lq * D, Lq * D, D, 1,
+                                                                   0, 0, 0, 0]))
+    # D = 128: 256-row items of 512 threads: at most 2^23 - 1 items
+    assert sd.sdpa_plan(4, 512, 512, 7936, 64, 128, 1, sd.SDPA_BF16).threads == 512
+    assert dense(512, 512, 7936, 128) == OK       # 262144 * 31 items
+    assert dense(512, 512, 8192, 128) == SHAPE    # 262144 * 32 = 2^23 items
+    # D = 64: 128-row items of 256 threads: at most 2^24 - 1 items
+    assert sd.sdpa_plan(4, 512, 512, 7936, 64, 64, 1, sd.SDPA_BF16).threads == 256
+    assert dense(512, 512, 8064, 64) == OK        # 262144 * 63 items
+    assert dense(512, 512, 8192, 64) == SHAPE     # 262144 * 64 = 2^24 items
+    with pytest.raises(sd.SdpaError):
+        sd.sdpa_plan(4, 512, 512, 8192, 64, 64, 1, sd.SDPA_BF16)
+    # split keys: the merge runs one wave per (head, query row), bh * Lq < 2^26
+    c = sd.sdpa_fwd_splitkv_check
+    big = dict(sargs(), B=1024, H=64, Lq=1023, Lk=64, num_splits=1, workspace_bytes=1 << 62)
+    big["strides"] = [64 * 1023 * 128, 1023 * 128, 128, 1, 64 * 64 * 128, 64 * 128, 128, 1,
+                      64 * 64 * 128, 64 * 128, 128, 1, 64 * 1023 * 128, 1023 * 128, 128, 1]
+    assert c(**big) == OK                          # 67043328 rows
+    assert c(**dict(big, Lq=1024, strides=[64 * 1024 * 128, 1024 * 128, 128, 1] + big["strides"][4:12]
+                    + [64 * 1024 * 128, 1024 * 128, 128, 1])) == SHAPE  # 2^26 rows
