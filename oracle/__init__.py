@@ -65,6 +65,13 @@ def _load():
             ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
             ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
             ctypes.c_int, ctypes.c_double, dp, dp, dp, ctypes.c_int]
+        lib.oracle_sdpa_bwd_bias.restype = ctypes.c_int
+        lib.oracle_sdpa_bwd_bias.argtypes = [
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64,
+            ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, ctypes.c_void_p, i64p,
+            ctypes.c_void_p, i64p, ctypes.c_void_p, i64p, dp, i64p,
+            ctypes.c_int, ctypes.c_double, dp, dp, dp, ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -118,11 +125,25 @@ def _mask_args(mask, q, Lk):
     return ctypes.c_void_p(mask_t.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(mask_t)), mask_t
 
 
-def sdpa_bwd_oracle(q, k, v, dout, *, mask=None, is_causal=False, scale=None, nthreads=0):
+def _bias_args(bias, q, Lk):
+    """(pointer, strides array, keep-alive tensor) of a float bias expanded to q's rows,
+    read exactly as float64."""
+    if bias is None:
+        return None, None, None
+    # converted in its own (unbroadcast) shape, then broadcast with zero strides
+    bias_t = _as_tensor(bias).to(torch.float64).expand(tuple(q.shape[:-1]) + (Lk,))
+    bptr = ctypes.cast(ctypes.c_void_p(bias_t.data_ptr()), ctypes.POINTER(ctypes.c_double))
+    return bptr, (ctypes.c_int64 * 4)(*_strides4(bias_t)), bias_t
+
+
+def sdpa_bwd_oracle(q, k, v, dout, *, mask=None, is_causal=False, scale=None, nthreads=0,
+                    bias=None):
     """Gradients (dq, dk, dv) of out = sdpa(q, k, v) for the upstream gradient dout, in fp64.
 
-    Same tensor conventions as sdpa_oracle; dout has q's shape and dtype.  Returns float64
-    numpy arrays shaped like q, k and v.  Fully masked query rows contribute nothing.
+    Same tensor conventions as sdpa_oracle (mask, bias, is_causal, scale); dout has q's shape
+    and dtype.  The bias is a constant: it shifts the scores, and no gradient is returned for
+    it.  Returns float64 numpy arrays shaped like q, k and v.  Fully masked query rows
+    contribute nothing.
     """
     q, k, v, dout = _as_tensor(q), _as_tensor(k), _as_tensor(v), _as_tensor(dout)
     B, H, Lq, Lk, D = _check_qkv(q, k, v)
@@ -131,21 +152,22 @@ def sdpa_bwd_oracle(q, k, v, dout, *, mask=None, is_causal=False, scale=None, nt
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     mptr, ms_arr, _keep = _mask_args(mask, q, Lk)
+    bptr, bs_arr, _keep_b = _bias_args(bias, q, Lk)
     dq = np.zeros((B * H * Lq, D), dtype=np.float64)
     dk = np.zeros((B * H * Lk, D), dtype=np.float64)
     dv = np.zeros((B * H * Lk, D), dtype=np.float64)
-    st = _load().oracle_sdpa_bwd(
+    st = _load().oracle_sdpa_bwd_bias(
         _DTYPE_CODE[q.dtype], B, H, Lq, Lk, D,
         ctypes.c_void_p(q.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(q)),
         ctypes.c_void_p(k.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(k)),
         ctypes.c_void_p(v.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(v)),
         ctypes.c_void_p(dout.data_ptr()), (ctypes.c_int64 * 4)(*_strides4(dout)),
-        mptr, ms_arr, 1 if is_causal else 0, float(scale),
+        mptr, ms_arr, bptr, bs_arr, 1 if is_causal else 0, float(scale),
         dq.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
         dk.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
         dv.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))
     if st != 0:
-        raise RuntimeError(f"oracle_sdpa_bwd failed with status {st}")
+        raise RuntimeError(f"oracle_sdpa_bwd_bias failed with status {st}")
     return dq.reshape(tuple(q.shape)), dk.reshape(tuple(k.shape)), dv.reshape(tuple(v.shape))
 
 

@@ -215,7 +215,7 @@ int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
  * oracle_sdpa_bwd -- gradients of out = sdpa(q, k, v) for a given upstream gradient dout,
  * one head at a time, whole [Lq, Lk] matrices in fp64:
  *
- *   S   = scale * q.k^T, hidden positions -inf       (the forward's steps 1-3)
+ *   S   = scale * q.k^T (+ bias), hidden positions -inf   (the forward's steps 1-3)
  *   P   = row softmax of S; a row with every key hidden is all zero (safe softmax)
  *   dV  = P^T dout                                   (through step 5, out = P v)
  *   dP  = dout v^T
@@ -224,20 +224,26 @@ int oracle_sdpa_fwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
  *   dK  = scale * dS^T q
  *
  *   dtype, B..D, q/k/v and their strides, mask, is_causal, scale: as in oracle_sdpa_fwd
+ *   bias, bs     optional additive mask as in oracle_sdpa_fwd_bias: S = scale * q.k^T + bias,
+ *                -inf hides the key.  The bias is a constant of the forward (the SDPA call
+ *                takes it as a given mask), so it shifts S and P but adds no term to the
+ *                chain rule, and no gradient is produced for it; NULL = none
  *   dout, dos    upstream gradient [B,H,Lq,D] of q's dtype, four element strides
  *   dq           [B,H,Lq,D] doubles, row-major;  dk, dv: [B,H,Lk,D] doubles, row-major
  *   nthreads     OpenMP threads over heads (<= 0: the runtime's default)
  *
  * Returns 0 on success, 1 on a bad argument, 2 if scratch memory could not be allocated.
  */
-int oracle_sdpa_bwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
-                    const void* q, const int64_t* qs, const void* k, const int64_t* ks,
-                    const void* v, const int64_t* vs, const void* dout, const int64_t* dos,
-                    const uint8_t* mask, const int64_t* ms, int is_causal, double scale,
-                    double* dq, double* dk, double* dv, int nthreads) {
+int oracle_sdpa_bwd_bias(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                         const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                         const void* v, const int64_t* vs, const void* dout,
+                         const int64_t* dos, const uint8_t* mask, const int64_t* ms,
+                         const double* bias, const int64_t* bs, int is_causal, double scale,
+                         double* dq, double* dk, double* dv, int nthreads) {
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return 1;
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || D < 0) return 1;
-  if (!dq || !dk || !dv || !qs || !ks || !vs || !dos || (mask && !ms)) return 1;
+  if (!dq || !dk || !dv || !qs || !ks || !vs || !dos || (mask && !ms) || (bias && !bs))
+    return 1;
   int status = 0;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -274,6 +280,10 @@ int oracle_sdpa_bwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
             dot += load_elem(q, dtype, qb + i * qs[2] + d * qs[3]) *
                    load_elem(k, dtype, kb + j * ks[2] + d * ks[3]);
           pr[j] = scale * dot;
+          if (bias) { /* the additive mask, as in the forward; -inf hides the key */
+            pr[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];
+            if (pr[j] == -INFINITY) continue;
+          }
           if (!any || pr[j] > m) m = pr[j];
           any = 1;
         }
@@ -322,6 +332,16 @@ int oracle_sdpa_bwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int
     free(dS);
   }
   return status;
+}
+
+/* oracle_sdpa_bwd -- oracle_sdpa_bwd_bias without an additive mask. */
+int oracle_sdpa_bwd(int dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                    const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                    const void* v, const int64_t* vs, const void* dout, const int64_t* dos,
+                    const uint8_t* mask, const int64_t* ms, int is_causal, double scale,
+                    double* dq, double* dk, double* dv, int nthreads) {
+  return oracle_sdpa_bwd_bias(dtype, B, H, Lq, Lk, D, q, qs, k, ks, v, vs, dout, dos, mask, ms,
+                              NULL, NULL, is_causal, scale, dq, dk, dv, nthreads);
 }
 
 /* Threads the OpenMP runtime would use by default (reported next to CPU timings). */

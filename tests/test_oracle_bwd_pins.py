@@ -171,3 +171,91 @@ def test_bwd_reads_bf16_exactly_and_any_strides():
     got2 = oracle.sdpa_bwd_oracle(qt, k, v, dout, is_causal=True)
     for a, b in zip(got2, got):
         np.testing.assert_array_equal(a, b)
+
+
+# ---- the additive mask (bias): a constant added to the scaled scores, -inf hides a key ----
+
+def make_bias(seed, B, H, Lq, Lk, hide=0.15, empty_row=None):
+    g = torch.Generator().manual_seed(seed)
+    bias = torch.randn(B, H, Lq, Lk, generator=g, dtype=F64) * 1.5
+    bias[torch.rand(bias.shape, generator=g) < hide] = float("-inf")
+    if empty_row is not None:
+        bias[empty_row] = float("-inf")
+    return bias
+
+
+BIAS_CASES = [
+    dict(Lq=5, Lk=7, causal=False),
+    dict(Lq=6, Lk=6, causal=True),
+    dict(Lq=6, Lk=5, causal=False, empty=(0, 1, 2)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BIAS_CASES)))
+def test_bwd_bias_matches_finite_differences(case):
+    """Central differences of the forward oracle with the same bias."""
+    c = BIAS_CASES[case]
+    B, H, D = 1, 2, 4
+    q, k, v = rand(60 + case, B, H, c["Lq"], D), rand(70 + case, B, H, c["Lk"], D), \
+        rand(80 + case, B, H, c["Lk"], D)
+    dout = rand(90 + case, B, H, c["Lq"], D)
+    bias = make_bias(95 + case, B, H, c["Lq"], c["Lk"], empty_row=c.get("empty"))
+    kw = dict(is_causal=c["causal"], bias=bias, scale=0.6)
+    dq, dk, dv = oracle.sdpa_bwd_oracle(q, k, v, dout, **kw)
+    for name, got in (("q", dq), ("k", dk), ("v", dv)):
+        fd = finite_difference(q.clone(), k.clone(), v.clone(), dout, name, **kw)
+        np.testing.assert_allclose(got, fd, rtol=1e-6, atol=1e-8, err_msg=f"d{name}")
+    if "empty" in c:
+        assert np.all(dq[c["empty"]] == 0.0)
+
+
+def test_bwd_bias_matches_library_autograd_fp64():
+    """The library's math-backend SDPA in fp64 with a float attn_mask (added to the scaled
+    scores), differentiated by autograd; the bias broadcast over heads, -inf entries on
+    rows that keep some visible key."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    for seed, (B, H, Lq, Lk, D, causal, scale) in enumerate([
+            (2, 3, 13, 13, 16, True, None), (1, 2, 9, 21, 8, False, 0.37)]):
+        q, k, v = rand(seed + 400, B, H, Lq, D), rand(seed + 410, B, H, Lk, D), \
+            rand(seed + 420, B, H, Lk, D)
+        dout = rand(seed + 430, B, H, Lq, D)
+        bias = make_bias(seed + 440, B, 1, Lq, Lk)
+        bias[..., 0] = 0.0  # key 0 visible to every row
+        dq, dk, dv = oracle.sdpa_bwd_oracle(q, k, v, dout, is_causal=causal, scale=scale,
+                                            bias=bias)
+        qq, kk, vv = (t.clone().requires_grad_() for t in (q, k, v))
+        m = bias
+        if causal:
+            m = bias.masked_fill(~torch.ones(Lq, Lk, dtype=torch.bool).tril(), float("-inf"))
+        with sdpa_kernel(SDPBackend.MATH):
+            out = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=m,
+                                                                   scale=scale)
+        out.backward(dout)
+        np.testing.assert_allclose(dq, qq.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk, kk.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, vv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_bwd_bias_special_cases():
+    """A zero bias is no bias and a 0 / -inf bias is the boolean mask, bit for bit; a bias
+    constant along each row changes no gradient."""
+    B, H, Lq, Lk, D = 1, 2, 9, 11, 8
+    q, k, v = rand(501, B, H, Lq, D), rand(502, B, H, Lk, D), rand(503, B, H, Lk, D)
+    dout = rand(504, B, H, Lq, D)
+    ref = oracle.sdpa_bwd_oracle(q, k, v, dout, is_causal=True)
+    got = oracle.sdpa_bwd_oracle(q, k, v, dout, is_causal=True,
+                                 bias=torch.zeros(B, H, Lq, Lk, dtype=F64))
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+    mask = bernoulli_mask(505, (B, H, Lq, Lk), 0.5)
+    mask[..., 0] = True
+    ref = oracle.sdpa_bwd_oracle(q, k, v, dout, mask=mask)
+    zb = torch.zeros(B, H, Lq, Lk, dtype=F64).masked_fill(~mask, float("-inf"))
+    got = oracle.sdpa_bwd_oracle(q, k, v, dout, bias=zb)
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+    row_const = rand(506, B, H, Lq, 1).expand(B, H, Lq, Lk).contiguous()
+    ref = oracle.sdpa_bwd_oracle(q, k, v, dout, is_causal=True)
+    got = oracle.sdpa_bwd_oracle(q, k, v, dout, is_causal=True, bias=row_const)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12)

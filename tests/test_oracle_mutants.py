@@ -58,6 +58,13 @@ BWD_MUTANTS = {
     "bwd_p_unnormalised": ("pr[j] = any ? pr[j] / l : 0.0;", "pr[j] = any ? pr[j] : 0.0;"),
     "bwd_empty_row_not_zeroed": ("pr[j] = any ? pr[j] / l : 0.0;", "pr[j] = pr[j] / l;"),
     "bwd_dout_row_stride": ("ob + i * dos[2] + d * dos[3]) *", "ob + i * dos[3] + d * dos[3]) *"),
+    "bwd_bias_subtracted": ("pr[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];",
+                            "pr[j] -= bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];"),
+    "bwd_bias_transposed": ("pr[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];",
+                            "pr[j] += bias[b * bs[0] + h * bs[1] + j * bs[2] + i * bs[3]];"),
+    "bwd_bias_scaled": ("pr[j] += bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];",
+                        "pr[j] += scale * bias[b * bs[0] + h * bs[1] + i * bs[2] + j * bs[3]];"),
+    "bwd_bias_minus_inf_kept": ("            if (pr[j] == -INFINITY) continue;\n", ""),
 }
 
 
