@@ -340,6 +340,93 @@ int sdpa_bwd_check(const void* q, const void* k, const void* v, const void* out,
                    int is_causal, const uint8_t* mask, int dtype);
 
 /*
+ * sdpa_bwd_bias -- gradients dq, dk, dv of sdpa_fwd_bias, with the additive mask held
+ * constant (no gradient is formed for it).
+ *
+ * sdpa_bwd's chain rule with the forward's scores scale * q_i.k_j + bias[b,h,i,j]: only P
+ * changes, P[i,j] = exp(scale * q_i.k_j + bias[b,h,i,j] - lse[i]) (0 where the bias is
+ * -inf); dv, dP, delta, dS, dq and dk then follow as in sdpa_bwd.  The forward it
+ * differentiates is sdpa_fwd_bias: the naive module's masked fill before the softmax (the
+ * Hungarian edition of "Profiling in PyTorch" part 3), with the mask's entries generalised
+ * from 0 / -inf to any finite value or -inf.  The pages define no backward; this is the
+ * chain rule through that forward.
+ *
+ *   bias          device fp32, 4-byte aligned, addressed with the mask strides of
+ *                 `strides` (rank entries each, 0 broadcasts an axis, innermost 1); the
+ *                 same tensor, with the same values, that sdpa_fwd_bias used for lse.
+ *                 Entries must be finite or -inf.  NULL is the bias-free sdpa_bwd.
+ *   everything else
+ *                 exactly as in sdpa_bwd (lse from sdpa_fwd_bias on the same problem).
+ *
+ * Two kernel launches on `stream`, as sdpa_bwd; nothing allocated, freed or synchronised.
+ * Deterministic.  With all-zero bias the result equals sdpa_bwd's, bit for bit.
+ */
+int sdpa_bwd_bias(const void* q, const void* k, const void* v, const void* out,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  float* delta, int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                  int64_t D, const int64_t* strides, float scale, int is_causal,
+                  const float* bias, int dtype, void* stream);
+
+/* sdpa_bwd_bias_check -- the host-side validation of sdpa_bwd_bias alone (no stream, no
+ * HIP call, no device read). */
+int sdpa_bwd_bias_check(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, const void* dq, const void* dk,
+                        const void* dv, const float* delta, int rank, int64_t B, int64_t H,
+                        int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                        int is_causal, const float* bias, int dtype);
+
+/*
+ * sdpa_bwd_varlen -- gradients dq, dk, dv of sdpa_fwd_varlen (packed sequences).
+ *
+ * Each (sequence, head) is sdpa_bwd's problem on that sequence's rows alone, with the
+ * causal mode applied per sequence as in sdpa_fwd_varlen; no gradient flows across
+ * sequences.  Same rounding and determinism as sdpa_bwd.
+ *
+ *   q, out, dout, dq
+ *                 device [total_q, H, D] of `dtype` (bf16 or fp16); k, v, dk, dv device
+ *                 [total_k, H, D].  Any token and head strides, unit dim stride; bases and
+ *                 strides (bytes) multiples of 16.  Outputs must not overlap each other or
+ *                 any input.  The query-side tensors may be NULL when total_q == 0, the
+ *                 key-side ones when total_k == 0.
+ *   lse           device [H, total_q] contiguous floats written by sdpa_fwd_varlen for this
+ *                 problem.
+ *   delta         device [H, total_q] contiguous floats of caller-owned scratch (fp32
+ *                 delta[i] = sum_d dout[i,d] out[i,d]).
+ *   cu_seqlens_q, cu_seqlens_k, nseq
+ *                 as in sdpa_fwd_varlen (contents clamped on the device, never read out of
+ *                 bounds).
+ *   max_seqlen_q, max_seqlen_k
+ *                 upper bounds of every sequence's query and key length, at most total_q
+ *                 and total_k; they size the launches.  Rows of a longer sequence past them
+ *                 are not written.
+ *   total_q, total_k, H, D
+ *                 sizes; D in {32, 64, 96, 128}; (total + 64) times the token stride of q,
+ *                 dout, k and v (each with its own total) must stay below 2 GiB.
+ *   strides       24 element strides: (token, head, dim) for q, k, v, out, dout, dq, dk, dv.
+ *   scale, causal, dtype, stream
+ *                 as in sdpa_bwd (causal: an sdpa_causal mode).
+ *
+ * Two kernel launches on `stream`; nothing allocated, freed or synchronised.  Returns a
+ * status as sdpa_bwd does; nseq * H == 0 or max_seqlen_q + max_seqlen_k == 0 is a no-op.
+ */
+int sdpa_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    float* delta, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int64_t nseq, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t total_q,
+                    int64_t total_k, int64_t H, int64_t D, const int64_t* strides, float scale,
+                    int causal, int dtype, void* stream);
+
+/* sdpa_bwd_varlen_check -- the host-side validation of sdpa_bwd_varlen alone (no stream,
+ * no HIP call, no device read). */
+int sdpa_bwd_varlen_check(const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, const void* dq, const void* dk,
+                          const void* dv, const float* delta, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int64_t nseq, int64_t max_seqlen_q,
+                          int64_t max_seqlen_k, int64_t total_q, int64_t total_k, int64_t H,
+                          int64_t D, const int64_t* strides, float scale, int causal,
+                          int dtype);
+
+/*
  * Launch plan (host-only introspection of the tile scheduler of sdpa_fwd; sdpa_fwd_bias
  * takes the same tiles).
  *

@@ -27,7 +27,8 @@ SDPA_STATIC_WORKSPACE_BYTES = 16 << 20
 
 EXPORTS = ("sdpa_fwd", "sdpa_check", "sdpa_fwd_bias", "sdpa_fwd_bias_check", "sdpa_fwd_splitkv", "sdpa_fwd_splitkv_check",
            "sdpa_fwd_splitkv_workspace", "sdpa_fwd_splitkv_noalloc", "sdpa_fwd_varlen", "sdpa_fwd_varlen_check", "sdpa_bwd",
-           "sdpa_bwd_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
+           "sdpa_bwd_check", "sdpa_bwd_bias", "sdpa_bwd_bias_check", "sdpa_bwd_varlen",
+           "sdpa_bwd_varlen_check", "sdpa_strerror", "sdpa_plan", "sdpa_plan_item")
 
 
 class SdpaError(RuntimeError):
@@ -69,6 +70,16 @@ def load_library():
     lib.sdpa_bwd.restype = ctypes.c_int
     lib.sdpa_bwd_check.argtypes = bwd_common
     lib.sdpa_bwd_check.restype = ctypes.c_int
+    lib.sdpa_bwd_bias.argtypes = bwd_common + [vp]  # the bias takes the mask's place
+    lib.sdpa_bwd_bias.restype = ctypes.c_int
+    lib.sdpa_bwd_bias_check.argtypes = bwd_common
+    lib.sdpa_bwd_bias_check.restype = ctypes.c_int
+    bwd_varlen_common = [vp] * 12 + [i64] * 7 + [ctypes.POINTER(i64), ctypes.c_float,
+                                                 ctypes.c_int, ctypes.c_int]
+    lib.sdpa_bwd_varlen.argtypes = bwd_varlen_common + [vp]
+    lib.sdpa_bwd_varlen.restype = ctypes.c_int
+    lib.sdpa_bwd_varlen_check.argtypes = bwd_varlen_common
+    lib.sdpa_bwd_varlen_check.restype = ctypes.c_int
     varlen_common = [vp] * 7 + [i64] * 6 + [ctypes.POINTER(i64), ctypes.c_float, ctypes.c_int,
                                         ctypes.c_int]
     lib.sdpa_fwd_varlen.argtypes = varlen_common + [vp]
@@ -213,7 +224,7 @@ def _mask_view(mask, lead_shape, Lk):
 
 def sdpa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, delta=None, *, scale=None,
              is_causal=False, mask=None, stream=None):
-    """Gradients of the fused SDPA through the C ABI `sdpa_bwd` (bf16 only).
+    """Gradients of the fused SDPA through the C ABI `sdpa_bwd` (bf16 or fp16).
 
     q, k, v, mask, scale, is_causal: as passed to sdpa_fwd; out and lse: what sdpa_fwd
     returned for them; dout: the upstream gradient, shaped like out.  dq/dk/dv (shaped and
@@ -222,6 +233,29 @@ def sdpa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, delta=None, *, 
     `stream` (default: torch's current stream of q's device), nothing is synchronised.
     """
     _check_shapes(q, k, v, out, lse, mask)
+    return _bwd_call("sdpa_bwd", q, k, v, out, dout, lse, dq, dk, dv, delta, scale, is_causal,
+                     None if mask is None else _mask_view(mask, q.shape[:-1], k.shape[-2]),
+                     stream)
+
+
+def sdpa_bwd_bias(q, k, v, out, dout, lse, bias, dq=None, dk=None, dv=None, delta=None, *,
+                  scale=None, is_causal=False, stream=None):
+    """Gradients of sdpa_fwd_bias through the C ABI `sdpa_bwd_bias`, the bias held constant.
+
+    bias: the float32 tensor passed to sdpa_fwd_bias (broadcastable to q.shape[:-1] +
+    (Lk,)); out and lse: what sdpa_fwd_bias returned.  Otherwise as sdpa_bwd.  Returns
+    (dq, dk, dv)."""
+    if bias is None or bias.dtype != torch.float32:
+        raise TypeError("bias must be a float32 tensor")
+    _check_shapes(q, k, v, out, lse, bias)
+    return _bwd_call("sdpa_bwd_bias", q, k, v, out, dout, lse, dq, dk, dv, delta, scale,
+                     is_causal, bias.expand(*q.shape[:-1], k.shape[-2]), stream)
+
+
+def _bwd_call(entry, q, k, v, out, dout, lse, dq, dk, dv, delta, scale, is_causal, extra,
+              stream):
+    """Marshal the dense backward's arguments for `entry` (sdpa_bwd with the boolean mask
+    view `extra`, or sdpa_bwd_bias with the expanded bias `extra`; None for neither)."""
     for name, t, like in (("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
         if t is not None and (tuple(t.shape) != tuple(like.shape) or t.dtype != q.dtype or
                               t.device != q.device):
@@ -241,23 +275,76 @@ def sdpa_bwd(q, k, v, out, dout, lse, dq=None, dk=None, dv=None, delta=None, *, 
     B, H, Lq, Lk, D = _sizes(q, k)
     strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride(), *dout.stride(),
                *dq.stride(), *dk.stride(), *dv.stride()]
-    mask_ptr = None
-    if mask is not None:
-        m = _mask_view(mask, q.shape[:-1], Lk)
-        strides += list(m.stride())
-        mask_ptr = m.data_ptr()
-    else:
-        strides += [0] * rank
+    strides += [0] * rank if extra is None else list(extra.stride())
     arr = (ctypes.c_int64 * len(strides))(*strides)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
-        status = load_library().sdpa_bwd(
+        status = getattr(load_library(), entry)(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-            rank, B, H, Lq, Lk, D, arr, float(scale), causal_mode(is_causal), mask_ptr,
-            _DTYPES.get(q.dtype, -1), handle)
+            rank, B, H, Lq, Lk, D, arr, float(scale), causal_mode(is_causal),
+            None if extra is None else extra.data_ptr(), _DTYPES.get(q.dtype, -1), handle)
+    _raise_on(status)
+    return dq, dk, dv
+
+
+def sdpa_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, dq=None, dk=None, dv=None, delta=None, *, scale=None,
+                    is_causal=False, stream=None):
+    """Gradients of sdpa_fwd_varlen through the C ABI `sdpa_bwd_varlen` (bf16 or fp16).
+
+    q, k, v, cu_seqlens_q, cu_seqlens_k, scale, is_causal: as passed to sdpa_fwd_varlen;
+    out, lse: what it returned; dout shaped like out; max_seqlen_q / max_seqlen_k: int
+    bounds of the query and key lengths.  dq/dk/dv and delta ([H, total_q] float32
+    scratch) are allocated when not given.  Returns (dq, dk, dv)."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k and v must be [tokens, H, D]")
+    if tuple(k.shape) != tuple(v.shape) or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k and v must be [total_k, H, D] with q's H and D")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same nseq + 1 >= 1 entries")
+    if out is None or dout is None or lse is None:
+        raise ValueError("out, dout and the forward's lse are required")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    for name, t, like in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k),
+                          ("dv", dv, k)):
+        if t is not None and (tuple(t.shape) != tuple(like.shape) or t.dtype != q.dtype):
+            raise ValueError(f"{name} must match {'q' if like is q else 'k'} in shape and dtype")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t is not None and (tuple(t.shape) != (H, total_q) or t.dtype != torch.float32 or
+                              not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor [H, total_q]")
+    ts = (q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, dq, dk, dv, delta)
+    if any(t is not None and t.device.type != "cuda" for t in ts):
+        raise ValueError("sdpa_bwd_varlen runs on the GPU only: every tensor must be on a cuda device")
+    if len({t.device for t in ts if t is not None}) != 1:
+        raise ValueError("all tensors must be on the same device")
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    strides = [*q.stride(), *k.stride(), *v.stride(), *out.stride(), *dout.stride(),
+               *dq.stride(), *dk.stride(), *dv.stride()]
+    arr = (ctypes.c_int64 * 24)(*strides)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        status = load_library().sdpa_bwd_varlen(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1,
+            int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, H, D, arr, float(scale),
+            causal_mode(is_causal), _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return dq, dk, dv
 
@@ -448,6 +535,26 @@ def sdpa_bwd_check(ptrs, rank, B, H, Lq, Lk, D, strides, scale, is_causal, mask_
     arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
     return load_library().sdpa_bwd_check(*ptrs, rank, B, H, Lq, Lk, D, arr, float(scale),
                                          int(is_causal), mask_ptr, int(dtype))
+
+
+def sdpa_bwd_bias_check(ptrs, rank, B, H, Lq, Lk, D, strides, scale, is_causal, bias_ptr,
+                        dtype) -> int:
+    """The C ABI `sdpa_bwd_bias_check` on raw integers (as sdpa_bwd_check, with the bias
+    pointer in the mask's place).  Host-only."""
+    arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
+    return load_library().sdpa_bwd_bias_check(*ptrs, rank, B, H, Lq, Lk, D, arr, float(scale),
+                                              int(is_causal), bias_ptr, int(dtype))
+
+
+def sdpa_bwd_varlen_check(ptrs, nseq, max_seqlen_q, max_seqlen_k, total_q, total_k, H, D,
+                          strides, scale, causal, dtype) -> int:
+    """The C ABI `sdpa_bwd_varlen_check` on raw integers: ptrs = the 12 pointers (q, k, v,
+    out, dout, lse, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k) as ints, strides a list
+    of 24 ints.  Host-only."""
+    arr = (ctypes.c_int64 * len(strides))(*strides) if strides is not None else None
+    return load_library().sdpa_bwd_varlen_check(*ptrs, nseq, max_seqlen_q, max_seqlen_k, total_q,
+                                                total_k, H, D, arr, float(scale), int(causal),
+                                                int(dtype))
 
 
 def sdpa_check(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, rank, B, H, Lq, Lk, D, strides, scale,

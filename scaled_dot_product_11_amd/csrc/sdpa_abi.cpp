@@ -238,9 +238,140 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
     memcpy(p->sdk, s4[DK], sizeof p->sdk);
     memcpy(p->sdv, s4[DV], sizeof p->sdv);
     memcpy(p->sm, s4[M], sizeof p->sm);
+    p->bias = nullptr;
+    p->cu_q = p->cu_k = nullptr;
+    p->nseq = p->max_seqlen_q = p->max_seqlen_k = 0;
     p->scale = scale;
     p->causal = is_causal;
     p->dtype = dtype;
+    p->varlen = 0;
+  }
+  return SDPA_OK;
+}
+
+// The backward with an additive mask: sdpa_bwd's validation with the bias in the mask's
+// place (same stride rules); fp32, 4-byte aligned.
+int normalise_bwd_bias(const void* q, const void* k, const void* v, const void* out,
+                       const void* dout, const float* lse, const void* dq, const void* dk,
+                       const void* dv, const float* delta, int rank, int64_t B, int64_t H,
+                       int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                       int is_causal, const float* bias, int dtype, sdpa::BwdProblem* p) {
+  const int st = normalise_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, rank, B, H, Lq, Lk,
+                               D, strides, scale, is_causal,
+                               reinterpret_cast<const uint8_t*>(bias), dtype, p);
+  if (st != SDPA_OK) return st;
+  if (bias && !aligned(bias, 4)) return SDPA_ERR_ALIGN;
+  if (p) {
+    p->mask = nullptr;
+    p->bias = bias;
+  }
+  return SDPA_OK;
+}
+
+// The backward of packed sequences: tensors [tokens, H, D] with (token, head, dim) strides
+// for q, k, v, out, dout, dq, dk, dv; lse and delta [H, total_q].
+int normalise_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, const void* dq, const void* dk,
+                         const void* dv, const float* delta, const int32_t* cu_q,
+                         const int32_t* cu_k, int64_t nseq, int64_t max_seqlen_q,
+                         int64_t max_seqlen_k, int64_t total_q, int64_t total_k, int64_t H,
+                         int64_t D, const int64_t* strides, float scale, int causal, int dtype,
+                         sdpa::BwdProblem* p) {
+  if (nseq < 0 || H < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return SDPA_ERR_SHAPE;
+  if (nseq >= kMaxDim || H > kMaxDim || total_q > kMaxDim || total_k > kMaxDim)
+    return SDPA_ERR_SHAPE;
+  if (nseq != 0 && H > kMaxDim / nseq) return SDPA_ERR_SHAPE;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return SDPA_ERR_SHAPE;
+  if (H != 0 && total_q > kMaxDim / H) return SDPA_ERR_SHAPE;  // lse / delta [H, total_q]
+  if (!sdpa::bwd_head_dim_ok(D)) return SDPA_ERR_HEAD_DIM;
+  if (dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
+  if (!strides) return SDPA_ERR_NULL;
+  if (!isfinite(scale)) return SDPA_ERR_SCALE;
+  if (causal < SDPA_CAUSAL_NONE || causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
+  const int64_t heads = nseq * H;
+  const int64_t tq = (max_seqlen_q + sdpa::kBwdBlockQ - 1) / sdpa::kBwdBlockQ;
+  const int64_t tk = (max_seqlen_k + sdpa::kBwdBlockK - 1) / sdpa::kBwdBlockK;
+  if (heads != 0 && (tq > kMaxDim / heads || tk > kMaxDim / heads ||
+                     !launch_fits(heads * tq, sdpa::kThreadsBwdQ) ||
+                     !launch_fits(heads * tk, sdpa::kThreadsBwdK)))
+    return SDPA_ERR_SHAPE;  // grid sizes
+  // the dq kernel runs when some sequence may have query rows, the dkdv kernel when some
+  // may have keys; each reads the other side's rows too
+  const bool rows = heads != 0 && max_seqlen_q != 0;
+  const bool keys = heads != 0 && max_seqlen_k != 0;
+  const bool any = rows || keys;
+
+  enum { Q, K, V, O, DO, DQ, DK, DV, NT };
+  int64_t s4[NT][4];
+  for (int t = 0; t < NT; ++t) {
+    const int64_t* st = strides + 3 * t;
+    s4[t][0] = 0;
+    s4[t][1] = st[1];
+    s4[t][2] = st[0];
+    s4[t][3] = st[2];
+    for (int a = 0; a < 4; ++a)
+      if (s4[t][a] < 0) return SDPA_ERR_STRIDE;
+    if (s4[t][3] != 1) return SDPA_ERR_STRIDE;
+  }
+  if (any && (!cu_q || !cu_k)) return SDPA_ERR_NULL;
+  const void* bases[8] = {q, k, v, out, dout, dq, dk, dv};
+  for (int t = 0; t < 8; ++t) {
+    const bool key_side = t == K || t == V || t == DK || t == DV;
+    if (!any || (key_side ? total_k : total_q) == 0) continue;
+    if (!bases[t]) return SDPA_ERR_NULL;
+    if (!aligned(bases[t], 16)) return SDPA_ERR_ALIGN;
+    for (int a = 1; a < 3; ++a)
+      if ((s4[t][a] * 2) % 16 != 0) return SDPA_ERR_ALIGN;
+  }
+  if (any && total_q != 0 && (!lse || !delta)) return SDPA_ERR_NULL;
+  if ((lse && !aligned(lse, 4)) || (delta && !aligned(delta, 4)) ||
+      (cu_q && !aligned(cu_q, 4)) || (cu_k && !aligned(cu_k, 4)))
+    return SDPA_ERR_ALIGN;
+  // a sequence's streamed rows are addressed with 32-bit byte offsets from its first row
+  if (any) {
+    for (int t : {K, V})
+      if (s4[t][2] > kMaxDim / 2 / (total_k + sdpa::kBwdStep)) return SDPA_ERR_SHAPE;
+    for (int t : {Q, DO})
+      if (s4[t][2] > kMaxDim / 2 / (total_q + sdpa::kBwdStep)) return SDPA_ERR_SHAPE;
+  }
+
+  if (p) {
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->out = out;
+    p->dout = dout;
+    p->lse = lse;
+    p->delta = const_cast<float*>(delta);
+    p->dq = const_cast<void*>(dq);
+    p->dk = const_cast<void*>(dk);
+    p->dv = const_cast<void*>(dv);
+    p->mask = nullptr;
+    p->bias = nullptr;
+    p->cu_q = cu_q;
+    p->cu_k = cu_k;
+    p->B = 1;
+    p->H = H;
+    p->Lq = total_q;
+    p->Lk = total_k;
+    p->D = D;
+    p->nseq = nseq;
+    p->max_seqlen_q = max_seqlen_q;
+    p->max_seqlen_k = max_seqlen_k;
+    memcpy(p->sq, s4[Q], sizeof p->sq);
+    memcpy(p->sk, s4[K], sizeof p->sk);
+    memcpy(p->sv, s4[V], sizeof p->sv);
+    memcpy(p->so, s4[O], sizeof p->so);
+    memcpy(p->sdo, s4[DO], sizeof p->sdo);
+    memcpy(p->sdq, s4[DQ], sizeof p->sdq);
+    memcpy(p->sdk, s4[DK], sizeof p->sdk);
+    memcpy(p->sdv, s4[DV], sizeof p->sdv);
+    memset(p->sm, 0, sizeof p->sm);
+    p->scale = scale;
+    p->causal = causal;
+    p->dtype = dtype;
+    p->varlen = 1;
   }
   return SDPA_OK;
 }
@@ -573,6 +704,59 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* out, const
                                D, strides, scale, is_causal, mask, dtype, &p);
   if (st != SDPA_OK) return st;
   if (p.B * p.H * (p.Lq + p.Lk) == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  return sdpa::launch_bwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
+int sdpa_bwd_bias_check(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, const void* dq, const void* dk,
+                        const void* dv, const float* delta, int rank, int64_t B, int64_t H,
+                        int64_t Lq, int64_t Lk, int64_t D, const int64_t* strides, float scale,
+                        int is_causal, const float* bias, int dtype) {
+  return normalise_bwd_bias(q, k, v, out, dout, lse, dq, dk, dv, delta, rank, B, H, Lq, Lk, D,
+                            strides, scale, is_causal, bias, dtype, nullptr);
+}
+
+int sdpa_bwd_bias(const void* q, const void* k, const void* v, const void* out,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  float* delta, int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                  int64_t D, const int64_t* strides, float scale, int is_causal,
+                  const float* bias, int dtype, void* stream) {
+  sdpa::BwdProblem p;
+  const int st = normalise_bwd_bias(q, k, v, out, dout, lse, dq, dk, dv, delta, rank, B, H, Lq,
+                                    Lk, D, strides, scale, is_causal, bias, dtype, &p);
+  if (st != SDPA_OK) return st;
+  if (p.B * p.H * (p.Lq + p.Lk) == 0) return SDPA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
+  return sdpa::launch_bwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;
+}
+
+int sdpa_bwd_varlen_check(const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, const void* dq, const void* dk,
+                          const void* dv, const float* delta, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int64_t nseq, int64_t max_seqlen_q,
+                          int64_t max_seqlen_k, int64_t total_q, int64_t total_k, int64_t H,
+                          int64_t D, const int64_t* strides, float scale, int causal,
+                          int dtype) {
+  return normalise_bwd_varlen(q, k, v, out, dout, lse, dq, dk, dv, delta, cu_seqlens_q,
+                              cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k, total_q, total_k,
+                              H, D, strides, scale, causal, dtype, nullptr);
+}
+
+int sdpa_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    float* delta, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int64_t nseq, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t total_q,
+                    int64_t total_k, int64_t H, int64_t D, const int64_t* strides, float scale,
+                    int causal, int dtype, void* stream) {
+  sdpa::BwdProblem p;
+  const int st = normalise_bwd_varlen(q, k, v, out, dout, lse, dq, dk, dv, delta, cu_seqlens_q,
+                                      cu_seqlens_k, nseq, max_seqlen_q, max_seqlen_k, total_q,
+                                      total_k, H, D, strides, scale, causal, dtype, &p);
+  if (st != SDPA_OK) return st;
+  if (p.nseq * p.H == 0 || p.max_seqlen_q + p.max_seqlen_k == 0) return SDPA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!device_is_gfx950(s)) return SDPA_ERR_DEVICE;
   return sdpa::launch_bwd(p, s) == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE;

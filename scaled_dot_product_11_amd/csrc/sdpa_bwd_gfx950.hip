@@ -68,13 +68,70 @@ struct BwdArgs {
   void* dk;
   void* dv;
   const uint8_t* mask;
+  const float* bias;     // additive mask (fp32), addressed with the mask strides
+  const int32_t* cu_q;   // packed sequences: sequence s owns query tokens cu_q[s] ..
+  const int32_t* cu_k;   // cu_q[s+1]-1 and key tokens cu_k[s] .. cu_k[s+1]-1
   int64_t sq[3], sk[3], sv[3], so[3], sdo[3], sdq[3], sdk[3], sdv[3], sm[3];
   int32_t H, Lq, Lk, q_items, k_items, bh_count;
   float scale;       // multiplies dQ and dK
   float scale_log2;  // scale * log2(e): scores in base-2 units
   int32_t mask_vec8; // mask rows may be read 8 bytes at a time
-  int32_t coff;      // causal: key j visible to query i iff j <= i + coff
+  int32_t coff;      // causal (dense heads): key j visible to query i iff j <= i + coff
+  int32_t bottom_right;  // causal alignment of packed sequences, per sequence
+  int32_t bias_vec4;     // bias rows may be read 16 bytes at a time
 };
+
+// How a launch maps work items to rows: dense (b, h) heads of the strided tensors, or
+// head h of packed sequence s of [tokens, H, D] tensors (lse and delta laid out [H, total
+// query tokens]).  MK: 0 no mask, 1 boolean mask, 2 additive mask (dense heads only).
+enum { kBwdDense = 0, kBwdVarlen = 1 };
+
+// The rows of one (sequence or batch entry, head): element offsets of row 0 in each
+// tensor, of the mask, and of its lse / delta, its row counts and causal offset.  Packed
+// offsets are clamped into [0, total] and made non-decreasing, so that any contents of
+// cu_q / cu_k keep every access in bounds.
+struct BwdItem {
+  int64_t q, k, v, o, dO, dq, dk, dv, m, lse;
+  int Lq, Lk, coff;
+};
+
+template <int MODE>
+__device__ inline BwdItem bwd_item(const BwdArgs& a, int64_t bh) {
+  BwdItem it;
+  const int64_t s = bh / a.H, h = bh - (bh / a.H) * a.H;
+  if (MODE == kBwdDense) {
+    it.q = s * a.sq[0] + h * a.sq[1];
+    it.o = s * a.so[0] + h * a.so[1];
+    it.dO = s * a.sdo[0] + h * a.sdo[1];
+    it.dq = s * a.sdq[0] + h * a.sdq[1];
+    it.k = s * a.sk[0] + h * a.sk[1];
+    it.v = s * a.sv[0] + h * a.sv[1];
+    it.dk = s * a.sdk[0] + h * a.sdk[1];
+    it.dv = s * a.sdv[0] + h * a.sdv[1];
+    it.m = s * a.sm[0] + h * a.sm[1];
+    it.lse = bh * a.Lq;
+    it.Lq = a.Lq;
+    it.Lk = a.Lk;
+    it.coff = a.coff;
+  } else {
+    const int q_lo = min(max(a.cu_q[s], 0), a.Lq), q_hi = min(max(a.cu_q[s + 1], q_lo), a.Lq);
+    const int k_lo = min(max(a.cu_k[s], 0), a.Lk), k_hi = min(max(a.cu_k[s + 1], k_lo), a.Lk);
+    it.q = q_lo * a.sq[2] + h * a.sq[1];
+    it.o = q_lo * a.so[2] + h * a.so[1];
+    it.dO = q_lo * a.sdo[2] + h * a.sdo[1];
+    it.dq = q_lo * a.sdq[2] + h * a.sdq[1];
+    it.k = k_lo * a.sk[2] + h * a.sk[1];
+    it.v = k_lo * a.sv[2] + h * a.sv[1];
+    it.dk = k_lo * a.sdk[2] + h * a.sdk[1];
+    it.dv = k_lo * a.sdv[2] + h * a.sdv[1];
+    it.m = 0;
+    it.lse = h * a.Lq + q_lo;
+    it.Lq = q_hi - q_lo;
+    it.Lk = k_hi - k_lo;
+    it.coff = a.bottom_right ? it.Lk - it.Lq : 0;
+  }
+  return it;
+}
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -200,9 +257,10 @@ struct StageMap {
 //   dQ^T    += K^T dS^T          (K^T by transposed reads, dS^T rounded to the input type)
 // LDS stage: K row copy | K transposed-read copy | V row copy.
 // ---------------------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool MASK>
+template <typename E, int D, bool CAUSAL, int MK, int MODE>
 __global__ __launch_bounds__(kThreadsBwdQ) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq(BwdArgs a) {
+  constexpr bool MASK = MK == 1, BIAS = MK == 2;
   typedef typename Vec16<E>::v8 v8;
   constexpr int BN = kBwdStep;
   constexpr int NT = kThreadsBwdQ;
@@ -224,20 +282,23 @@ void bwd_dq(BwdArgs a) {
 
   int64_t bh, qt;
   decode_item(blockIdx.x, a.bh_count, a.q_items, CAUSAL, &bh, &qt);
-  const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + b * a.sq[0] + h * a.sq[1];
-  const uint16_t* ob = static_cast<const uint16_t*>(a.out) + b * a.so[0] + h * a.so[1];
-  const uint16_t* dob = static_cast<const uint16_t*>(a.dout) + b * a.sdo[0] + h * a.sdo[1];
-  const char* kb = static_cast<const char*>(a.k) + 2 * (b * a.sk[0] + h * a.sk[1]);
-  const char* vb = static_cast<const char*>(a.v) + 2 * (b * a.sv[0] + h * a.sv[1]);
-  uint16_t* dqb = static_cast<uint16_t*>(a.dq) + b * a.sdq[0] + h * a.sdq[1];
-  const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
-
+  const BwdItem it = bwd_item<MODE>(a, bh);
+  const int Lq = it.Lq, Lk = it.Lk;
   const int q0 = int(qt) * kBwdBlockQ;
+  if (MODE == kBwdVarlen && q0 >= Lq) return;  // a tile past this sequence's rows
+  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + it.q;
+  const uint16_t* ob = static_cast<const uint16_t*>(a.out) + it.o;
+  const uint16_t* dob = static_cast<const uint16_t*>(a.dout) + it.dO;
+  const char* kb = static_cast<const char*>(a.k) + 2 * it.k;
+  const char* vb = static_cast<const char*>(a.v) + 2 * it.v;
+  uint16_t* dqb = static_cast<uint16_t*>(a.dq) + it.dq;
+  const uint8_t* mb = MASK ? a.mask + it.m : nullptr;
+  const float* bb = BIAS ? a.bias + it.m : nullptr;
+
   const int qw = q0 + 32 * wave;
   const int qi = qw + li;
-  const bool q_ok = qi < a.Lq;
-  const bool wave_live = qw < a.Lq;
+  const bool q_ok = qi < Lq;
+  const bool wave_live = qw < Lq;
 
   // Q^T and dO^T operands (chunk c = head dims 16c..16c+15, half hf supplies 8 of them),
   // and delta = dO . out of this row from the same halves of dO and out.
@@ -258,13 +319,13 @@ void bwd_dq(BwdArgs a) {
     for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf(float(dof[c][e]), float(of[e]), dpart);
   }
   const float delta = pair_sum(dpart);
-  const float lse2 = q_ok ? lse_base2(a.lse[bh * a.Lq + qi]) : INFINITY;
-  if (q_ok && hf == 0) a.delta[bh * a.Lq + qi] = delta;
+  const float lse2 = q_ok ? lse_base2(a.lse[it.lse + qi]) : INFINITY;
+  if (q_ok && hf == 0) a.delta[it.lse + qi] = delta;
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  const int coff = a.coff;
-  int kend = a.Lk;
-  if (CAUSAL) kend = max(0, min(kend, min(q0 + kBwdBlockQ, a.Lq) + coff));
+  const int coff = it.coff;
+  int kend = Lk;
+  if (CAUSAL) kend = max(0, min(kend, min(q0 + kBwdBlockQ, Lq) + coff));
   const int ntiles = (kend + BN - 1) / BN;
   const int wlast = qw + 31 + coff;  // last key any row of the wave may see (causal)
   const int wtiles = !wave_live ? 0 : CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
@@ -274,8 +335,8 @@ void bwd_dq(BwdArgs a) {
   // tile index past the staged range is sent beyond the extent).  Offsets stay below
   // 2^31: (Lk + 64) rows of K and of V span less than 2 GiB.
   const int k_rowb = int(a.sk[2]) * 2, v_rowb = int(a.sv[2]) * 2;
-  const int k_ext = a.Lk > 0 ? (a.Lk - 1) * k_rowb + 2 * D : 0;
-  const int v_ext = a.Lk > 0 ? (a.Lk - 1) * v_rowb + 2 * D : 0;
+  const int k_ext = Lk > 0 ? (Lk - 1) * k_rowb + 2 * D : 0;
+  const int v_ext = Lk > 0 ? (Lk - 1) * v_rowb + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, k_ext, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, v_ext, kBufferFlags);
   const StageMap<BN, DG, NT> sm_(tid);
@@ -340,13 +401,38 @@ void bwd_dq(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // x = S scale log2e - lse2 in base-2 units; hidden keys -> -inf.
+    // x = S scale log2e (+ bias log2e) - lse2 in base-2 units; hidden keys -> -inf.
     float x[2][16];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[kt][r] = __builtin_fmaf(s[kt][r], c2, -lse2);
-    const bool edge = (CAUSAL && k0 + BN - 1 > qw + coff) || (k0 + BN > a.Lk);
+    if (BIAS && q_ok) {
+      // the lane's runs of 8 keys: register r of sub-tile kt is key k0 + 32kt + 16(r/8) +
+      // 8hf + r%8; keys past Lk read nothing (they are hidden below)
+      const float* brow = bb + int64_t(qi) * a.sm[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int key0 = k0 + 32 * kt + 16 * g + 8 * hf;
+          if (a.bias_vec4 && key0 + 8 <= Lk) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(brow + key0);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(brow + key0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[kt][8 * g + e] = __builtin_fmaf(lo[e], kLog2e, x[kt][8 * g + e]);
+              x[kt][8 * g + e + 4] = __builtin_fmaf(hi[e], kLog2e, x[kt][8 * g + e + 4]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (key0 + e < Lk)
+                x[kt][8 * g + e] = __builtin_fmaf(brow[key0 + e], kLog2e, x[kt][8 * g + e]);
+          }
+        }
+    }
+    const bool edge = (CAUSAL && k0 + BN - 1 > qw + coff) || (k0 + BN > Lk);
     if (edge || MASK) {
       uint64_t mbits[4] = {~0ull, ~0ull, ~0ull, ~0ull};
       if (MASK && q_ok) {
@@ -354,12 +440,12 @@ void bwd_dq(BwdArgs a) {
 #pragma unroll
         for (int run = 0; run < 4; ++run) {
           const int key0 = k0 + 32 * (run >> 1) + 16 * (run & 1) + 8 * hf;
-          if (a.mask_vec8 && key0 + 8 <= a.Lk) {
+          if (a.mask_vec8 && key0 + 8 <= Lk) {
             mbits[run] = *reinterpret_cast<const uint64_t*>(mrow + key0);
           } else {
             uint64_t w = 0;
             for (int e = 0; e < 8; ++e)
-              if (key0 + e < a.Lk) w |= uint64_t(mrow[key0 + e]) << (8 * e);
+              if (key0 + e < Lk) w |= uint64_t(mrow[key0 + e]) << (8 * e);
             mbits[run] = w;
           }
         }
@@ -369,7 +455,7 @@ void bwd_dq(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
-          bool hide = key >= a.Lk;
+          bool hide = key >= Lk;
           if (CAUSAL) hide = hide || key > qi + coff;
           if (MASK) hide = hide || ((mbits[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xff) == 0;
           if (hide) x[kt][r] = -INFINITY;
@@ -423,7 +509,7 @@ void bwd_dq(BwdArgs a) {
   char* ot = lds + wave * 32 * RP;
   tile_to_lds<E, D, RP>(ot, dq, a.scale, li, hf);
   __syncthreads();
-  rows_to_global<D, RP>(ot, lane, qw, a.Lq, dqb, a.sdq[2]);
+  rows_to_global<D, RP>(ot, lane, qw, Lq, dqb, a.sdq[2]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -443,9 +529,10 @@ void bwd_dq(BwdArgs a) {
 // The P waves also stage the tiles.  LDS stage: Q row copy | Q transposed-read copy | dO row copy | dO transposed-read copy |
 // lse2[64] | delta[64].
 // ---------------------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool MASK>
+template <typename E, int D, bool CAUSAL, int MK, int MODE>
 __global__ __launch_bounds__(kThreadsBwdK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv(BwdArgs a) {
+  constexpr bool MASK = MK == 1, BIAS = MK == 2;
   typedef typename Vec16<E>::v8 v8;
   constexpr int BQ = kBwdStep;
   constexpr int NT = kThreadsBwdK / 2;  // the P waves stage the tiles
@@ -473,22 +560,25 @@ void bwd_dkdv(BwdArgs a) {
   // see the most queries, so the heaviest items are issued first.
   int64_t bh, kt_idx;
   decode_item(blockIdx.x, a.bh_count, a.k_items, false, &bh, &kt_idx);
-  const int64_t b = bh / a.H, h = bh - (bh / a.H) * a.H;
-  const char* qb = static_cast<const char*>(a.q) + 2 * (b * a.sq[0] + h * a.sq[1]);
-  const char* dob = static_cast<const char*>(a.dout) + 2 * (b * a.sdo[0] + h * a.sdo[1]);
-  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.sk[0] + h * a.sk[1];
-  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + b * a.sv[0] + h * a.sv[1];
-  uint16_t* dkb = static_cast<uint16_t*>(a.dk) + b * a.sdk[0] + h * a.sdk[1];
-  uint16_t* dvb = static_cast<uint16_t*>(a.dv) + b * a.sdv[0] + h * a.sdv[1];
-  const uint8_t* mb = MASK ? a.mask + b * a.sm[0] + h * a.sm[1] : nullptr;
-  const float* lse_h = a.lse + bh * a.Lq;
-  const float* del_h = a.delta + bh * a.Lq;
-
+  const BwdItem it = bwd_item<MODE>(a, bh);
+  const int Lq = it.Lq, Lk = it.Lk;
   const int k0 = int(kt_idx) * kBwdBlockK;
+  if (MODE == kBwdVarlen && k0 >= Lk) return;  // a tile past this sequence's keys
+  const char* qb = static_cast<const char*>(a.q) + 2 * it.q;
+  const char* dob = static_cast<const char*>(a.dout) + 2 * it.dO;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + it.k;
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + it.v;
+  uint16_t* dkb = static_cast<uint16_t*>(a.dk) + it.dk;
+  uint16_t* dvb = static_cast<uint16_t*>(a.dv) + it.dv;
+  const uint8_t* mb = MASK ? a.mask + it.m : nullptr;
+  const float* bb = BIAS ? a.bias + it.m : nullptr;
+  const float* lse_h = a.lse + it.lse;
+  const float* del_h = a.delta + it.lse;
+
   const int kw = k0 + 32 * (wave & 3);
   const int kj = kw + li;
-  const bool k_ok = kj < a.Lk;
-  const bool wave_live = kw < a.Lk;
+  const bool k_ok = kj < Lk;
+  const bool wave_live = kw < Lk;
 
   // K^T right operand of S (both waves) and V^T right operand of dP (dS wave): column =
   // this lane's key, half hf supplies head dims 16c + 8hf .. +7 of chunk c.
@@ -507,13 +597,13 @@ void bwd_dkdv(BwdArgs a) {
 
   // Query tiles of the walk: with a causal mask, queries i with i + coff < k0 see none of
   // the keys.
-  const int coff = a.coff;
-  const int ntiles = (a.Lq + BQ - 1) / BQ;
+  const int coff = it.coff;
+  const int ntiles = (Lq + BQ - 1) / BQ;
   const int tbeg = CAUSAL ? min(max(0, k0 - coff) / BQ, ntiles) : 0;
 
   const int q_rowb = int(a.sq[2]) * 2, d_rowb = int(a.sdo[2]) * 2;
-  const int q_ext = a.Lq > 0 ? (a.Lq - 1) * q_rowb + 2 * D : 0;
-  const int d_ext = a.Lq > 0 ? (a.Lq - 1) * d_rowb + 2 * D : 0;
+  const int q_ext = Lq > 0 ? (Lq - 1) * q_rowb + 2 * D : 0;
+  const int d_ext = Lq > 0 ? (Lq - 1) * d_rowb + 2 * D : 0;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qb, 0, q_ext, kBufferFlags);
   const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, d_ext, kBufferFlags);
   const StageMap<BQ, DG, NT> sm_(tid);  // the P waves' threads, tid < NT
@@ -531,7 +621,7 @@ void bwd_dkdv(BwdArgs a) {
       }
     if (tid < 2 * BQ) {
       const int row = t * BQ + (tid & (BQ - 1));
-      const bool ok = live && row < a.Lq;
+      const bool ok = live && row < Lq;
       if (tid < BQ) rowval = ok ? lse_base2(lse_h[row]) : INFINITY;
       else rowval = ok ? del_h[row] : 0.f;
     }
@@ -613,10 +703,12 @@ void bwd_dkdv(BwdArgs a) {
             const int i = 2 * e + u, r = 8 * g + i;
             const int qrow = qt0 + qc + i;
             float xv = __builtin_fmaf(sc[r], c2, -(i < 4 ? l0[i] : l1[i - 4]));
+            if (BIAS && k_ok && qrow < Lq)  // additive mask, in base-2 units
+              xv = __builtin_fmaf(bb[int64_t(qrow) * a.sm[2] + kj], kLog2e, xv);
             if (edge || MASK) {
               bool hide = false;
               if (CAUSAL) hide = kj > qrow + coff;
-              if (MASK) hide = hide || !k_ok || qrow >= a.Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
+              if (MASK) hide = hide || !k_ok || qrow >= Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
               if (hide) xv = -INFINITY;
             }
             const float p = exp2_fast(xv);
@@ -672,30 +764,39 @@ void bwd_dkdv(BwdArgs a) {
   tile_to_lds<E, D, RP>(ot, acc, ds_wave ? a.scale : 1.f, li, hf);
   __syncthreads();
   if (ds_wave)
-    rows_to_global<D, RP>(ot, lane, kw, a.Lk, dkb, a.sdk[2]);
+    rows_to_global<D, RP>(ot, lane, kw, Lk, dkb, a.sdk[2]);
   else
-    rows_to_global<D, RP>(ot, lane, kw, a.Lk, dvb, a.sdv[2]);
+    rows_to_global<D, RP>(ot, lane, kw, Lk, dvb, a.sdv[2]);
 }
 
-template <typename E, int D, bool CAUSAL, bool MASK>
+template <typename E, int D, bool CAUSAL, int MK, int MODE>
 hipError_t launch_pair(const BwdArgs& a, unsigned grid_q, unsigned grid_k, hipStream_t s) {
   void* args[] = {const_cast<BwdArgs*>(&a)};
   if (grid_q) {
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq<E, D, CAUSAL, MASK>),
-                                         dim3(grid_q), dim3(kThreadsBwdQ), args, 0, s);
+    const hipError_t e =
+        hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq<E, D, CAUSAL, MK, MODE>),
+                        dim3(grid_q), dim3(kThreadsBwdQ), args, 0, s);
     if (e != hipSuccess) return e;
   }
   if (grid_k)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv<E, D, CAUSAL, MASK>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv<E, D, CAUSAL, MK, MODE>),
                            dim3(grid_k), dim3(kThreadsBwdK), args, 0, s);
   return hipSuccess;
 }
 
+template <typename E, int D, bool CAUSAL>
+hipError_t launch_bwd_c(const BwdArgs& a, bool varlen, unsigned gq, unsigned gk, hipStream_t s) {
+  if (varlen) return launch_pair<E, D, CAUSAL, 0, kBwdVarlen>(a, gq, gk, s);
+  if (a.mask) return launch_pair<E, D, CAUSAL, 1, kBwdDense>(a, gq, gk, s);
+  if (a.bias) return launch_pair<E, D, CAUSAL, 2, kBwdDense>(a, gq, gk, s);
+  return launch_pair<E, D, CAUSAL, 0, kBwdDense>(a, gq, gk, s);
+}
+
 template <typename E, int D>
-hipError_t launch_bwd_d(const BwdArgs& a, bool causal, unsigned gq, unsigned gk, hipStream_t s) {
-  const bool m = a.mask != nullptr;
-  if (causal) return m ? launch_pair<E, D, true, true>(a, gq, gk, s) : launch_pair<E, D, true, false>(a, gq, gk, s);
-  return m ? launch_pair<E, D, false, true>(a, gq, gk, s) : launch_pair<E, D, false, false>(a, gq, gk, s);
+hipError_t launch_bwd_d(const BwdArgs& a, bool causal, bool varlen, unsigned gq, unsigned gk,
+                        hipStream_t s) {
+  return causal ? launch_bwd_c<E, D, true>(a, varlen, gq, gk, s)
+                : launch_bwd_c<E, D, false>(a, varlen, gq, gk, s);
 }
 
 }  // namespace
@@ -713,6 +814,9 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   a.dk = p.dk;
   a.dv = p.dv;
   a.mask = p.mask;
+  a.bias = p.bias;
+  a.cu_q = p.cu_q;
+  a.cu_k = p.cu_k;
   for (int i = 0; i < 3; ++i) {
     a.sq[i] = p.sq[i];
     a.sk[i] = p.sk[i];
@@ -727,29 +831,36 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   a.H = int32_t(p.H);
   a.Lq = int32_t(p.Lq);
   a.Lk = int32_t(p.Lk);
-  a.bh_count = int32_t(p.B * p.H);
-  a.q_items = int32_t((p.Lq + kBwdBlockQ - 1) / kBwdBlockQ);
-  a.k_items = int32_t((p.Lk + kBwdBlockK - 1) / kBwdBlockK);
+  // dense: B*H heads of Lq query and Lk key rows; packed: nseq*H heads of at most
+  // max_seqlen_q / max_seqlen_k rows
+  const int64_t qrows = p.varlen ? p.max_seqlen_q : p.Lq;
+  const int64_t krows = p.varlen ? p.max_seqlen_k : p.Lk;
+  a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);
+  a.q_items = int32_t((qrows + kBwdBlockQ - 1) / kBwdBlockQ);
+  a.k_items = int32_t((krows + kBwdBlockK - 1) / kBwdBlockK);
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
                 p.sm[1] % 8 == 0 && p.sm[2] % 8 == 0;
   a.coff = p.causal == 2 ? int32_t(p.Lk - p.Lq) : 0;
+  a.bottom_right = p.causal == 2;
+  a.bias_vec4 = p.bias && (reinterpret_cast<uintptr_t>(p.bias) % 16 == 0) && p.sm[0] % 4 == 0 &&
+                p.sm[1] % 4 == 0 && p.sm[2] % 4 == 0;
   const unsigned gq = unsigned(int64_t(a.q_items) * a.bh_count);
   const unsigned gk = unsigned(int64_t(a.k_items) * a.bh_count);
   const bool causal = p.causal != 0;
   if (p.dtype == 2)
     switch (p.D) {
-      case 32: return launch_bwd_d<_Float16, 32>(a, causal, gq, gk, stream);
-      case 64: return launch_bwd_d<_Float16, 64>(a, causal, gq, gk, stream);
-      case 96: return launch_bwd_d<_Float16, 96>(a, causal, gq, gk, stream);
-      default: return launch_bwd_d<_Float16, 128>(a, causal, gq, gk, stream);
+      case 32: return launch_bwd_d<_Float16, 32>(a, causal, p.varlen != 0, gq, gk, stream);
+      case 64: return launch_bwd_d<_Float16, 64>(a, causal, p.varlen != 0, gq, gk, stream);
+      case 96: return launch_bwd_d<_Float16, 96>(a, causal, p.varlen != 0, gq, gk, stream);
+      default: return launch_bwd_d<_Float16, 128>(a, causal, p.varlen != 0, gq, gk, stream);
     }
   switch (p.D) {
-    case 32: return launch_bwd_d<__bf16, 32>(a, causal, gq, gk, stream);
-    case 64: return launch_bwd_d<__bf16, 64>(a, causal, gq, gk, stream);
-    case 96: return launch_bwd_d<__bf16, 96>(a, causal, gq, gk, stream);
-    default: return launch_bwd_d<__bf16, 128>(a, causal, gq, gk, stream);
+    case 32: return launch_bwd_d<__bf16, 32>(a, causal, p.varlen != 0, gq, gk, stream);
+    case 64: return launch_bwd_d<__bf16, 64>(a, causal, p.varlen != 0, gq, gk, stream);
+    case 96: return launch_bwd_d<__bf16, 96>(a, causal, p.varlen != 0, gq, gk, stream);
+    default: return launch_bwd_d<__bf16, 128>(a, causal, p.varlen != 0, gq, gk, stream);
   }
 }
 

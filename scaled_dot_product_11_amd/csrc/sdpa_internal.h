@@ -178,15 +178,21 @@ struct BwdProblem {
   void* dk;
   void* dv;
   const uint8_t* mask;
+  const float* bias;     // additive mask, addressed with the sm strides (never with mask)
+  const int32_t* cu_q;   // packed sequences (varlen != 0): nseq + 1 query offsets
+  const int32_t* cu_k;   // and key offsets; Lq / Lk are then the total token counts
   int64_t B, H, Lq, Lk, D;
+  int64_t nseq, max_seqlen_q, max_seqlen_k;
+  // dense: (batch, head, row, dim) strides; packed: (0, head, token, dim)
   int64_t sq[4], sk[4], sv[4], so[4], sdo[4], sdq[4], sdk[4], sdv[4], sm[4];
   float scale;
   int causal;
   int dtype;  // 1 bf16, 2 fp16
+  int varlen;
 };
 
-// Launches the dQ kernel (B*H*Lq > 0) and then the dK/dV kernel (B*H*Lk > 0) on
-// `stream`.  p must already be validated.  Returns a hipError_t.
+// Launches the dQ kernel and then the dK/dV kernel on `stream` (each only when it has
+// rows to cover).  p must already be validated.  Returns a hipError_t.
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
 
 }  // namespace sdpa

@@ -549,3 +549,104 @@ def test_grid_limits_follow_the_launched_tile():
     assert c(**big) == OK                          # 67043328 rows
     assert c(**dict(big, Lq=1024, strides=[64 * 1024 * 128, 1024 * 128, 128, 1] + big["strides"][4:12]
                     + [64 * 1024 * 128, 1024 * 128, 128, 1])) == SHAPE  # 2^26 rows
+
+
+# ---- sdpa_bwd_bias_check and sdpa_bwd_varlen_check ----------------------------------------
+
+def test_bwd_bias_check():
+    def bb(bias_ptr=A + 0xA0000, **kw):
+        a = bargs(mask=True, **kw)
+        a.pop("mask_ptr")
+        return sd.sdpa_bwd_bias_check(bias_ptr=bias_ptr, **a)
+    assert bb() == OK
+    assert bb(bias_ptr=None) == OK                   # no bias: sdpa_bwd's problem
+    assert bb(bias_ptr=A + 4) == OK                  # fp32 bias: 4-byte alignment suffices
+    assert bb(bias_ptr=A + 2) == ALIGN
+    assert bb(D=256) == HEAD
+    assert bb(dtype=sd.SDPA_F32) == DTYPE
+    assert bb(is_causal=3) == CAUSAL_ERR
+    a = bargs(mask=True)
+    a.pop("mask_ptr")
+    a["strides"] = list(a["strides"])
+    a["strides"][35] = 2                             # the bias key stride must be 1
+    assert sd.sdpa_bwd_bias_check(bias_ptr=A, **a) == STRIDE
+    a["strides"][35], a["strides"][32] = 1, -4       # none negative
+    assert sd.sdpa_bwd_bias_check(bias_ptr=A, **a) == STRIDE
+    a["strides"][32] = 0                             # 0 broadcasts
+    assert sd.sdpa_bwd_bias_check(bias_ptr=A, **a) == OK
+
+
+def bvargs(nseq=3, max_q=50, max_k=40, total_q=100, total_k=90, H=4, D=64,
+           dtype=sd.SDPA_BF16, **over):
+    """Arguments of sdpa_bwd_varlen_check: q, k, v, out, dout, lse, dq, dk, dv, delta, cu_q,
+    cu_k; [tokens, H, D] tensors."""
+    t = [H * D, D, 1]
+    a = dict(ptrs=[A + i * 0x10000 for i in range(12)], nseq=nseq, max_seqlen_q=max_q,
+             max_seqlen_k=max_k, total_q=total_q, total_k=total_k, H=H, D=D, strides=t * 8,
+             scale=0.125, causal=2, dtype=dtype)
+    a.update(over)
+    return a
+
+
+def bvcheck(**kw):
+    return sd.sdpa_bwd_varlen_check(**kw)
+
+
+def test_bwd_varlen_check():
+    assert bvcheck(**bvargs()) == OK
+    assert bvcheck(**bvargs(dtype=sd.SDPA_F16, D=128)) == OK
+    assert bvcheck(**bvargs(D=96)) == OK and bvcheck(**bvargs(D=32)) == OK
+    assert bvcheck(**bvargs(D=256)) == HEAD
+    assert bvcheck(**bvargs(dtype=sd.SDPA_F32)) == DTYPE
+    assert bvcheck(**bvargs(causal=3)) == CAUSAL_ERR
+    assert bvcheck(**bvargs(nseq=-1)) == SHAPE
+    assert bvcheck(**bvargs(max_q=101)) == SHAPE     # longer than every query token
+    assert bvcheck(**bvargs(max_k=91)) == SHAPE      # longer than every key token
+    assert bvcheck(**bvargs(strides=None)) == NULL
+    assert bvcheck(**bvargs(scale=float("nan"))) == SCALE
+    for i in range(12):                              # every pointer is required
+        a = bvargs()
+        a["ptrs"] = list(a["ptrs"])
+        a["ptrs"][i] = None
+        assert bvcheck(**a) == NULL, i
+    for i in range(12):                              # 16-byte tensors, 4-byte lse/delta/offsets
+        a = bvargs()
+        a["ptrs"] = list(a["ptrs"])
+        a["ptrs"][i] = A + 4
+        assert bvcheck(**a) == (OK if i in (5, 9, 10, 11) else ALIGN), i
+    s = bvargs()["strides"]
+    for t in range(8):                               # (token, head, dim) per tensor
+        for idx, val, want in ((2, 2, STRIDE), (0, -64, STRIDE), (0, 68, ALIGN), (1, 60, ALIGN)):
+            a = bvargs()
+            a["strides"] = list(s)
+            a["strides"][3 * t + idx] = val
+            assert bvcheck(**a) == want, (t, idx, val)
+    # streamed rows of a sequence (plus a tile) must span less than 2 GiB
+    assert bvcheck(**bvargs(total_q=2 ** 20, max_q=64, strides=[1024, 128, 1] * 8, D=128)) == SHAPE
+    assert bvcheck(**bvargs(total_q=2 ** 20, max_q=64, strides=[512, 128, 1] * 8, D=128)) == OK
+    # a side with no tokens needs no pointers on that side
+    a = bvargs(total_q=0, max_q=0)
+    a["ptrs"] = [None if i in (0, 3, 4, 5, 6, 9) else p for i, p in enumerate(a["ptrs"])]
+    assert bvcheck(**a) == OK
+    a = bvargs(total_k=0, max_k=0)
+    a["ptrs"] = [None if i in (1, 2, 7, 8) else p for i, p in enumerate(a["ptrs"])]
+    assert bvcheck(**a) == OK
+    assert bvcheck(**bvargs(nseq=0, max_q=0, max_k=0, total_q=0, total_k=0,
+                            ptrs=[None] * 12)) == OK
+
+
+def test_bwd_bias_and_varlen_reject_before_any_device_call():
+    import ctypes
+    lib = sd.load_library()
+    a = bargs(D=256)
+    arr = (ctypes.c_int64 * 36)(*a["strides"])
+    assert lib.sdpa_bwd_bias(*a["ptrs"], 4, 2, 3, 100, 90, 256, arr, 0.125, 1, None, 1,
+                             None) == HEAD
+    assert lib.sdpa_bwd_bias(*([None] * 10), 4, 0, 3, 100, 90, 64, arr, 0.125, 1, None, 1,
+                             None) == OK  # B == 0: nothing to do
+    v = bvargs(D=256)
+    varr = (ctypes.c_int64 * 24)(*v["strides"])
+    assert lib.sdpa_bwd_varlen(*v["ptrs"], 3, 50, 40, 100, 90, 4, 256, varr, 0.125, 2, 1,
+                               None) == HEAD
+    assert lib.sdpa_bwd_varlen(*([None] * 12), 0, 0, 0, 0, 0, 4, 64, varr, 0.125, 2, 1,
+                               None) == OK  # no sequences: nothing to do

@@ -4,14 +4,16 @@ A fused backend runs the whole forward as one kernel ("PyTorch 프로파일링 (
 table of kernels per forward: one each for the efficient, flash and cuDNN backends, against
 five to twenty for the unfused ones).  Expected here: sdpa_fwd (any dtype, mask kind or
 causal mode), sdpa_fwd_bias and sdpa_fwd_varlen launch exactly one kernel; sdpa_fwd_splitkv
-two (the key chunks, then their merge); sdpa_bwd two (dq with delta, then dk and dv).
+two (the key chunks, then their merge); sdpa_bwd, sdpa_bwd_bias and sdpa_bwd_varlen two
+(dq with delta, then dk and dv).
 Outputs are preallocated, so no other kernel runs inside the profiled region.
 """
 import pytest
 import torch
 
 import workloads as W
-from scaled_dot_product_11_amd import (sdpa_bwd, sdpa_fwd, sdpa_fwd_bias, sdpa_fwd_splitkv,
+from scaled_dot_product_11_amd import (sdpa_bwd, sdpa_bwd_bias, sdpa_bwd_varlen, sdpa_fwd,
+                                       sdpa_fwd_bias, sdpa_fwd_splitkv,
                                        sdpa_fwd_splitkv_workspace, sdpa_fwd_varlen)
 from scaled_dot_product_11_amd._binding import _DTYPES
 
@@ -111,4 +113,28 @@ def test_backward_is_two_kernels(profiler_sees_kernels):
     delta = torch.empty_like(lse)
     names = kernels_of(lambda: sdpa_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta,
                                         is_causal=True))
+    assert len(names) == 2 and len(ours(names)) == 2, names
+
+
+def test_bias_backward_is_two_kernels(profiler_sees_kernels):
+    q, k, v = small(D=128)
+    bias = torch.randn(1, 3, q.shape[2], k.shape[2], device=DEV)
+    out, lse = sdpa_fwd_bias(q, k, v, bias, is_causal=True)
+    dout = torch.randn_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+    names = kernels_of(lambda: sdpa_bwd_bias(q, k, v, out, dout, lse, bias, dq, dk, dv, delta,
+                                             is_causal=True))
+    assert len(names) == 2 and len(ours(names)) == 2, names
+
+
+def test_varlen_backward_is_two_kernels(profiler_sees_kernels):
+    q, k, v, cq, ck = W.packed(44, [100, 37, 260], [90, 37, 300], 4, 64)
+    q, k, v, cq, ck = (t.to(DEV) for t in (q, k, v, cq, ck))
+    out, lse = sdpa_fwd_varlen(q, k, v, cq, ck, 260, is_causal=2)
+    dout = torch.randn_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+    names = kernels_of(lambda: sdpa_bwd_varlen(q, k, v, out, dout, lse, cq, ck, 260, 300, dq,
+                                               dk, dv, delta, is_causal=2))
     assert len(names) == 2 and len(ours(names)) == 2, names
