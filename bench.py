@@ -61,8 +61,8 @@ VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf1
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
 # kernel source they were taken on (sha256 prefix below); reported as null otherwise.
-TRAFFIC_BYTES = 526976 * 1024
-TRAFFIC_KERNEL_SHA256 = "fa3c1f62b264aa8e"
+TRAFFIC_BYTES = 500980 * 1024
+TRAFFIC_KERNEL_SHA256 = "2b3bfb179d58fa67"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 # The same for one backward call (dq and dk/dv kernels together).
 BWD_TRAFFIC_BYTES = 1615844 * 1024
