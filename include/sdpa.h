@@ -295,10 +295,10 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
  *   dS[i,j] = P[i,j] (dP[i,j] - delta[i])
  *   dq[i,:] = scale * sum_j dS[i,j] k[j,:],   dk[j,:] = scale * sum_i dS[i,j] q[i,:]
  *
- * P and dS are rounded to the input type (nearest-even) before their products; every
- * product accumulates in fp32, and dq, dk, dv are rounded to the input type once at the
- * end.  Deterministic:
- * no atomics, every output element is written by exactly one lane.  A query row with no
+ * P and dS are rounded to the input type (nearest-even) before their products (for dk,
+ * dS is formed from the rounded P); every product accumulates in fp32, and dq, dk, dv
+ * are rounded to the input type once at the end.  Deterministic: no atomics, every
+ * output element is written by exactly one lane.  A query row with no
  * visible key gets dq = 0 and contributes nothing to dk, dv; a key seen by no query gets
  * dk = dv = 0.
  *

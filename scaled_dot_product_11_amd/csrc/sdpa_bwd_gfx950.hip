@@ -174,6 +174,10 @@ __device__ inline uint32_t pack2(float lo, float hi) {
   const f32x2 p = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, typename Vec16<E>::v2));
 }
+template <typename E>
+__device__ inline f32x2 unpack2(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(typename Vec16<E>::v2, w), f32x2);
+}
 
 // The transposed operand of a 32x32x16 product from a row-major tile in LDS: rows are
 // the reduction index, columns the output rows.  Within each group of 16 lanes, lane i of
@@ -238,11 +242,9 @@ struct StageMap {
   int tid, row0, col0;
   __device__ explicit StageMap(int t) : tid(t), row0(t / DG), col0(t % DG) {}
   __device__ bool ok(int p) const { return kEven || tid + p * NT < R * DG; }
-  __device__ int off(int p, int pitch) const {
-    if (kEven) return (row0 + p * (NT / DG)) * pitch + col0 * 16;
-    const int c = tid + p * NT;
-    return (c / DG) * pitch + (c % DG) * 16;
-  }
+  __device__ int off(int p, int pitch) const { return row(p) * pitch + col(p) * 16; }
+  __device__ int row(int p) const { return kEven ? row0 + p * (NT / DG) : (tid + p * NT) / DG; }
+  __device__ int col(int p) const { return kEven ? col0 : (tid + p * NT) % DG; }
 };
 
 // ---------------------------------------------------------------------------------------
@@ -513,41 +515,69 @@ void bwd_dq(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Single-copy staging layout of the dK/dV kernel.  A streamed [64 x D] tile is read two
+// ways: along a row (16-byte reads of head dims, left operands of S and dP) and down the
+// columns (ds_read_b64_tr_b16, left operands of dV^T and dK^T).  Rows have a power-of-two
+// number of 16-byte slots (4, 8 or 16; D = 96 takes 16 slots for its 12 chunks), and chunk
+// j of row r sits in slot j ^ sw(r).  Within the 16 lanes of one row-read pass (16 rows,
+// one chunk) and within the 32 lanes of one transposed-read pass (4 consecutive rows from
+// a multiple of 4, 4 consecutive chunks from a multiple of 4) every lane then reaches a
+// different 16-byte bank group of the 256-byte bank space; the staging writes (consecutive
+// chunks of consecutive rows) do as well.
+template <int D>
+struct BwdSwz {
+  static constexpr int DG = D / 8;                              // 16-byte chunks per row
+  static constexpr int SL = DG <= 4 ? 4 : (DG <= 8 ? 8 : 16);   // slots per row
+  static constexpr int RB = 16 * SL;                            // row pitch (bytes)
+  static constexpr int SH = SL == 16 ? 0 : (SL == 8 ? 1 : 2);
+  __device__ static int sw(int r) { return ((r >> 2) & 3) | (((r & 3) >> SH) << 2); }
+  __device__ static int at(int r, int j) { return r * RB + 16 * (j ^ sw(r)); }
+};
+
+// ---------------------------------------------------------------------------------------
 // dkdv kernel.  Workgroup: 128 keys of one (b, h) in 8 waves, two per SIMD.  The two waves
 // of a SIMD own the same 32 keys k0 + 32(w % 4) + 0..31 (lane (li, hf): key
-// k0 + 32(w % 4) + li) and split the products between them, so that each holds only one
-// accumulator block and the pair fits two waves per SIMD:
-//   both:     S[qs] = Q[qs] K^T         (Q rows read in perm5 order: register r of half hf
+// k0 + 32(w % 4) + li) and split the four products of each 64-query tile between them,
+// two each, with P handed from one to the other through LDS:
+//   P wave:   S[qs] = Q[qs] K^T         (Q rows read in perm5 order: register r of half hf
 //                                         is query 32qs + 16(r/8) + 8hf + r%8)
-//             P = 2^(S scale log2e - lse2[query]), hidden -> 0
-//   P wave:   dV^T += dO^T P             (dO^T by transposed reads, P in the input type)
-//   dS wave:  dP[qs] = dO[qs] V^T,  dS = P * (dP - delta[query]),
-//             dK^T += Q^T dS             (Q^T by transposed reads, dS in the input type)
-// The scores are computed by both waves (a fifth product per pair instead of an exchange
-// of P through LDS, which holds the staged tiles); the dS wave carries three products and
-// the P wave two, and on each SIMD one wave's vector work runs under the other's products.
-// The P waves also stage the tiles.  LDS stage: Q row copy | Q transposed-read copy | dO row copy | dO transposed-read copy |
-// lse2[64] | delta[64].
+//             P = 2^(S scale log2e - lse2[query]), hidden -> 0, rounded to the input type
+//             and written to LDS;  dV^T += dO^T P   (dO^T by transposed reads)
+//   dS wave, one tile behind:
+//             dP[qs] - delta = dO[qs] V^T + (-delta[query])  (accumulators start at -delta)
+//             dS = P * (dP - delta) with P from LDS,  dK^T += Q^T dS   (Q^T by transposed reads)
+// Each wave holds one accumulator block and one of K, V, and the two waves of a SIMD meet
+// only at the one barrier per tile, so one's vector work (the exponentials; dS) runs under
+// the other's products.  Only on the causal diagonal (or with a mask) does the P wave
+// test elements.  The P waves also stage the tiles.
+// LDS: three stages of [Q | dO | lse2[64] | -delta[64]] in the layout above (the tile the
+// P waves compute on, the one the dS waves compute on, the next), then P of two tiles
+// (4 KB per SIMD each).
 // ---------------------------------------------------------------------------------------
 template <typename E, int D, bool CAUSAL, int MK, int MODE>
 __global__ __launch_bounds__(kThreadsBwdK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv(BwdArgs a) {
   constexpr bool MASK = MK == 1, BIAS = MK == 2;
   typedef typename Vec16<E>::v8 v8;
+  typedef BwdSwz<D> SW;
   constexpr int BQ = kBwdStep;
   constexpr int NT = kThreadsBwdK / 2;  // the P waves stage the tiles
   constexpr int DG = D / 8;
   constexpr int CH = (BQ * DG + NT - 1) / NT;
-  constexpr int RP = k_pitch_bf16(D);
-  constexpr int TP = v_pitch_bf16(D);
-  constexpr int OFF_QT = BQ * RP;
-  constexpr int OFF_DR = OFF_QT + BQ * TP;
-  constexpr int OFF_DT = OFF_DR + BQ * RP;
-  constexpr int OFF_LSE = OFF_DT + BQ * TP;
-  constexpr int OFF_DEL = OFF_LSE + 4 * BQ;
-  constexpr int STAGE = OFF_DEL + 4 * BQ;
-  static_assert(2 * STAGE == lds_bytes_bwd_dkdv(D), "plan and kernel disagree on LDS");
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+  constexpr int RB = SW::RB;
+  // Stage k: Q at k TILE, dO at (3 + k) TILE, lse2 and -delta at ROWS + k ROWB; then P.
+  // Every operand read in the loop is a per-lane base (which includes the Q or dO region)
+  // plus an immediate below 64 KB.
+  constexpr int NSTAGE = 3;
+  constexpr int TILE = BQ * RB;
+  constexpr int OFF_DO = NSTAGE * TILE;
+  constexpr int ROWS = 2 * NSTAGE * TILE;
+  constexpr int ROWB = 8 * BQ;  // lse2[BQ] | -delta[BQ]
+  constexpr int OFF_P = ROWS + NSTAGE * ROWB;
+  constexpr int PBYTES = 32 * BQ * 2;  // one SIMD's P tile in the input type
+  constexpr int LDS_BYTES = OFF_P + 2 * 4 * PBYTES;
+  static_assert(LDS_BYTES == lds_bytes_bwd_dkdv(D), "plan and kernel disagree on LDS");
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -580,18 +610,18 @@ void bwd_dkdv(BwdArgs a) {
   const bool k_ok = kj < Lk;
   const bool wave_live = kw < Lk;
 
-  // K^T right operand of S (both waves) and V^T right operand of dP (dS wave): column =
-  // this lane's key, half hf supplies head dims 16c + 8hf .. +7 of chunk c.
-  v8 kf[D / 16], vf[D / 16];
+  // Right operand of the wave's first product: K^T (S, P wave) or V^T (dP, dS wave);
+  // column = this lane's key, half hf supplies head dims 16c + 8hf .. +7 of chunk c.
+  v8 kvf[D / 16];
+  {
+    const uint16_t* src = ds_wave ? vb : kb;
+    const int64_t rs = ds_wave ? a.sv[2] : a.sk[2];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    u32x4 wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
-    if (k_ok) {
-      wk = ld16(kb + int64_t(kj) * a.sk[2] + 16 * c + 8 * hf);
-      if (ds_wave) wv = ld16(vb + int64_t(kj) * a.sv[2] + 16 * c + 8 * hf);
+    for (int c = 0; c < D / 16; ++c) {
+      u32x4 w = {0, 0, 0, 0};
+      if (k_ok) w = ld16(src + int64_t(kj) * rs + 16 * c + 8 * hf);
+      kvf[c] = __builtin_bit_cast(v8, w);
     }
-    kf[c] = __builtin_bit_cast(v8, wk);
-    vf[c] = __builtin_bit_cast(v8, wv);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -608,7 +638,9 @@ void bwd_dkdv(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, d_ext, kBufferFlags);
   const StageMap<BQ, DG, NT> sm_(tid);  // the P waves' threads, tid < NT
   u32x4 qreg[CH], dreg[CH];
-  float rowval = 0.f;  // threads 0..63: lse2 of row tid; 64..127: delta of row tid - 64
+  // threads 0..63: lse of row tid; 64..127: delta of row tid - 64 (as loaded; converted
+  // when stored, so the load is waited for one tile later)
+  float rowval = 0.f;
   auto load = [&](int t) {
     const bool live = t < ntiles;
     const int qbase = live ? t * BQ * q_rowb : q_ext;
@@ -622,26 +654,55 @@ void bwd_dkdv(BwdArgs a) {
     if (tid < 2 * BQ) {
       const int row = t * BQ + (tid & (BQ - 1));
       const bool ok = live && row < Lq;
-      if (tid < BQ) rowval = ok ? lse_base2(lse_h[row]) : INFINITY;
+      if (tid < BQ) rowval = ok ? lse_h[row] : -INFINITY;
       else rowval = ok ? del_h[row] : 0.f;
     }
   };
   auto store = [&](int st) {
-    char* s = lds + st * STAGE;
+    char* s = lds + st * TILE;
 #pragma unroll
     for (int p = 0; p < CH; ++p)
       if (sm_.ok(p)) {
-        *reinterpret_cast<u32x4*>(s + sm_.off(p, RP)) = qreg[p];
-        *reinterpret_cast<u32x4*>(s + OFF_QT + sm_.off(p, TP)) = qreg[p];
-        *reinterpret_cast<u32x4*>(s + OFF_DR + sm_.off(p, RP)) = dreg[p];
-        *reinterpret_cast<u32x4*>(s + OFF_DT + sm_.off(p, TP)) = dreg[p];
+        const int o = SW::at(sm_.row(p), sm_.col(p));
+        *reinterpret_cast<u32x4*>(s + o) = qreg[p];
+        *reinterpret_cast<u32x4*>(s + OFF_DO + o) = dreg[p];
       }
-    if (tid < 2 * BQ) reinterpret_cast<float*>(s + OFF_LSE)[tid] = rowval;
+    // lse2 of the rows, and -delta (the initial value of the dP accumulators)
+    if (tid < 2 * BQ)
+      reinterpret_cast<float*>(lds + ROWS + st * ROWB)[tid] = tid < BQ ? lse_base2(rowval) : -rowval;
   };
 
-  const int rfrag = perm5(li) * RP + hf * 16;
-  const int tfrag = tr_lane_offset(lane, TP);
+  // Row reads: lane row perm5(li) (+ 32qs), chunk 2c + hf.  Transposed reads: rows
+  // 16c + 8(lane / 32) + 4h + (lane / 4) % 4, chunks 4dt + 2((lane / 16) % 2) + (lane % 4) / 2.
+  // Row reads (Q for the P wave, dO for the dS wave) and transposed reads (dO for the P
+  // wave, Q for the dS wave): per-lane bases into the stage the wave computes on (moved to
+  // the next stage after each step), plus immediates below 64 KB.  The empty asm keeps the
+  // compiler from rebuilding the bases from the loop-invariant parts (a register each).
+  int raddr[D / 16];
+  {
+    const int r = perm5(li), region = ds_wave ? OFF_DO : 0;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      raddr[c] = region + SW::at(r, 2 * c + hf);
+      asm("" : "+v"(raddr[c]));
+    }
+  }
+  int taddr[2][D / 32];
+  {
+    const int g16 = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+    const int region = ds_wave ? 0 : OFF_DO;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        taddr[h][dt] = region + 8 * (q4 & 1) +
+                       SW::at(8 * (g16 >> 1) + 4 * h + e4, 4 * dt + 2 * (g16 & 1) + (q4 >> 1));
+        asm("" : "+v"(taddr[h][dt]));
+      }
+  }
   const float c2 = a.scale_log2;
+  // P of tile t: slot t % 2, chunk c at + c * 1024
+  char* pex0 = lds + OFF_P + (wave & 3) * PBYTES + lane * 16;
 
   // dV^T (P wave) or dK^T (dS wave)
   f32x16 acc[D / 32];
@@ -650,116 +711,190 @@ void bwd_dkdv(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
-  // One query tile for one role.  The 32-query sub-tiles are taken one at a time (their
-  // scores, then their P or dS), so only one sub-tile of S and dP is live at once.
-  auto compute = [&](auto role, int t) {
-    constexpr bool DS = decltype(role)::value;
-    const char* st = lds + (t & 1) * STAGE;
-    const int qt0 = t * BQ;
-    const float* lse2s = reinterpret_cast<const float*>(st + OFF_LSE);
-    const float* dels = reinterpret_cast<const float*>(st + OFF_DEL);
-    const bool edge = CAUSAL && qt0 + coff < kw + 31;
-    v8 opf[4];  // P (P wave) or dS (dS wave): chunk c = queries 16c + 8hf + 0..7
+  // The wave's product over head dims for sub-tile qs: S (P wave, Q rows) or dP (dS wave,
+  // dO rows); operands are read two chunks ahead, fenced so the scheduler keeps that order.
+  auto dim_product2 = [&](f32x16 (&x)[2]) {
+    const char* rows = lds;
+    constexpr int NR = 2 * (D / 16);  // reads, i = 2c + qs
+    v8 opa[4];
+    auto read = [&](int i) {
+      opa[i % 4] = __builtin_bit_cast(v8, ld16(rows + raddr[i / 2] + (i % 2) * 32 * RB));
+    };
+    read(0);
+    read(1);
+    read(2);
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      f32x16 sc, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = dp[r] = 0.f;
-      // Operands are read two chunks ahead of their products; the fences keep that order
-      // (near the register limit the scheduler would otherwise read each operand just
-      // before its product and wait out the full LDS latency every time).
-      v8 qa[3], da[3];
-      auto read = [&](int c) {
-        qa[c % 3] = __builtin_bit_cast(v8, ld16(st + rfrag + qs * 32 * RP + 32 * c));
-        if (DS)
-          da[c % 3] = __builtin_bit_cast(v8, ld16(st + OFF_DR + rfrag + qs * 32 * RP + 32 * c));
-      };
-      read(0);
-      read(1);
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        if (c + 2 < D / 16) read(c + 2);
-        sc = mfma16(qa[c % 3], kf[c], sc);
-        if (DS) dp = mfma16(da[c % 3], vf[c], dp);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int c = 2 * qs + g;
-        const int qc = 16 * c + 8 * hf;  // first query of the run, within the tile
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + qc);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + qc + 4);
-        f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-        if (DS) {
-          d0 = *reinterpret_cast<const f32x4*>(dels + qc);
-          d1 = *reinterpret_cast<const f32x4*>(dels + qc + 4);
-        }
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float o[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int i = 2 * e + u, r = 8 * g + i;
-            const int qrow = qt0 + qc + i;
-            float xv = __builtin_fmaf(sc[r], c2, -(i < 4 ? l0[i] : l1[i - 4]));
-            if (BIAS && k_ok && qrow < Lq)  // additive mask, in base-2 units
-              xv = __builtin_fmaf(bb[int64_t(qrow) * a.sm[2] + kj], kLog2e, xv);
-            if (edge || MASK) {
-              bool hide = false;
-              if (CAUSAL) hide = kj > qrow + coff;
-              if (MASK) hide = hide || !k_ok || qrow >= Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
-              if (hide) xv = -INFINITY;
-            }
-            const float p = exp2_fast(xv);
-            o[u] = DS ? p * (dp[r] - (i < 4 ? d0[i] : d1[i - 4])) : p;
-          }
-          w[e] = pack2<E>(o[0], o[1]);
-        }
-        opf[c] = __builtin_bit_cast(v8, w);
-      }
+    for (int i = 0; i < NR; ++i) {
+      if (i + 3 < NR) read(i + 3);
+      x[i % 2] = mfma16(opa[i % 4], kvf[i / 2], x[i % 2]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); operands two products ahead
-    const char* ltr = st + (DS ? OFF_QT : OFF_DT) + tfrag;
+  };
+  // acc += T^T op over the tile's 64 queries, T = dO (P wave) or Q (dS wave) by transposed
+  // reads; op chunk c = queries 16c + 8hf + 0..7 (P or dS in the input type).
+  auto query_product = [&](const v8 (&op)[4]) {
+    const char* rows = lds;
     constexpr int NP = 4 * (D / 32);  // products, i = c * (D / 32) + dt
     v8 ta[3];
-    auto tread = [&](int i) { ta[i % 3] = tr_operand<v8, TP>(ltr, i / (D / 32), i % (D / 32)); };
+    auto tread = [&](int i) {
+      const int c = i / (D / 32), dt = i % (D / 32);
+      const s16x4 lo = ds_read_tr(rows + taddr[0][dt] + 16 * c * RB);
+      const s16x4 hi = ds_read_tr(rows + taddr[1][dt] + 16 * c * RB);
+      const s16x4 both[2] = {lo, hi};
+      ta[i % 3] = __builtin_bit_cast(v8, both);
+    };
     __builtin_amdgcn_sched_barrier(0);
     tread(0);
     tread(1);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (i + 2 < NP) tread(i + 2);
-      acc[i % (D / 32)] = mfma16(ta[i % 3], opf[i / (D / 32)],
-                                                                  acc[i % (D / 32)]);
+      acc[i % (D / 32)] = mfma16(ta[i % 3], op[i / (D / 32)], acc[i % (D / 32)]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // A wave's keys are visible to some query of tile t iff the tile's last query + coff >= kw.
+  auto tile_live = [&](int t) { return wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw); };
+  // Points the operand bases at stage k (from stage 0) / moves them on from stage k to the
+  // next one.
+  auto bases_add = [&](int bytes) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      raddr[c] += bytes;
+      asm("" : "+v"(raddr[c]));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        taddr[h][dt] += bytes;
+        asm("" : "+v"(taddr[h][dt]));
+      }
+  };
+  auto bases_next = [&](int k) { bases_add(k == NSTAGE - 1 ? -(NSTAGE - 1) * TILE : TILE); };
 
-  // The two roles run separate loops with the same barriers, one per query tile, so that
-  // the staging registers (P waves only) never count against the dS waves' products.  A
-  // wave's keys are visible to some query of tile t iff the tile's last query + coff >= kw.
-  // The P waves load each tile right after its predecessor is written to LDS.
+  // The roles run separate loops with the same one barrier per step, so that the staging
+  // registers (P waves only) never count against the dS waves.  Step t: the P waves
+  // compute tile t (P into slot t % 2) and stage tile t + 1; the dS waves compute tile
+  // t - 1.  The barrier publishes P of tile t and stage t + 1; stage (t + 2) % 3, written
+  // at step t + 1, was last read at step t - 1.  Each tile is loaded right after its
+  // predecessor is written to LDS.
   if (!ds_wave) {
     load(tbeg);
-    store(tbeg & 1);
+    store(tbeg % NSTAGE);
     load(tbeg + 1);
     __syncthreads();
-    for (int t = tbeg; t < ntiles; ++t) {
-      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw)) compute(std::false_type{}, t);
-      store((t + 1) & 1);
+    int k = tbeg % NSTAGE;  // stage of tile t
+    bases_add(k * TILE);
+    for (int t = tbeg; t <= ntiles; ++t) {
+      char* pex = pex0 + (t & 1) * 4 * PBYTES;
+      const bool live = t < ntiles && tile_live(t);
+      v8 pf[4];  // P, chunk c = queries 16c + 8hf + 0..7
+      const int qt0 = t * BQ;
+      const float* lse2s = reinterpret_cast<const float*>(lds + ROWS + k * ROWB);
+      // One tile of P; HIDE: some element may be hidden (causal diagonal, mask, bias).
+      auto p_tile = [&](auto hide_tag) {
+        constexpr bool HIDE = decltype(hide_tag)::value;
+        f32x16 sc2[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc2[0][r] = sc2[1][r] = 0.f;
+        dim_product2(sc2);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          const f32x16 sc = sc2[qs];
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int c = 2 * qs + g;
+            const int qc = 16 * c + 8 * hf;  // first query of the run, within the tile
+            const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + qc);
+            const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + qc + 4);
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float o[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int i = 2 * e + u, r = 8 * g + i;
+                const int qrow = qt0 + qc + i;
+                float xv = __builtin_fmaf(sc[r], c2, -(i < 4 ? l0[i] : l1[i - 4]));
+                if (HIDE) {
+                  if (BIAS && k_ok && qrow < Lq)  // additive mask, in base-2 units
+                    xv = __builtin_fmaf(bb[int64_t(qrow) * a.sm[2] + kj], kLog2e, xv);
+                  bool hide = false;
+                  if (CAUSAL) hide = kj > qrow + coff;
+                  if (MASK) hide = hide || !k_ok || qrow >= Lq || mb[int64_t(qrow) * a.sm[2] + kj] == 0;
+                  if (hide) xv = -INFINITY;
+                }
+                o[u] = exp2_fast(xv);
+              }
+              w[e] = pack2<E>(o[0], o[1]);
+            }
+            pf[c] = __builtin_bit_cast(v8, w);
+            *reinterpret_cast<u32x4*>(pex + c * 1024) = w;
+          }
+        }
+      };
+      if (live) {
+        if (MASK || BIAS || (CAUSAL && qt0 + coff < kw + 31))
+          p_tile(std::true_type{});
+        else
+          p_tile(std::false_type{});
+        query_product(pf);
+      }
+      const int kn = k == NSTAGE - 1 ? 0 : k + 1;
+      if (t + 1 < ntiles) store(kn);
       load(t + 2);
-      __syncthreads();
+      bases_next(k);
+      k = kn;
+      __syncthreads();  // P of tile t written; tile t + 1 staged; tile t - 1 read
     }
   } else {
     __syncthreads();
-    for (int t = tbeg; t < ntiles; ++t) {
-      if (wave_live && (!CAUSAL || t * BQ + BQ - 1 + coff >= kw)) compute(std::true_type{}, t);
+    // tile u = t - 1, one step behind the P waves, on stage k = u % 3
+    int k = (tbeg + NSTAGE - 1) % NSTAGE;
+    bases_add(k * TILE);
+    for (int t = tbeg; t <= ntiles; ++t) {
+      const int u = t - 1;
+      const char* pex = pex0 + (u & 1) * 4 * PBYTES;
+      if (u >= tbeg && tile_live(u)) {
+        // dP - delta: the accumulators start at -delta of their rows (register r of half hf
+        // is query 32qs + 16(r/8) + 8hf + r%8), then P of the tile
+        const float* ndel = reinterpret_cast<const float*>(lds + ROWS + k * ROWB + 4 * BQ);
+        f32x16 dp[2];
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d = *reinterpret_cast<const f32x4*>(ndel + 32 * qs + 16 * (g >> 1) + 8 * hf + 4 * (g & 1));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[qs][4 * g + e] = d[e];
+          }
+        u32x4 pw[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pw[c] = *reinterpret_cast<const u32x4*>(pex + c * 1024);
+        dim_product2(dp);
+        v8 dsf[4];  // dS, chunk c = queries 16c + 8hf + 0..7
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x2 p = unpack2<E>(pw[c][e]);
+            const int r = 8 * (c & 1) + 2 * e;
+            w[e] = pack2<E>(p[0] * dp[c >> 1][r], p[1] * dp[c >> 1][r + 1]);
+          }
+          dsf[c] = __builtin_bit_cast(v8, w);
+        }
+        query_product(dsf);
+      }
+      bases_next(k);
+      k = k == NSTAGE - 1 ? 0 : k + 1;
       __syncthreads();
     }
   }
   // dV (P waves) and dK (dS waves) of the same 32 keys per SIMD, written as whole rows
-  static_assert(8 * 32 * RP <= 2 * STAGE, "the output tiles fit the LDS");
+  constexpr int RP = k_pitch_bf16(D);
+  static_assert(8 * 32 * RP <= LDS_BYTES, "the output tiles fit the LDS");
   char* ot = lds + wave * 32 * RP;
   tile_to_lds<E, D, RP>(ot, acc, ds_wave ? a.scale : 1.f, li, hf);
   __syncthreads();

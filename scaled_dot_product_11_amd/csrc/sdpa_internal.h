@@ -156,14 +156,18 @@ constexpr int kThreadsBwdK = 512;
 constexpr int kBwdBlockQ = 256;
 constexpr int kBwdBlockK = 128;
 constexpr int kBwdStep = 64;
-// LDS per workgroup of the two backward kernels: two stages, each holding the streamed
-// tiles once in row-read layout (pitch k_pitch_bf16) and once in transposed-read layout
-// (pitch v_pitch_bf16); the dK/dV kernel also stages the tile's lse and delta.
+// LDS per workgroup of the two backward kernels.  dQ: two stages, each holding the K tile
+// in row-read layout (pitch k_pitch_bf16) and in transposed-read layout (pitch
+// v_pitch_bf16), and the V tile in row-read layout.
 constexpr int64_t lds_bytes_bwd_dq(int D) {
   return 2 * int64_t(kBwdStep) * (2 * k_pitch_bf16(D) + v_pitch_bf16(D));
 }
 constexpr int64_t lds_bytes_bwd_dkdv(int D) {
-  return 2 * (int64_t(kBwdStep) * 2 * (k_pitch_bf16(D) + v_pitch_bf16(D)) + 8 * kBwdStep);
+  // three stages of Q and dO in one swizzled copy (rows of 4, 8 or 16 slots of 16 bytes)
+  // with the tile's lse and delta, then two tiles of P (32 keys x kBwdStep queries,
+  // 16-bit) per SIMD
+  return 3 * (int64_t(kBwdStep) * 2 * 16 * (D <= 32 ? 4 : D <= 64 ? 8 : 16) + 8 * kBwdStep) +
+         2 * 4 * 32 * kBwdStep * 2;
 }
 
 struct BwdProblem {
