@@ -65,8 +65,8 @@ TRAFFIC_BYTES = 500980 * 1024
 TRAFFIC_KERNEL_SHA256 = "2b3bfb179d58fa67"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 # The same for one backward call (dq and dk/dv kernels together).
-BWD_TRAFFIC_BYTES = 1615844 * 1024
-BWD_TRAFFIC_KERNEL_SHA256 = "c1a410f457bc9196"
+BWD_TRAFFIC_BYTES = 1619503 * 1024
+BWD_TRAFFIC_KERNEL_SHA256 = "338c206bd353e304"
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_bwd_gfx950.hip")
 
 
