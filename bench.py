@@ -219,6 +219,29 @@ def bench_workload(wl, steps, warmup):
             "tflops_median": flops / (statistics.median(per) * 1e-3) / 1e12}
 
 
+# Vector-unit ceiling of the 16-bit forward.  A wave64 fp32 vector instruction issues in 4
+# cycles (16 lanes per clock per SIMD; packed fp32 is not used), v_exp_f32 in ~8.6 cycles
+# (device micro-benchmark).  Per workload, the vector instructions per computed score
+# (SQ_INSTS_VALU / SQ_INSTS_VALU_TRANS_F32, one exponential per score) and the fraction of
+# computed scores that are algorithmic (visible / computed) are counter measurements of the
+# current kernels (profiles/sdpa_fwd_vector_work_per_score.md).  The ceiling is the rate at
+# which 1024 SIMDs at 2.4 GHz could issue that vector work: 4*D flops per algorithmic score.
+VALU_CYCLES_PER_INST = 4.0
+EXP_CYCLES_PER_INST = 8.6
+VALU_PER_SCORE = {  # workload name prefix: (vector instructions per score, visible / computed)
+    "c2_": (6.28, 0.925), "c3_": (6.43, 0.961), "c4_": (5.42, 0.990), "c5_": (9.77, 0.998),
+}
+
+
+def valu_ceiling_tflops(name, D):
+    """Vector-issue ceiling (TFLOP/s of algorithmic work) of a measured workload, or None."""
+    for prefix, (v, frac) in VALU_PER_SCORE.items():
+        if name.startswith(prefix):
+            cycles_per_score = ((v - 1) * VALU_CYCLES_PER_INST + EXP_CYCLES_PER_INST) / 64
+            return 4 * D * 1024 * 2.4e9 / cycles_per_score * frac / 1e12
+    return None
+
+
 def copy_calibration(mib):
     """One elementwise kernel that reads `mib` MiB and writes `mib` MiB: the HBM counters
     read for it give their scale factor against known traffic."""
@@ -643,14 +666,26 @@ def main():
         copy_calibration(args.copy_calibration_mib)
 
     if args.report:
-        rows = [r]
+        rows = [(r, wl)]
         for name, fn in (("c1", W.config1), ("c2", W.config2), ("c5", W.config5)):
-            rows.append(bench_workload(fn(), args.steps, args.warmup))
+            w = fn()
+            rows.append((bench_workload(w, args.steps, args.warmup), w))
         for rank in (3, 4):
-            rows.append(bench_workload(W.config3(rank=rank), args.steps, args.warmup))
+            w = W.config3(rank=rank)
+            rows.append((bench_workload(w, args.steps, args.warmup), w))
+        results = []
+        for row, w in rows:
+            # both ceilings of the 16-bit kernels: the matrix cores and the vector issue
+            D = w.shape4()[4]
+            vc = valu_ceiling_tflops(w.name, D) if w.q.dtype != torch.float32 else None
+            row = dict(row, pct_of_mfma_peak=round(100 * row["tflops_median"] / PEAK_BF16_TFLOPS, 2))
+            if vc:
+                row.update(valu_ceiling_tflops=round(vc, 1),
+                           pct_of_valu_ceiling=round(100 * row["tflops_median"] / vc, 2))
+            results.append(row)
         with open(args.report, "w") as f:
             json.dump({"peak_bf16_tflops": PEAK_BF16_TFLOPS, "device": props.name,
-                       "results": rows}, f, indent=1)
+                       "results": results}, f, indent=1)
 
     print(json.dumps(line), flush=True)
 
