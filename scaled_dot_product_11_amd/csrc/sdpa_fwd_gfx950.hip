@@ -552,8 +552,10 @@ void fwd_mfma(Args a) {
     }
     // Hidden keys -> -inf: on the tiles that cross the causal diagonal or the end of the
     // keys, by position (and mask byte); on the others, with a mask, by mask byte only.
-    auto mask_byte = [&](int kt, int r) {
-      return uint32_t(mcur[2 * kt + (r >> 3)] >> (8 * (r & 7))) & 0xffu;
+    auto mask_byte = [&](int kt, int r) {  // 32-bit halves: byte tests, not 64-bit compares
+      const uint64_t w = mcur[2 * kt + (r >> 3)];
+      const uint32_t half = (r & 4) ? uint32_t(w >> 32) : uint32_t(w);
+      return (half >> (8 * (r & 3))) & 0xffu;
     };
     const bool edge = (CAUSAL && k0 + BN - 1 > qw + coff) || (k0 + BN > Lk);
     if (edge) {
@@ -574,7 +576,14 @@ void fwd_mfma(Args a) {
         for (int r = 0; r < 16; ++r)
           if (mask_byte(kt, r) == 0) s[kt][r] = -INFINITY;
     }
+    // With a boolean mask, whether any key of this tile is visible to the lane's row by its
+    // mask bytes (keys past Lk have byte 0; keys hidden by position alone still count).
+    bool mvis = true;
     if (MASK) {
+      uint32_t any = 0;
+#pragma unroll
+      for (int i = 0; i < NMB; ++i) any |= uint32_t(mcur[i]) | uint32_t(mcur[i] >> 32);
+      mvis = any != 0;
 #pragma unroll
       for (int i = 0; i < NMB; ++i) mcur[i] = mnext[i];
     }
@@ -601,17 +610,25 @@ void fwd_mfma(Args a) {
     };
     // Fast path: the exponentials against the current reference, no row max.  A lane whose
     // 32 values sum to at most 2^kRescaleSlack has every p <= 2^kRescaleSlack, i.e. no score
-    // above the reference by more than the slack, so no rescale is due.  Otherwise (and
-    // while a row has no reference yet, or with a boolean mask, whose empty rows keep none)
-    // the wave takes the slow path: the row maxima (a chain of 3-input maxima and one
-    // permlane32 swap), the rescale of O and l where some row's max grew by more than the
-    // slack, and the exponentials again.  Both paths make the same rescale decisions as
-    // always computing the maxima, so the result does not depend on which path ran.
+    // above the reference by more than the slack, so no rescale is due.  A row with no
+    // reference yet takes the fast path only when none of its keys in the tile is visible
+    // (boolean mask: all of the lane's mask bytes zero), against reference 0: every p is 0,
+    // as the slow path would give.  Otherwise the wave takes the slow path: the row maxima
+    // (a chain of 3-input maxima and one permlane32 swap), the rescale of O and l where some
+    // row's max grew by more than the slack, and the exponentials again.  Both paths make
+    // the same rescale decisions as always computing the maxima, so the result does not
+    // depend on which path ran.
     float lt = 0.f;
     bool slow = true;
-    if (!MASK && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
-      exps(m_ref, &lt);
-      slow = !(lt <= kRescaleBound);
+    const bool noref = m_ref == -INFINITY;
+    if (!MASK) {
+      if (!__builtin_amdgcn_ballot_w64(noref)) {
+        exps(m_ref, &lt);
+        slow = !(lt <= kRescaleBound);
+      }
+    } else if (!__builtin_amdgcn_ballot_w64(noref && mvis)) {
+      exps(noref ? 0.f : m_ref, &lt);
+      slow = !noref && !(lt <= kRescaleBound);
     }
     if (__builtin_amdgcn_ballot_w64(slow)) {
       float mx = fmaxf(s[0][0], s[0][1]);
