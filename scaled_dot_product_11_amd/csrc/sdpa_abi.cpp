@@ -30,9 +30,9 @@ bool launch_fits(int64_t blocks, int64_t threads) {
 
 // Workgroups and threads of the forward kernel for `rows` query rows per head: the tile
 // sdpa::fwd_groups picks for this problem (dense, split-key or packed).
-void fwd_tile(int dtype, int64_t D, bool dense, bool split, int64_t bh, int64_t rows,
-              int64_t* q_tiles, int64_t* threads) {
-  const int groups = sdpa::fwd_groups(dtype, D, dense, bh, rows, split);
+void fwd_tile(int dtype, int64_t D, bool dense, bool split, bool causal, int64_t bh,
+              int64_t rows, int64_t keys, int64_t* q_tiles, int64_t* threads) {
+  const int groups = sdpa::fwd_groups(dtype, D, dense, causal, bh, rows, keys, split);
   const int64_t bm = dtype != SDPA_F32 ? 128 * groups : sdpa::kBlockMF32;
   *q_tiles = (rows + bm - 1) / bm;
   *threads = dtype != SDPA_F32 ? 256 * groups : sdpa::kThreadsF32;
@@ -86,7 +86,7 @@ int normalise(const void* q, const void* k, const void* v, const void* out, cons
 
   const int64_t bh = B * H;
   int64_t q_tiles, threads;
-  fwd_tile(dtype, D, true, false, bh, Lq, &q_tiles, &threads);
+  fwd_tile(dtype, D, true, false, is_causal != SDPA_CAUSAL_NONE, bh, Lq, Lk, &q_tiles, &threads);
   if (bh != 0 && (q_tiles > kMaxDim / bh || !launch_fits(bh * q_tiles, threads)))
     return SDPA_ERR_SHAPE;  // grid size
   const bool any_rows = bh * Lq != 0;
@@ -394,7 +394,8 @@ int normalise_varlen(const void* q, const void* k, const void* v, const void* ou
   if (causal < SDPA_CAUSAL_NONE || causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t heads = nseq * H;
   int64_t q_tiles, threads;
-  fwd_tile(dtype, D, false, false, heads, max_seqlen_q, &q_tiles, &threads);
+  fwd_tile(dtype, D, false, false, causal != SDPA_CAUSAL_NONE, heads, max_seqlen_q, 0, &q_tiles,
+           &threads);
   if (heads != 0 && (q_tiles > kMaxDim / heads || !launch_fits(heads * q_tiles, threads)))
     return SDPA_ERR_SHAPE;  // grid size
   const bool any_rows = heads != 0 && total_q != 0 && max_seqlen_q != 0;
@@ -471,7 +472,7 @@ int splitkv_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, int64
   const int64_t bm = sdpa::block_m(dtype, int(D));
   sdpa::splitkv_plan(bh, (Lq + bm - 1) / bm, Lk, num_splits, nsplit, split_len);
   int64_t q_tiles, threads;
-  fwd_tile(dtype, D, false, true, bh, Lq, &q_tiles, &threads);
+  fwd_tile(dtype, D, false, true, false, bh, Lq, Lk, &q_tiles, &threads);
   // the chunk launch, and the merge launch of one 64-lane wave per query row
   if (bh != 0 && (q_tiles > kMaxDim / bh / *nsplit || !launch_fits(bh * q_tiles * *nsplit, threads) ||
                   !launch_fits((bh * Lq + 3) / 4, 256)))
@@ -802,7 +803,8 @@ int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
                            1.0f, is_causal, nullptr, dtype, nullptr);
   if (st != SDPA_OK) return st;
   // small 16-bit problems take the one-group tile
-  const int groups = sdpa::fwd_groups(dtype, D, true, B * H, Lq, false);
+  const int groups = sdpa::fwd_groups(dtype, D, true, is_causal != SDPA_CAUSAL_NONE, B * H, Lq, Lk,
+                                      false);
   plan->block_m = dtype != SDPA_F32 ? 128 * groups : sdpa::block_m(dtype, int(D));
   plan->block_n = sdpa::block_n(dtype);
   plan->threads = dtype != SDPA_F32 ? 256 * groups : sdpa::block_threads(dtype, int(D));

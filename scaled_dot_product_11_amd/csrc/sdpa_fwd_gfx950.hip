@@ -1148,7 +1148,8 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   // dense: B*H heads of Lq rows; packed: nseq*H heads of up to max_seqlen_q rows
   const int64_t rows = p.varlen ? p.max_seqlen_q : p.Lq;
   const int mode = p.varlen ? kVarlen : p.nsplit > 0 ? kSplit : kDense;
-  const int groups = fwd_groups(p.dtype, p.D, mode == kDense, p.B * p.H, p.Lq, mode == kSplit);
+  const int groups = fwd_groups(p.dtype, p.D, mode == kDense, p.causal != 0, p.B * p.H, p.Lq,
+                                p.Lk, mode == kSplit);
   const int bm = p.dtype != 0 ? 128 * groups : kBlockMF32;
   a.q_tiles = int32_t((rows + bm - 1) / bm);
   a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);

@@ -45,15 +45,25 @@ constexpr int block_threads(int dtype, int D) {
 // phase partner; with few items the launch takes as long as its longest item, which the
 // shorter 128-row items halve (measured: [1,32,8192,D] causal, 1024 items: D = 32 -12 %,
 // D = 64 -7 %, D = 96 +9 %, D = 128 +4 %; 512 and 256 items at D = 64 and 128: -4 % to -19 %).
+// Short causal walks at D = 128 take it too, up to four 256-row items per CU: each item of
+// the two-group tile runs its first and last key steps half empty and waits for its first
+// tiles, a fixed cost that walks of at most 2048 keys do not amortise, while two one-group
+// workgroups per CU hide each other's (measured, bf16 causal: [16,16,1024] -6 %,
+// [8,16,1536] -4 %, [8,16,2048] -2 %; with 1536 or more items, or without the causal mask,
+// the two-group tile stays ahead by 1 to 18 %).
 // Split-key launches of decode shapes (at most 128 query rows) take the one-group tile too:
 // their workgroups stream K and V for a single live query tile, and two of them per CU keep
 // twice as many tile loads in flight.
 constexpr int64_t kSmallProblemItems = 512;
+constexpr int64_t kShortWalkItems = 1024;
+constexpr int64_t kShortWalkKeys = 2048;
 constexpr int64_t kDecodeRows = 128;
-constexpr int fwd_groups(int dtype, int64_t D, bool dense, int64_t bh, int64_t Lq,
-                         bool split) {
+constexpr int fwd_groups(int dtype, int64_t D, bool dense, bool causal, int64_t bh, int64_t Lq,
+                         int64_t Lk, bool split) {
   return dtype != 0 && D <= 128 &&
-                 ((dense && (D <= 64 || bh * ((Lq + 255) / 256) <= kSmallProblemItems)) ||
+                 ((dense && (D <= 64 || bh * ((Lq + 255) / 256) <= kSmallProblemItems ||
+                             (D == 128 && causal && Lk <= kShortWalkKeys &&
+                              bh * ((Lq + 255) / 256) <= kShortWalkItems))) ||
                   (split && Lq <= kDecodeRows))
              ? 1
              : (dtype != 0 ? groups_16(int(D)) : 1);

@@ -227,17 +227,25 @@ def test_plan_tiles_per_head_dim(D, dtype):
 @pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
 def test_plan_small_problems_take_the_one_group_tile(D):
     """16-bit problems take 128-row items of 4 waves at D <= 64, or with at most 512 items of
-    256 rows, causal or not; D = 96 and 128 with more items, and fp32, keep their tiles."""
+    256 rows, causal or not, and at D = 128 causal problems of at most 1024 such items and
+    2048 keys; D = 96 and 128 with more items, and fp32, keep their tiles."""
     small = sd.sdpa_plan(4, 8, 16, 1024, 1024, D, 1, sd.SDPA_BF16)   # 128 heads x 4 = 512
     small_nc = sd.sdpa_plan(4, 8, 16, 1024, 1024, D, 0, sd.SDPA_F16)
     large = sd.sdpa_plan(4, 8, 16, 1025, 1025, D, 1, sd.SDPA_BF16)   # 128 heads x 5 = 640
     large_nc = sd.sdpa_plan(4, 8, 16, 1025, 1025, D, 0, sd.SDPA_BF16)
+    short4 = sd.sdpa_plan(4, 8, 16, 2048, 2048, D, 2, sd.SDPA_BF16)  # 128 heads x 8 = 1024
+    many = sd.sdpa_plan(4, 8, 16, 2049, 2049, D, 1, sd.SDPA_BF16)    # 128 heads x 9 = 1152
+    long_keys = sd.sdpa_plan(4, 8, 16, 1025, 2049, D, 1, sd.SDPA_BF16)  # 640 items, 2049 keys
     f32 = sd.sdpa_plan(4, 8, 16, 1024, 1024, D, 1, sd.SDPA_F32)
     assert (small.block_m, small.threads, small.q_tiles) == (128, 256, 8)
     assert (small_nc.block_m, small_nc.threads) == (128, 256)
     big = (256, 512) if D in (96, 128) else (128, 256)
-    assert (large.block_m, large.threads) == big
+    one = (128, 256)
+    assert (large.block_m, large.threads) == (one if D == 128 else big)
+    assert (short4.block_m, short4.threads) == (one if D == 128 else big)
     assert (large_nc.block_m, large_nc.threads) == big
+    assert (many.block_m, many.threads) == big
+    assert (long_keys.block_m, long_keys.threads) == big
     assert (f32.block_m, f32.threads) == (128, 256)
     assert small.items == 128 * 8
 

@@ -132,21 +132,21 @@ def test_small_problem_tile_equals_two_group_tile(dtype, D):
     """The one-group tile (128 rows, 4 waves) and the two-group tile (256 rows, 8 waves in
     alternating phases) give each 32-row slice the same sequence of operations, so they agree
     bit for bit.  Which tile a launch takes is asserted through sdpa_plan.  At D = 96 and 128
-    a 2-head problem runs the one-group tile and a 520-head problem the two-group tile; their
+    a 2-head problem runs the one-group tile and a 1040-head problem the two-group tile; their
     shared heads are compared with no mask, both causal alignments, a boolean mask broadcast
     over heads and an additive mask.  At D <= 64 every dense problem runs the one-group tile
-    (the 520-head comparison is then a determinism check), and the two-group side is the same
+    (the 1040-head comparison is then a determinism check), and the two-group side is the same
     two heads packed as one sequence through sdpa_fwd_varlen, which always takes the
     two-group tile (no mask, both causal alignments).  Everything is also checked against the
     oracle."""
     code = {torch.bfloat16: SDPA_BF16, torch.float16: SDPA_F16}[dtype]
     for n, (Lq, Lk) in enumerate([(33, 33), (129, 200), (300, 77), (300, 300)]):
         g = torch.Generator().manual_seed(4100 + n + D)
-        q, k, v = W.draw_qkv(g, (1, 520, Lq, D), (1, 520, Lk, D), dtype=dtype)
+        q, k, v = W.draw_qkv(g, (1, 1040, Lq, D), (1, 1040, Lk, D), dtype=dtype)
         bmask = torch.rand((1, 1, Lq, Lk), generator=g) < 0.3
         bmask[..., Lq // 2, :] = False  # one fully hidden row
         assert sdpa_plan(4, 1, 2, Lq, Lk, D, 1, code).threads == 256, "2 heads: one-group tile"
-        big_threads = sdpa_plan(4, 1, 520, Lq, Lk, D, 1, code).threads
+        big_threads = sdpa_plan(4, 1, 1040, Lq, Lk, D, 1, code).threads
         assert big_threads == (512 if D >= 96 else 256), (D, Lq, big_threads)
         for mode in (0, 1, 2, "mask"):
             causal = 0 if mode == "mask" else mode
@@ -166,7 +166,7 @@ def test_small_problem_tile_equals_two_group_tile(dtype, D):
                 torch.cuda.synchronize()
                 assert torch.equal(vo.transpose(0, 1), small_o[0]), where + " varlen"
                 assert torch.equal(vl, small_l[0]), where + " varlen lse"
-            heads = [0, 1, 263, 519]
+            heads = [0, 1, 263, 1039]
             rows = np.concatenate([h * Lq + np.arange(Lq) for h in heads]).astype(np.int64)
             if mode == 2:
                 tri = torch.ones(Lq, Lk, dtype=torch.bool).tril(Lk - Lq)
@@ -185,7 +185,7 @@ def test_small_problem_tile_equals_two_group_tile(dtype, D):
         torch.cuda.synchronize()
         where = f"bias D={D} Lq={Lq} Lk={Lk}"
         assert torch.equal(big_o[:, :2], small_o) and torch.equal(big_l[:, :2], small_l), where
-        rows = np.concatenate([h * Lq + np.arange(Lq) for h in (0, 519)]).astype(np.int64)
+        rows = np.concatenate([h * Lq + np.arange(Lq) for h in (0, 1039)]).astype(np.int64)
         ro, rl = sdpa_oracle(q, k, v, is_causal=True, bias=bias, rows=rows)
         idx = torch.from_numpy(rows).to(DEV)
         compare(big_o.reshape(-1, D)[idx], big_l.reshape(-1)[idx], ro, rl, dtype, where)
