@@ -61,8 +61,8 @@ VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf1
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
 # kernel source they were taken on (sha256 prefix below); reported as null otherwise.
-TRAFFIC_BYTES = 500980 * 1024
-TRAFFIC_KERNEL_SHA256 = "98e957222236f91e"
+TRAFFIC_BYTES = 498528 * 1024
+TRAFFIC_KERNEL_SHA256 = "df7eefdd3f137122"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 # The same for one backward call (dq and dk/dv kernels together).
 BWD_TRAFFIC_BYTES = 1619503 * 1024
@@ -229,7 +229,7 @@ def bench_workload(wl, steps, warmup):
 VALU_CYCLES_PER_INST = 4.0
 EXP_CYCLES_PER_INST = 8.6
 VALU_PER_SCORE = {  # workload name prefix: (vector instructions per score, visible / computed)
-    "c2_": (6.28, 0.925), "c3_": (6.43, 0.961), "c4_": (5.42, 0.990), "c5_": (8.38, 0.997),
+    "c2_": (6.28, 0.925), "c3_": (6.61, 0.961), "c4_": (5.42, 0.990), "c5_": (8.38, 0.997),
 }
 
 
