@@ -166,26 +166,40 @@ def _marshal(q, k, v, out, lse, mask, scale, is_causal):
 
 
 def _check_shapes(q, k, v, out, lse, mask):
-    if not (q.dim() == k.dim() == v.dim()):
+    rank = q.dim()
+    if k.dim() != rank or v.dim() != rank:
         raise ValueError("q, k and v must have the same rank")
-    if q.dim() in (3, 4):
-        if tuple(k.shape) != tuple(v.shape):
+    if rank in (3, 4):
+        qs, ks = q.shape, k.shape
+        if ks != v.shape:
             raise ValueError("k and v must have the same shape")
-        if tuple(k.shape[:-2]) != tuple(q.shape[:-2]) or k.shape[-1] != q.shape[-1]:
+        if ks[:-2] != qs[:-2] or ks[-1] != qs[-1]:
             raise ValueError("k must match q in the leading dims and the head dim")
-        if out is not None and tuple(out.shape) != tuple(q.shape):
+        if out is not None and out.shape != qs:
             raise ValueError("out must have q's shape")
-        if lse is not None and (tuple(lse.shape) != tuple(q.shape[:-1]) or
-                                lse.dtype != torch.float32 or not lse.is_contiguous()):
+        if lse is not None and (lse.shape != qs[:-1] or lse.dtype != torch.float32 or
+                                not lse.is_contiguous()):
             raise ValueError("lse must be a contiguous float32 tensor of shape q.shape[:-1]")
-    if not (q.dtype == k.dtype == v.dtype) or (out is not None and out.dtype != q.dtype):
+    dt = q.dtype
+    if k.dtype != dt or v.dtype != dt or (out is not None and out.dtype != dt):
         raise ValueError("q, k, v and out must share one dtype")
-    for t in (q, k, v, out, lse, mask):
-        if t is not None and t.device.type != "cuda":
+    tensors = (q, k, v, out, lse, mask)
+    for t in tensors:
+        if t is not None and not t.is_cuda:
             raise ValueError("sdpa_fwd runs on the GPU only: every tensor must be on a cuda device")
-    devs = {t.device for t in (q, k, v, out, lse, mask) if t is not None}
-    if len(devs) != 1:
-        raise ValueError("all tensors must be on the same device")
+    dev = q.device
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+
+
+def _on_device(device, fn, *args):
+    """fn(*args) with `device` current; the current device is switched (and restored) only
+    when it is another one."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
 
 
 def sdpa_fwd(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, mask=None,
@@ -207,8 +221,7 @@ def sdpa_fwd(q, k, v, out=None, lse=None, *, scale=None, is_causal=False, mask=N
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     args, _keep = _marshal(q, k, v, out, lse, mask, scale, is_causal)
     handle = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):
-        status = load_library().sdpa_fwd(*args, handle)
+    status = _on_device(q.device, load_library().sdpa_fwd, *args, handle)
     _raise_on(status)
     return out, lse
 
@@ -280,12 +293,11 @@ def _bwd_call(entry, q, k, v, out, dout, lse, dq, dk, dv, delta, scale, is_causa
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     handle = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):
-        status = getattr(load_library(), entry)(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-            rank, B, H, Lq, Lk, D, arr, float(scale), causal_mode(is_causal),
-            None if extra is None else extra.data_ptr(), _DTYPES.get(q.dtype, -1), handle)
+    status = _on_device(q.device, getattr(load_library(), entry),
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+        rank, B, H, Lq, Lk, D, arr, float(scale), causal_mode(is_causal),
+        None if extra is None else extra.data_ptr(), _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return dq, dk, dv
 
@@ -338,13 +350,12 @@ def sdpa_bwd_varlen(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seq
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     handle = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):
-        status = load_library().sdpa_bwd_varlen(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1,
-            int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, H, D, arr, float(scale),
-            causal_mode(is_causal), _DTYPES.get(q.dtype, -1), handle)
+    status = _on_device(q.device, load_library().sdpa_bwd_varlen,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1,
+        int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, H, D, arr, float(scale),
+        causal_mode(is_causal), _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return dq, dk, dv
 
@@ -368,11 +379,10 @@ def sdpa_fwd_bias(q, k, v, bias, out=None, lse=None, *, scale=None, is_causal=Fa
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     handle = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):
-        status = load_library().sdpa_fwd_bias(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            None if lse is None else lse.data_ptr(), q.dim(), B, H, Lq, Lk, D, arr,
-            float(scale), causal_mode(is_causal), b.data_ptr(), _DTYPES.get(q.dtype, -1), handle)
+    status = _on_device(q.device, load_library().sdpa_fwd_bias,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        None if lse is None else lse.data_ptr(), q.dim(), B, H, Lq, Lk, D, arr,
+        float(scale), causal_mode(is_causal), b.data_ptr(), _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return out, lse
 
@@ -419,12 +429,11 @@ def sdpa_fwd_splitkv(q, k, v, out=None, lse=None, *, scale=None, is_causal=False
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     handle = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):
-        status = load_library().sdpa_fwd_splitkv(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr, float(scale),
-            causal_mode(is_causal), int(num_splits), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), dtype, handle)
+    status = _on_device(q.device, load_library().sdpa_fwd_splitkv,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr, float(scale),
+        causal_mode(is_causal), int(num_splits), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), dtype, handle)
     _raise_on(status)
     return out, lse
 
@@ -446,11 +455,10 @@ def sdpa_fwd_splitkv_noalloc(q, k, v, out, lse=None, *, scale=None, is_causal=Fa
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     handle = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):
-        status = load_library().sdpa_fwd_splitkv_noalloc(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr, float(scale),
-            causal_mode(is_causal), int(num_splits), _DTYPES.get(q.dtype, -1), handle)
+    status = _on_device(q.device, load_library().sdpa_fwd_splitkv_noalloc,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        None if lse is None else lse.data_ptr(), rank, B, H, Lq, Lk, D, arr, float(scale),
+        causal_mode(is_causal), int(num_splits), _DTYPES.get(q.dtype, -1), handle)
     _raise_on(status)
     return out, lse
 
@@ -508,13 +516,12 @@ def sdpa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     handle = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):
-        status = load_library().sdpa_fwd_varlen(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            None if lse is None else lse.data_ptr(), cu_seqlens_q.data_ptr(),
-            cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, int(max_seqlen_q), total_q,
-            total_k, H, D, arr, float(scale), causal_mode(is_causal), _DTYPES.get(q.dtype, -1),
-            handle)
+    status = _on_device(q.device, load_library().sdpa_fwd_varlen,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        None if lse is None else lse.data_ptr(), cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, int(max_seqlen_q), total_q,
+        total_k, H, D, arr, float(scale), causal_mode(is_causal), _DTYPES.get(q.dtype, -1),
+        handle)
     _raise_on(status)
     return out, lse
 
