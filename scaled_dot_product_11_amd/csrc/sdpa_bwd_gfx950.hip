@@ -135,6 +135,30 @@ __device__ inline BwdItem bwd_item(const BwdArgs& a, int64_t bh) {
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// A raw buffer resource (base, no stride, extent in bytes) as four scalar registers, for
+// the loads below that are written in asm.
+__device__ inline u32x4 buffer_desc(const void* base, int extent) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{uint32_t(b), uint32_t(b >> 32) & 0xFFFFu, uint32_t(extent), uint32_t(kBufferFlags)};
+}
+// A 16-byte buffer load per lane that writes the LDS instead of registers: lane l fills
+// bytes lds_dst + 16l .. +15 (lds_dst wave-uniform), offsets past the extent fill zeros.
+// The compiler does not see the LDS write: the caller waits for the memory counter before
+// the barrier that publishes the data, and issues no such load into LDS still being read.
+// M0 is named as clobbered although the compiler reserves it (and warns so): nothing in
+// these kernels reads M0 but these loads.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void buffer_to_lds16(const u32x4& desc, uint32_t lds_dst, int offset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_dst), "v"(offset), "s"(desc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// LDS address of a shared-memory pointer, as the 32-bit value the hardware takes.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
 __device__ inline float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -552,7 +576,9 @@ struct BwdSwz {
 // test elements.  The P waves also stage the tiles.
 // LDS: three stages of [Q | dO | lse2[64] | -delta[64]] in the layout above (the tile the
 // P waves compute on, the one the dS waves compute on, the next), then P of two tiles
-// (4 KB per SIMD each).
+// (4 KB per SIMD each).  Q and dO go from memory straight into their stage (buffer loads
+// that write the LDS), issued by the P waves at the start of the step before the one that
+// computes on them.
 // ---------------------------------------------------------------------------------------
 template <typename E, int D, bool CAUSAL, int MK, int MODE>
 __global__ __launch_bounds__(kThreadsBwdK) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -561,9 +587,7 @@ void bwd_dkdv(BwdArgs a) {
   typedef typename Vec16<E>::v8 v8;
   typedef BwdSwz<D> SW;
   constexpr int BQ = kBwdStep;
-  constexpr int NT = kThreadsBwdK / 2;  // the P waves stage the tiles
   constexpr int DG = D / 8;
-  constexpr int CH = (BQ * DG + NT - 1) / NT;
   constexpr int RB = SW::RB;
   // Stage k: Q at k TILE, dO at (3 + k) TILE, lse2 and -delta at ROWS + k ROWB; then P.
   // Every operand read in the loop is a per-lane base (which includes the Q or dO region)
@@ -634,23 +658,36 @@ void bwd_dkdv(BwdArgs a) {
   const int q_rowb = int(a.sq[2]) * 2, d_rowb = int(a.sdo[2]) * 2;
   const int q_ext = Lq > 0 ? (Lq - 1) * q_rowb + 2 * D : 0;
   const int d_ext = Lq > 0 ? (Lq - 1) * d_rowb + 2 * D : 0;
-  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qb, 0, q_ext, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc((void*)dob, 0, d_ext, kBufferFlags);
-  const StageMap<BQ, DG, NT> sm_(tid);  // the P waves' threads, tid < NT
-  u32x4 qreg[CH], dreg[CH];
+  // A tile of Q (dO) fills RB * BQ / 1024 blocks of 1 KB of its stage, block b loaded by P
+  // wave b % 4: lane l of the load writes bytes 16l..16l+15 of the block and reads the
+  // chunk that the swizzled layout puts there (row r, slot s hold chunk s ^ sw(r)); slots
+  // past the row's DG chunks read past the extent, zeros.
+  constexpr int NDMA = RB * BQ / 4096;  // blocks per P wave and tensor
+  static_assert(RB * BQ % 4096 == 0, "whole blocks for every P wave");
+  int qoff[NDMA], doff[NDMA];
+#pragma unroll
+  for (int p = 0; p < NDMA; ++p) {
+    const int pos = (4 * p + (wave & 3)) * 1024 + 16 * lane;
+    const int r = pos / RB, j = (pos % RB) / 16 ^ SW::sw(r);
+    qoff[p] = j < DG ? r * q_rowb + 16 * j : -1;
+    doff[p] = j < DG ? r * d_rowb + 16 * j : -1;
+  }
+  const u32x4 qdesc = buffer_desc(qb, q_ext), ddesc = buffer_desc(dob, d_ext);
+  const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(lds) + uint32_t((wave & 3) * 1024));
+  // Q and dO of tile t into stage st (P waves)
+  auto load_tile = [&](int t, int st) {
+#pragma unroll
+    for (int p = 0; p < NDMA; ++p) {
+      const uint32_t dst = dma_base + uint32_t(st * TILE + 4 * p * 1024);
+      buffer_to_lds16(qdesc, dst, qoff[p] >= 0 ? t * BQ * q_rowb + qoff[p] : q_ext);
+      buffer_to_lds16(ddesc, dst + OFF_DO, doff[p] >= 0 ? t * BQ * d_rowb + doff[p] : d_ext);
+    }
+  };
   // threads 0..63: lse of row tid; 64..127: delta of row tid - 64 (as loaded; converted
   // when stored, so the load is waited for one tile later)
   float rowval = 0.f;
   auto load = [&](int t) {
     const bool live = t < ntiles;
-    const int qbase = live ? t * BQ * q_rowb : q_ext;
-    const int dbase = live ? t * BQ * d_rowb : d_ext;
-#pragma unroll
-    for (int p = 0; p < CH; ++p)
-      if (sm_.ok(p)) {
-        qreg[p] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qbase + sm_.off(p, q_rowb), 0, 0);
-        dreg[p] = __builtin_amdgcn_raw_buffer_load_b128(drs, dbase + sm_.off(p, d_rowb), 0, 0);
-      }
     if (tid < 2 * BQ) {
       const int row = t * BQ + (tid & (BQ - 1));
       const bool ok = live && row < Lq;
@@ -659,14 +696,6 @@ void bwd_dkdv(BwdArgs a) {
     }
   };
   auto store = [&](int st) {
-    char* s = lds + st * TILE;
-#pragma unroll
-    for (int p = 0; p < CH; ++p)
-      if (sm_.ok(p)) {
-        const int o = SW::at(sm_.row(p), sm_.col(p));
-        *reinterpret_cast<u32x4*>(s + o) = qreg[p];
-        *reinterpret_cast<u32x4*>(s + OFF_DO + o) = dreg[p];
-      }
     // lse2 of the rows, and -delta (the initial value of the dP accumulators)
     if (tid < 2 * BQ)
       reinterpret_cast<float*>(lds + ROWS + st * ROWB)[tid] = tid < BQ ? lse_base2(rowval) : -rowval;
@@ -773,20 +802,23 @@ void bwd_dkdv(BwdArgs a) {
   };
   auto bases_next = [&](int k) { bases_add(k == NSTAGE - 1 ? -(NSTAGE - 1) * TILE : TILE); };
 
-  // The roles run separate loops with the same one barrier per step, so that the staging
-  // registers (P waves only) never count against the dS waves.  Step t: the P waves
-  // compute tile t (P into slot t % 2) and stage tile t + 1; the dS waves compute tile
-  // t - 1.  The barrier publishes P of tile t and stage t + 1; stage (t + 2) % 3, written
-  // at step t + 1, was last read at step t - 1.  Each tile is loaded right after its
-  // predecessor is written to LDS.
+  // The roles run separate loops with the same one barrier per step.  Step t: the P waves
+  // load tile t + 1 into its stage, compute tile t (P into slot t % 2) and wait for their
+  // loads; the dS waves compute tile t - 1.  The barrier publishes P of tile t and stage
+  // t + 1; stage (t + 1) % 3 was last read at step t - 1 (tile t - 2).  The rows' lse and
+  // delta go through registers, loaded a step before they are stored.
   if (!ds_wave) {
+    if (tbeg < ntiles) load_tile(tbeg, tbeg % NSTAGE);
     load(tbeg);
     store(tbeg % NSTAGE);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     load(tbeg + 1);
     __syncthreads();
     int k = tbeg % NSTAGE;  // stage of tile t
     bases_add(k * TILE);
     for (int t = tbeg; t <= ntiles; ++t) {
+      const int kn = k == NSTAGE - 1 ? 0 : k + 1;
+      if (t + 1 < ntiles) load_tile(t + 1, kn);
       char* pex = pex0 + (t & 1) * 4 * PBYTES;
       const bool live = t < ntiles && tile_live(t);
       v8 pf[4];  // P, chunk c = queries 16c + 8hf + 0..7
@@ -841,8 +873,8 @@ void bwd_dkdv(BwdArgs a) {
           p_tile(std::false_type{});
         query_product(pf);
       }
-      const int kn = k == NSTAGE - 1 ? 0 : k + 1;
       if (t + 1 < ntiles) store(kn);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads into stage kn
       load(t + 2);
       bases_next(k);
       k = kn;
