@@ -573,12 +573,12 @@ struct BwdSwz {
 // Each wave holds one accumulator block and one of K, V, and the two waves of a SIMD meet
 // only at the one barrier per tile, so one's vector work (the exponentials; dS) runs under
 // the other's products.  Only on the causal diagonal (or with a mask) does the P wave
-// test elements.  The P waves also stage the tiles.
+// test elements.  The dS waves load the Q and dO tiles, the P waves the rows' lse and delta.
 // LDS: three stages of [Q | dO | lse2[64] | -delta[64]] in the layout above (the tile the
 // P waves compute on, the one the dS waves compute on, the next), then P of two tiles
 // (4 KB per SIMD each).  Q and dO go from memory straight into their stage (buffer loads
-// that write the LDS), issued by the P waves at the start of the step before the one that
-// computes on them.
+// that write the LDS), issued by the dS waves at the start of the step before the one in
+// which the P waves compute on them.
 // ---------------------------------------------------------------------------------------
 template <typename E, int D, bool CAUSAL, int MK, int MODE>
 __global__ __launch_bounds__(kThreadsBwdK) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -658,8 +658,8 @@ void bwd_dkdv(BwdArgs a) {
   const int q_rowb = int(a.sq[2]) * 2, d_rowb = int(a.sdo[2]) * 2;
   const int q_ext = Lq > 0 ? (Lq - 1) * q_rowb + 2 * D : 0;
   const int d_ext = Lq > 0 ? (Lq - 1) * d_rowb + 2 * D : 0;
-  // A tile of Q (dO) fills RB * BQ / 1024 blocks of 1 KB of its stage, block b loaded by P
-  // wave b % 4: lane l of the load writes bytes 16l..16l+15 of the block and reads the
+  // A tile of Q (dO) fills RB * BQ / 1024 blocks of 1 KB of its stage, block b loaded by
+  // dS wave b % 4: lane l of the load writes bytes 16l..16l+15 of the block and reads the
   // chunk that the swizzled layout puts there (row r, slot s hold chunk s ^ sw(r)); slots
   // past the row's DG chunks read past the extent, zeros.
   constexpr int NDMA = RB * BQ / 4096;  // blocks per P wave and tensor
@@ -673,12 +673,13 @@ void bwd_dkdv(BwdArgs a) {
     doff[p] = j < DG ? r * d_rowb + 16 * j : -1;
   }
   const u32x4 qdesc = buffer_desc(qb, q_ext), ddesc = buffer_desc(dob, d_ext);
-  const uint32_t dma_base = __builtin_amdgcn_readfirstlane(lds_addr(lds) + uint32_t((wave & 3) * 1024));
-  // Q and dO of tile t into stage st (P waves)
+  const uint32_t dma_base = lds_addr(lds) + uint32_t((wave & 3) * 1024);
+  // Q and dO of tile t into stage st (dS waves; the LDS address must be wave-uniform)
   auto load_tile = [&](int t, int st) {
 #pragma unroll
     for (int p = 0; p < NDMA; ++p) {
-      const uint32_t dst = dma_base + uint32_t(st * TILE + 4 * p * 1024);
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(dma_base + uint32_t(st * TILE + 4 * p * 1024));
       buffer_to_lds16(qdesc, dst, qoff[p] >= 0 ? t * BQ * q_rowb + qoff[p] : q_ext);
       buffer_to_lds16(ddesc, dst + OFF_DO, doff[p] >= 0 ? t * BQ * d_rowb + doff[p] : d_ext);
     }
@@ -803,22 +804,19 @@ void bwd_dkdv(BwdArgs a) {
   auto bases_next = [&](int k) { bases_add(k == NSTAGE - 1 ? -(NSTAGE - 1) * TILE : TILE); };
 
   // The roles run separate loops with the same one barrier per step.  Step t: the P waves
-  // load tile t + 1 into its stage, compute tile t (P into slot t % 2) and wait for their
-  // loads; the dS waves compute tile t - 1.  The barrier publishes P of tile t and stage
-  // t + 1; stage (t + 1) % 3 was last read at step t - 1 (tile t - 2).  The rows' lse and
-  // delta go through registers, loaded a step before they are stored.
+  // compute tile t (P into slot t % 2) and stage the rows' lse and delta of tile t + 1
+  // (through registers, loaded a step earlier); the dS waves load Q and dO of tile t + 1
+  // into its stage, compute tile t - 1 and wait for their loads.  The barrier publishes P
+  // of tile t and stage t + 1; stage (t + 1) % 3 was last read at step t - 1 (tile t - 2).
   if (!ds_wave) {
-    if (tbeg < ntiles) load_tile(tbeg, tbeg % NSTAGE);
     load(tbeg);
     store(tbeg % NSTAGE);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     load(tbeg + 1);
     __syncthreads();
     int k = tbeg % NSTAGE;  // stage of tile t
     bases_add(k * TILE);
     for (int t = tbeg; t <= ntiles; ++t) {
       const int kn = k == NSTAGE - 1 ? 0 : k + 1;
-      if (t + 1 < ntiles) load_tile(t + 1, kn);
       char* pex = pex0 + (t & 1) * 4 * PBYTES;
       const bool live = t < ntiles && tile_live(t);
       v8 pf[4];  // P, chunk c = queries 16c + 8hf + 0..7
@@ -871,21 +869,23 @@ void bwd_dkdv(BwdArgs a) {
           p_tile(std::true_type{});
         else
           p_tile(std::false_type{});
-        query_product(pf);
       }
+      if (live) query_product(pf);
       if (t + 1 < ntiles) store(kn);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads into stage kn
       load(t + 2);
       bases_next(k);
       k = kn;
       __syncthreads();  // P of tile t written; tile t + 1 staged; tile t - 1 read
     }
   } else {
+    if (tbeg < ntiles) load_tile(tbeg, tbeg % NSTAGE);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     // tile u = t - 1, one step behind the P waves, on stage k = u % 3
     int k = (tbeg + NSTAGE - 1) % NSTAGE;
     bases_add(k * TILE);
     for (int t = tbeg; t <= ntiles; ++t) {
+      if (t + 1 < ntiles) load_tile(t + 1, (t + 1) % NSTAGE);
       const int u = t - 1;
       const char* pex = pex0 + (u & 1) * 4 * PBYTES;
       if (u >= tbeg && tile_live(u)) {
@@ -921,6 +921,7 @@ void bwd_dkdv(BwdArgs a) {
       }
       bases_next(k);
       k = k == NSTAGE - 1 ? 0 : k + 1;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile t + 1
       __syncthreads();
     }
   }
