@@ -519,15 +519,24 @@ void bwd_dq(BwdArgs a) {
   };
 
   // Each tile is loaded right after its predecessor is written to LDS, a whole step
-  // before its own store.
+  // before its own store.  The second wave of each SIMD (waves 4..7) stages at the start of
+  // the step, while the first one's products hold the matrix core, the first wave at the
+  // end, while the second one's products run; stage (t + 1) & 1 was last read at step t - 1.
   load(0);
   store(0);
   load(1);
   __syncthreads();
+  const bool stage_first = __builtin_amdgcn_readfirstlane(wave) >= 4;
   for (int t = 0; t < ntiles; ++t) {
+    if (stage_first) {
+      store((t + 1) & 1);
+      load(t + 2);
+    }
     if (t < wtiles) compute(t);
-    store((t + 1) & 1);
-    load(t + 2);
+    if (!stage_first) {
+      store((t + 1) & 1);
+      load(t + 2);
+    }
     __syncthreads();
   }
 
