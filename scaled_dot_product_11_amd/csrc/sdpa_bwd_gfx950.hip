@@ -671,8 +671,8 @@ void bwd_dkdv(BwdArgs a) {
   // dS wave b % 4: lane l of the load writes bytes 16l..16l+15 of the block and reads the
   // chunk that the swizzled layout puts there (row r, slot s hold chunk s ^ sw(r)); slots
   // past the row's DG chunks read past the extent, zeros.
-  constexpr int NDMA = RB * BQ / 4096;  // blocks per P wave and tensor
-  static_assert(RB * BQ % 4096 == 0, "whole blocks for every P wave");
+  constexpr int NDMA = RB * BQ / 4096;  // blocks per loading (dS) wave and tensor
+  static_assert(RB * BQ % 4096 == 0, "whole blocks for every loading wave");
   int qoff[NDMA], doff[NDMA];
 #pragma unroll
   for (int p = 0; p < NDMA; ++p) {
