@@ -145,12 +145,14 @@ __device__ inline u32x4 buffer_desc(const void* base, int extent) {
 // bytes lds_dst + 16l .. +15 (lds_dst wave-uniform), offsets past the extent fill zeros.
 // The compiler does not see the LDS write: the caller waits for the memory counter before
 // the barrier that publishes the data, and issues no such load into LDS still being read.
+// On gfx9 an LDS-writing load reads M0 one wait state after a scalar write of it at the
+// earliest (the compiler keeps that distance for its own such loads), hence the s_nop.
 // M0 is named as clobbered although the compiler reserves it (and warns so): nothing in
 // these kernels reads M0 but these loads.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ inline void buffer_to_lds16(const u32x4& desc, uint32_t lds_dst, int offset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_dst), "v"(offset), "s"(desc) : "memory", "m0");
 }
 #pragma clang diagnostic pop
