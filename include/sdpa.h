@@ -431,13 +431,18 @@ int sdpa_bwd_varlen_check(const void* q, const void* k, const void* v, const voi
  * takes the same tiles).
  *
  * A work item is one (b*H + h, query tile) pair: block_m query rows of one head, which
- * walk the key/value tiles of block_n keys.  16-bit inputs take one of two tiles:
+ * walk the key/value tiles of block_n keys.  16-bit inputs take one of three tiles:
  *   - 256 rows and 512 threads (two waves per SIMD in alternating matrix / vector phases),
  *     for D = 96 and 128 when the problem has more than 512 items of 256 rows (at D = 128
  *     with is_causal: more than 1024 such items, or more than 2048 keys);
+ *   - 128 rows and 512 threads, the key split (two groups of four waves walk the two halves
+ *     of the item's key tiles in alternating phases and merge their rows; one workgroup
+ *     per CU, lds_bytes twice the 128-row tile's), for causal problems at D <= 64 with at
+ *     most 256 items of 128 rows and at least 1024 keys, or at most 512 such items and at
+ *     least 2048 keys;
  *   - 128 rows and 256 threads (one wave per SIMD; two such workgroups share a CU up to
- *     D = 128) otherwise: every problem at D <= 64, problems of at most 512 items of 256
- *     rows at D = 96 and 128, causal problems at D = 128 of at most 1024 such items and
+ *     D = 128) otherwise: every other problem at D <= 64, problems of at most 512 items of
+ *     256 rows at D = 96 and 128, causal problems at D = 128 of at most 1024 such items and
  *     2048 keys, and D = 256.
  * fp32 inputs: 128 rows, 256 threads.  (sdpa_fwd_varlen always takes the 256-row tile up to
  * D = 128; sdpa_fwd_splitkv the 128-row tile when Lq <= 128.)  With is_causal the items are

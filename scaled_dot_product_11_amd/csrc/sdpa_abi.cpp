@@ -33,9 +33,10 @@ bool launch_fits(int64_t blocks, int64_t threads) {
 void fwd_tile(int dtype, int64_t D, bool dense, bool split, bool causal, int64_t bh,
               int64_t rows, int64_t keys, int64_t* q_tiles, int64_t* threads) {
   const int groups = sdpa::fwd_groups(dtype, D, dense, causal, bh, rows, keys, split);
-  const int64_t bm = dtype != SDPA_F32 ? 128 * groups : sdpa::kBlockMF32;
+  const bool ks = sdpa::fwd_key_split(dtype, D, dense, causal, bh, rows, keys);
+  const int64_t bm = dtype != SDPA_F32 ? (ks ? 128 : 128 * groups) : sdpa::kBlockMF32;
   *q_tiles = (rows + bm - 1) / bm;
-  *threads = dtype != SDPA_F32 ? 256 * groups : sdpa::kThreadsF32;
+  *threads = dtype != SDPA_F32 ? (ks ? 512 : 256 * groups) : sdpa::kThreadsF32;
 }
 
 // One tensor's `rank` strides as canonical (b, h, row, col) strides: rank 3 [N,L,*] is
@@ -802,16 +803,21 @@ int sdpa_plan(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
   const int st = normalise(dummy, dummy, dummy, dummy, nullptr, rank, B, H, Lq, Lk, D, strides,
                            1.0f, is_causal, nullptr, dtype, nullptr);
   if (st != SDPA_OK) return st;
-  // small 16-bit problems take the one-group tile
-  const int groups = sdpa::fwd_groups(dtype, D, true, is_causal != SDPA_CAUSAL_NONE, B * H, Lq, Lk,
-                                      false);
-  plan->block_m = dtype != SDPA_F32 ? 128 * groups : sdpa::block_m(dtype, int(D));
+  // small 16-bit problems take the one-group tile, or the key split (two streams of tiles)
+  const bool causal = is_causal != SDPA_CAUSAL_NONE;
+  const bool ks = sdpa::fwd_key_split(dtype, D, true, causal, B * H, Lq, Lk);
+  int64_t q_tiles = 0, threads = 0;
+  fwd_tile(dtype, D, true, false, causal, B * H, Lq, Lk, &q_tiles, &threads);
+  plan->block_m = dtype != SDPA_F32
+                      ? (ks ? 128 : 128 * sdpa::fwd_groups(dtype, D, true, causal, B * H, Lq, Lk, false))
+                      : sdpa::block_m(dtype, int(D));
   plan->block_n = sdpa::block_n(dtype);
-  plan->threads = dtype != SDPA_F32 ? 256 * groups : sdpa::block_threads(dtype, int(D));
-  plan->q_tiles = (Lq + plan->block_m - 1) / plan->block_m;
+  plan->threads = threads;
+  plan->q_tiles = q_tiles;
   plan->bh = B * H;
   plan->items = plan->bh * plan->q_tiles;
-  plan->lds_bytes = dtype == SDPA_F32 ? sdpa::lds_bytes_f32(int(D)) : sdpa::lds_bytes_bf16(int(D));
+  plan->lds_bytes = dtype == SDPA_F32 ? sdpa::lds_bytes_f32(int(D))
+                                      : (ks ? 2 : 1) * sdpa::lds_bytes_bf16(int(D));
   plan->is_causal = is_causal ? 1 : 0;
   return SDPA_OK;
 }

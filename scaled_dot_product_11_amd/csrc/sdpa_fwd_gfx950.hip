@@ -234,7 +234,14 @@ __device__ inline s16x4 ds_read_tr(const char* p) {
 
 // MK: 0 no mask, 1 boolean mask, 2 additive mask (POS is then false: the scale is applied
 // to the scores before the bias is added).
-template <typename E, int D, bool CAUSAL, int MK, bool POS, int MODE, int G = groups_16(D)>
+//
+// Key split (KS, two groups, dense rows only): the workgroup holds 128 query rows, and its
+// two groups walk the two halves of the item's key tiles, each staging its own K and V tiles
+// in its own half of the LDS, in the same alternating phases; at the end group 1 hands its
+// row state (O, exponent reference, row sum) to group 0 through LDS, which merges the two
+// and stores the rows.  It shortens the longest items of small causal problems.
+template <typename E, int D, bool CAUSAL, int MK, bool POS, int MODE, int G = groups_16(D),
+          bool KS = false>
 __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(waves_16(D), waves_16(D))))
 void fwd_mfma(Args a) {
   constexpr bool MASK = MK == 1, BIAS = MK == 2;
@@ -242,9 +249,10 @@ void fwd_mfma(Args a) {
   typedef typename Vec16<E>::v8 v8;
   typedef typename Vec16<E>::v2 v2;
   static_assert(G == 1 || G == 2, "one or two phase groups");
+  static_assert(!KS || (G == 2 && MODE == kDense), "the key split runs two groups on dense rows");
   constexpr int BN = kBlockNBf16;
-  constexpr int BM = 128 * G;              // query rows per workgroup
-  constexpr int NT = 256 * G;
+  constexpr int BM = KS ? 128 : 128 * G;   // query rows per workgroup
+  constexpr int NT = KS ? 256 : 256 * G;   // threads staging one stream of K and V tiles
   constexpr int DG = D / 8;                // 16-byte chunks per row
   constexpr int CH = (BN * DG + NT - 1) / NT;  // chunks per thread per K (or V) tile
   constexpr bool CH_FULL = CH * NT == BN * DG;  // every thread stages CH chunks
@@ -254,17 +262,21 @@ void fwd_mfma(Args a) {
   constexpr int VP = v_pitch_bf16(D);      // V row pitch in LDS (bytes)
   constexpr int KT = BN * KP;              // bytes of one K stage
   constexpr int VT = BN * VP;              // bytes of one V stage
-  static_assert(D % 32 == 0 && BM == 32 * 4 * G && NT == 64 * 4 * G, "tile shape");
-  static_assert(2 * KT + 2 * VT == lds_bytes_bf16(D), "plan and kernel disagree on LDS");
-  static_assert(4 * G * 32 * KP <= 2 * KT + 2 * VT, "the epilogue's output tiles fit the LDS");
+  static_assert(D % 32 == 0 && BM == 32 * 4 * (KS ? 1 : G) && NT == 64 * 4 * (KS ? 1 : G),
+                "tile shape");
+  constexpr int GLDS = 2 * KT + 2 * VT;    // two stages of K and of V: one stream of tiles
+  static_assert(GLDS == lds_bytes_bf16(D), "plan and kernel disagree on LDS");
+  static_assert(4 * G * 32 * KP <= GLDS, "the epilogue's output tiles fit the LDS");
   static_assert((32 * DG) % 64 == 0, "the epilogue's row chunks split evenly over a wave");
-  __shared__ __attribute__((aligned(16))) char lds[2 * KT + 2 * VT];
+  __shared__ __attribute__((aligned(16))) char lds_all[(KS ? 2 : 1) * GLDS];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;        // 0..4G-1; SIMD = wave % 4
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;  // 0..4G-1; SIMD = wave % 4
   const int grp = G == 2 ? wave >> 2 : 0;  // phase group
-  const int slice = G == 2 ? 2 * (wave & 3) + grp : wave;  // 32-row slice of the rows
+  // 32-row slice of the rows; with the key split both groups hold the same 128 rows
+  const int slice = KS ? wave & 3 : G == 2 ? 2 * (wave & 3) + grp : wave;
+  const int tid = KS ? threadIdx.x & 255 : threadIdx.x;  // index among the stream's stagers
+  char* const lds = lds_all + (KS ? grp * GLDS : 0);     // the stages of this group's stream
   const int li = lane & 31;
   const int hf = lane >> 5;
 
@@ -302,9 +314,18 @@ void fwd_mfma(Args a) {
   // the tiles this wave computes on (with a causal mask: tiles 0 .. (qw + 31 + coff) / 64).
   int kend = Lk;
   if (CAUSAL) kend = max(0, min(kend, min(q0 + BM, Lq) + coff));
-  const int ntiles = (kend + BN - 1) / BN;
+  const int ntiles_all = (kend + BN - 1) / BN;
   const int wlast = qw + 31 + coff;  // last key any row of the wave may see (causal)
-  const int wtiles = !wave_live ? 0 : CAUSAL ? (wlast < 0 ? 0 : min(ntiles, wlast / BN + 1)) : ntiles;
+  const int wtiles_all = !wave_live ? 0
+                         : CAUSAL   ? (wlast < 0 ? 0 : min(ntiles_all, wlast / BN + 1))
+                                    : ntiles_all;
+  // The key tiles of this group's walk: all of them, or with the key split tiles [0, n0)
+  // for group 0 and [n0, ntiles_all) for group 1.  Below, t is the index within the walk
+  // and kt0 + t the tile's index among the keys (positions, masks, loads).
+  const int n0 = KS ? (ntiles_all + 1) / 2 : ntiles_all;
+  const int kt0 = KS && grp ? n0 : 0;
+  const int ntiles = KS && grp ? ntiles_all - n0 : n0;
+  const int wtiles = KS ? min(max(wtiles_all - kt0, 0), ntiles) : wtiles_all;
 
   // ---- global -> register -> LDS staging of K and V tiles.  All threads stage: K(t+1) is
   // written to LDS at the end of phase A of step t and K(t+2) loaded right after; V(t) is
@@ -355,14 +376,14 @@ void fwd_mfma(Args a) {
   };
   u32x4 kreg[CH], vreg[CH];
   auto load_k = [&](int t) {
-    const int base = (EVEN ? k_goff : 0) + (t < ntiles ? t * BN * k_rowb : k_ext);
+    const int base = (EVEN ? k_goff : 0) + (t < ntiles ? (kt0 + t) * BN * k_rowb : k_ext);
 #pragma unroll
     for (int p = 0; p < CH; ++p)
       if (chunk_ok(p))
         kreg[p] = __builtin_amdgcn_raw_buffer_load_b128(krs, base + g_off(p, k_rowb), 0, 0);
   };
   auto load_v = [&](int t) {
-    const int base = (EVEN ? v_goff : 0) + (t < ntiles ? t * BN * v_rowb : v_ext);
+    const int base = (EVEN ? v_goff : 0) + (t < ntiles ? (kt0 + t) * BN * v_rowb : v_ext);
 #pragma unroll
     for (int p = 0; p < CH; ++p)
       if (chunk_ok(p))
@@ -434,8 +455,8 @@ void fwd_mfma(Args a) {
   for (int i = 0; i < NMB; ++i) mcur[i] = ~0ull;
 #pragma unroll
   for (int i = 0; i < NBV; ++i) bcur[i] = 0.f;
-  if (MASK && q_ok && wtiles > 0) load_mask(mcur, 0);
-  if (BIAS && q_ok && wtiles > 0) load_bias(bcur, 0);
+  if (MASK && q_ok && wtiles > 0) load_mask(mcur, kt0);
+  if (BIAS && q_ok && wtiles > 0) load_bias(bcur, kt0);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -525,7 +546,7 @@ void fwd_mfma(Args a) {
   // Vector phase V(t): the online softmax of S(t) into P(t).
   auto vphase = [&](int t) {
     if (t < 0 || t >= wtiles) return;
-    const int k0 = t * BN;
+    const int k0 = (kt0 + t) * BN;
     // Scores in the comparison domain: raw q.k when the scale is positive (the scale is
     // folded into the exponent), else scale * q.k.  Invisible keys -> -inf.
     if (!POS) {
@@ -539,7 +560,7 @@ void fwd_mfma(Args a) {
     if (MASK) {
 #pragma unroll
       for (int i = 0; i < NMB; ++i) mnext[i] = ~0ull;
-      if (pre) load_mask(mnext, t + 1);
+      if (pre) load_mask(mnext, kt0 + t + 1);
     }
     if (BIAS) {
       // additive mask of this lane's keys, in base-2 units; keys past Lk are hidden below
@@ -587,7 +608,7 @@ void fwd_mfma(Args a) {
 #pragma unroll
       for (int i = 0; i < NMB; ++i) mcur[i] = mnext[i];
     }
-    if (BIAS && pre) load_bias(bcur, t + 1);
+    if (BIAS && pre) load_bias(bcur, kt0 + t + 1);
     // Online softmax with a lagging reference.  p = 2^(x - m_ref), rounded to the input type
     // two at a time into the P^T operand; the row sum adds the fp32 values (the lse needs
     // them unrounded) in two independent chains.
@@ -685,8 +706,10 @@ void fwd_mfma(Args a) {
       __syncthreads();
     }
   } else {
+    // (with the key split both groups run the longer walk's n0 + 1 steps; tiles past a
+    // group's own walk read as zeros and are not computed on)
     if (grp == 0) prefetch_k(0);
-    for (int t = 0; t <= ntiles; ++t) {
+    for (int t = 0; t <= n0; ++t) {
       if (grp == 0) {
         mphase(t);
       } else {
@@ -708,6 +731,43 @@ void fwd_mfma(Args a) {
     }
   }
 
+  if (KS) {
+    // Group 1 hands its row state to the group 0 wave of the same slice through LDS (free
+    // after the loop's last barrier): O register-major, each 16-byte piece of a register
+    // quartet at lane * 16 of its own 1 KB block, then the reference and the row sum.  Group
+    // 0 rescales both to the larger reference and adds them.
+    constexpr int NR4 = D / 32 * 4;  // register quartets of O
+    char* xo = lds_all + slice * NR4 * 1024 + lane * 16;
+    float* xm = reinterpret_cast<float*>(lds_all + 4 * NR4 * 1024) + 2 * (slice * 64 + lane);
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(xo + (4 * dt + g) * 1024) =
+              f32x4{o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]};
+      xm[0] = m_ref;
+      xm[1] = l_run;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float m1 = xm[0], l1 = xm[1];
+      const float m = fmaxf(m_ref, m1);
+      const float a0 = m_ref == -INFINITY ? 0.f : exp2_fast(m_ref - m);
+      const float a1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - m);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(xo + (4 * dt + g) * 1024);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[dt][4 * g + e] = o[dt][4 * g + e] * a0 + w[e] * a1;
+        }
+      l_run = l_run * a0 + l1 * a1;
+      m_ref = m;
+    }
+    __syncthreads();  // the exchange area is read before the output tiles reuse it
+  }
   // ---- epilogue: normalise, safe-softmax zeros, store O and the LSE ----
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -731,7 +791,7 @@ void fwd_mfma(Args a) {
     // barrier; each wave uses its own 32 rows of pitch KP), so that the global stores write
     // whole rows: lane l stores 16-byte chunks l, l + 64, ... of the tile in row-major order,
     // four rows of D = 128 per instruction, instead of 8-byte pieces of 32 rows.
-    char* ot = lds + wave * 32 * KP;
+    char* ot = lds_all + wave * 32 * KP;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -749,13 +809,16 @@ void fwd_mfma(Args a) {
             u32x2{w[0], w[1]};
       }
     __syncthreads();
+    const bool stores = !KS || grp == 0;  // with the key split, group 0 holds the merged rows
+    if (stores) {
 #pragma unroll
-    for (int i = 0; i < 32 * DG / 64; ++i) {
-      const int c = i * 64 + lane, r = c / DG, col = c % DG;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(ot + r * KP + col * 16);
-      if (qw + r < Lq) *reinterpret_cast<u32x4*>(ob + int64_t(qw + r) * a.so[2] + col * 8) = w;
+      for (int i = 0; i < 32 * DG / 64; ++i) {
+        const int c = i * 64 + lane, r = c / DG, col = c % DG;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(ot + r * KP + col * 16);
+        if (qw + r < Lq) *reinterpret_cast<u32x4*>(ob + int64_t(qw + r) * a.so[2] + col * 8) = w;
+      }
     }
-    if (q_ok && a.lse && hf == 0)
+    if (stores && q_ok && a.lse && hf == 0)
       a.lse[it.lse + qi] =
           l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
@@ -1030,11 +1093,24 @@ __global__ __launch_bounds__(64 * kCombineRows) void splitkv_combine(Args a, int
 }
 
 template <int D, bool CAUSAL, int MK, int MODE>
-hipError_t launch(const Args& a, int dtype, int groups, unsigned grid, hipStream_t stream) {
+hipError_t launch(const Args& a, int dtype, int groups, bool key_split, unsigned grid,
+                  hipStream_t stream) {
   void* args[] = {const_cast<Args*>(&a)};
   const void* fn;
   constexpr bool POS_OK = MK != 2;  // an additive mask takes the explicitly scaled path
   const bool pos = POS_OK && a.scale_log2 > 0.f;
+  // the key split for small causal dense problems at D <= 64 (fwd_key_split)
+  if constexpr (MODE == kDense && CAUSAL && D <= 64) {
+    if (key_split && dtype != 0) {
+      if (dtype == 1)
+        fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, POS_OK, MODE, 2, true>)
+                 : reinterpret_cast<const void*>(&fwd_mfma<__bf16, D, CAUSAL, MK, false, MODE, 2, true>);
+      else
+        fn = pos ? reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MK, POS_OK, MODE, 2, true>)
+                 : reinterpret_cast<const void*>(&fwd_mfma<_Float16, D, CAUSAL, MK, false, MODE, 2, true>);
+      return hipLaunchKernel(fn, dim3(grid), dim3(512), args, 0, stream);
+    }
+  }
   // the one-group tile for small dense problems and decode-shaped split keys (fwd_groups)
   if constexpr ((MODE == kDense || MODE == kSplit) && D <= 128) {
     if (groups == 1 && dtype != 0) {
@@ -1059,19 +1135,19 @@ hipError_t launch(const Args& a, int dtype, int groups, unsigned grid, hipStream
 }
 
 template <int D>
-hipError_t launch_d(const Args& a, int dtype, int groups, bool causal, int mode, unsigned grid,
-                    hipStream_t s) {
+hipError_t launch_d(const Args& a, int dtype, int groups, bool ks, bool causal, int mode,
+                    unsigned grid, hipStream_t s) {
   if (mode == kVarlen)  // packed sequences take no mask
-    return causal ? launch<D, true, 0, kVarlen>(a, dtype, groups, grid, s)
-                  : launch<D, false, 0, kVarlen>(a, dtype, groups, grid, s);
+    return causal ? launch<D, true, 0, kVarlen>(a, dtype, groups, ks, grid, s)
+                  : launch<D, false, 0, kVarlen>(a, dtype, groups, ks, grid, s);
   if (mode == kSplit)  // neither do split keys
-    return causal ? launch<D, true, 0, kSplit>(a, dtype, groups, grid, s)
-                  : launch<D, false, 0, kSplit>(a, dtype, groups, grid, s);
+    return causal ? launch<D, true, 0, kSplit>(a, dtype, groups, ks, grid, s)
+                  : launch<D, false, 0, kSplit>(a, dtype, groups, ks, grid, s);
   if (a.mask)
-    return causal ? launch<D, true, 1, kDense>(a, dtype, groups, grid, s) : launch<D, false, 1, kDense>(a, dtype, groups, grid, s);
+    return causal ? launch<D, true, 1, kDense>(a, dtype, groups, ks, grid, s) : launch<D, false, 1, kDense>(a, dtype, groups, ks, grid, s);
   if (a.bias)
-    return causal ? launch<D, true, 2, kDense>(a, dtype, groups, grid, s) : launch<D, false, 2, kDense>(a, dtype, groups, grid, s);
-  return causal ? launch<D, true, 0, kDense>(a, dtype, groups, grid, s) : launch<D, false, 0, kDense>(a, dtype, groups, grid, s);
+    return causal ? launch<D, true, 2, kDense>(a, dtype, groups, ks, grid, s) : launch<D, false, 2, kDense>(a, dtype, groups, ks, grid, s);
+  return causal ? launch<D, true, 0, kDense>(a, dtype, groups, ks, grid, s) : launch<D, false, 0, kDense>(a, dtype, groups, ks, grid, s);
 }
 
 template <int D>
@@ -1150,7 +1226,8 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   const int mode = p.varlen ? kVarlen : p.nsplit > 0 ? kSplit : kDense;
   const int groups = fwd_groups(p.dtype, p.D, mode == kDense, p.causal != 0, p.B * p.H, p.Lq,
                                 p.Lk, mode == kSplit);
-  const int bm = p.dtype != 0 ? 128 * groups : kBlockMF32;
+  const bool ks = fwd_key_split(p.dtype, p.D, mode == kDense, p.causal != 0, p.B * p.H, p.Lq, p.Lk);
+  const int bm = p.dtype != 0 ? (ks ? 128 : 128 * groups) : kBlockMF32;
   a.q_tiles = int32_t((rows + bm - 1) / bm);
   a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);
   a.scale_log2 = p.scale * kLog2e;
@@ -1167,11 +1244,11 @@ hipError_t launch_fwd(const Problem& p, hipStream_t stream) {
   const bool causal = p.causal != 0;
   hipError_t e;
   switch (p.D) {
-    case 32: e = launch_d<32>(a, p.dtype, groups, causal, mode, grid, stream); break;
-    case 64: e = launch_d<64>(a, p.dtype, groups, causal, mode, grid, stream); break;
-    case 96: e = launch_d<96>(a, p.dtype, groups, causal, mode, grid, stream); break;
-    case 128: e = launch_d<128>(a, p.dtype, groups, causal, mode, grid, stream); break;
-    case 256: e = launch_d<256>(a, p.dtype, groups, causal, mode, grid, stream); break;
+    case 32: e = launch_d<32>(a, p.dtype, groups, ks, causal, mode, grid, stream); break;
+    case 64: e = launch_d<64>(a, p.dtype, groups, ks, causal, mode, grid, stream); break;
+    case 96: e = launch_d<96>(a, p.dtype, groups, ks, causal, mode, grid, stream); break;
+    case 128: e = launch_d<128>(a, p.dtype, groups, ks, causal, mode, grid, stream); break;
+    case 256: e = launch_d<256>(a, p.dtype, groups, ks, causal, mode, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || mode != kSplit) return e;

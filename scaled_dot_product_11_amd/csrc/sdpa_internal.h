@@ -69,6 +69,29 @@ constexpr int fwd_groups(int dtype, int64_t D, bool dense, bool causal, int64_t 
              : (dtype != 0 ? groups_16(int(D)) : 1);
 }
 
+// The key split (dense causal 16-bit problems at D <= 64): 8-wave workgroups of 128 rows
+// whose two groups walk the two halves of an item's key tiles and merge their row states,
+// one workgroup per CU (each group stages its own tiles).  Where the launch lasts as long as
+// its longest items it halves them: with at most 256 such items (one round) and walks of at
+// least 1024 keys, or at most 512 items and walks of at least 2048 keys.  Measured, bf16
+// causal D = 64 against the one-group tile: [1,16,1024] -12 %, [2,16,1024] -12 %,
+// [1,8,2048] -20 %, [1,32,2048] -5 %, [2,8,4096] -17 %, [1,8,8192] -23 %, the additive-mask
+// pass [2,8,4096] -6.5 %, with a boolean mask +1 %, D = 32 [2,16,1024] -10 %,
+// [1,8,4096] -20 %; and outside the rule [3,16,1024] +4 %, [4,16,1024] +13 %,
+// [8,16,512] +34 % (two rounds of short walks).  The decision depends on (B*H, Lq, Lk, D)
+// only, so rank-3 and rank-4 inputs of one problem take the same path.
+constexpr int64_t kKeySplitOneRound = 256;
+constexpr int64_t kKeySplitTwoRounds = 512;
+constexpr int64_t kKeySplitKeys = 1024;
+constexpr int64_t kKeySplitLongKeys = 2048;
+constexpr bool fwd_key_split(int dtype, int64_t D, bool dense, bool causal, int64_t bh,
+                             int64_t Lq, int64_t Lk) {
+  return dtype != 0 && dense && causal && D <= 64 &&
+         (bh * ((Lq + 127) / 128) <= kKeySplitOneRound
+              ? Lk >= kKeySplitKeys
+              : bh * ((Lq + 127) / 128) <= kKeySplitTwoRounds && Lk >= kKeySplitLongKeys);
+}
+
 // Rank-3 [N,L,D] and rank-4 [B,H,L,D] inputs both become this (b, h, row, col) view;
 // every stride is in elements of the tensor's own type.  Packed variable-length inputs
 // [tokens, H, D] use the h and row strides (b stride 0), Lq / Lk are the token totals,

@@ -250,6 +250,33 @@ def test_plan_small_problems_take_the_one_group_tile(D):
     assert small.items == 128 * 8
 
 
+@pytest.mark.parametrize("D", [32, 64])
+def test_plan_key_split_tile(D):
+    """Causal 16-bit problems at D <= 64 take the key split (128 rows, 512 threads, twice the
+    128-row tile's LDS) with at most 256 items of 128 rows and at least 1024 keys, or at most
+    512 items and at least 2048 keys; otherwise the one-group tile.  Rank 3 and rank 4 agree."""
+    one = sd.sdpa_plan(4, 1, 16, 1024, 1024, D, 1, sd.SDPA_BF16)    # 128 items
+    base = (one.block_m, one.threads, one.lds_bytes)
+    assert (one.block_m, one.threads) == (128, 512) and one.q_tiles == 8
+    for args in [(4, 2, 16, 1024, 1024, D, 2, sd.SDPA_F16),    # 256 items, bottom-right
+                 (4, 1, 32, 2048, 2048, D, 1, sd.SDPA_BF16),   # 512 items, 2048 keys
+                 (4, 1, 2, 40, 1100, D, 1, sd.SDPA_BF16),      # 2 items, 1100 keys
+                 (3, 1, 16, 1024, 1024, D, 1, sd.SDPA_BF16)]:  # rank 3
+        p = sd.sdpa_plan(*args)
+        assert (p.block_m, p.threads, p.lds_bytes) == base, args
+    plain = sd.sdpa_plan(4, 3, 16, 1024, 1024, D, 1, sd.SDPA_BF16)  # 384 items, 1024 keys
+    assert (plain.block_m, plain.threads) == (128, 256)
+    assert one.lds_bytes == 2 * plain.lds_bytes
+    for args in [(4, 1, 16, 1024, 1023, D, 1, sd.SDPA_BF16),   # fewer than 1024 keys
+                 (4, 1, 16, 1024, 1024, D, 0, sd.SDPA_BF16),   # not causal
+                 (4, 1, 64, 2048, 2048, D, 1, sd.SDPA_BF16),   # 1024 items
+                 (4, 1, 16, 1024, 1024, D, 1, sd.SDPA_F32)]:
+        p = sd.sdpa_plan(*args)
+        assert p.threads == 256, args
+    wide = sd.sdpa_plan(4, 1, 16, 1024, 1024, 96, 1, sd.SDPA_BF16)  # D = 96: one-group tile
+    assert (wide.block_m, wide.threads) == (128, 256)
+
+
 def test_plan_rejects_bad_sizes():
     with pytest.raises(sd.SdpaError) as e:
         sd.sdpa_plan(4, 1, 1, 16, 16, 80, 1, sd.SDPA_BF16)
