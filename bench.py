@@ -61,8 +61,8 @@ VARLEN_METRIC = ("causal packed-documents SDPA fwd TFLOP/s on 1 MI355X (% of bf1
 # WRITE_SIZE from two rocprofv3 --pmc passes, each scaled by what the same counter reads
 # for an elementwise kernel of known traffic (1 GiB in, 1 GiB out).  Valid only for the
 # kernel source they were taken on (sha256 prefix below); reported as null otherwise.
-TRAFFIC_BYTES = 498528 * 1024
-TRAFFIC_KERNEL_SHA256 = "df7eefdd3f137122"
+TRAFFIC_BYTES = 544232 * 1024
+TRAFFIC_KERNEL_SHA256 = "9a0c4c6655ddfdbb"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 # The same for one backward call (dq and dk/dv kernels together).
 BWD_TRAFFIC_BYTES = 1669448 * 1024
@@ -582,6 +582,23 @@ def main_bwd(args, props):
     print(json.dumps(line), flush=True)
 
 
+def main_counters():
+    """Three forward launches of each workload the per-score counter summaries cover, in the
+    order c2, c5, c3 (rank 4), c4, then [1,32,8192,64] and [1,32,8192,32] causal."""
+    import torch
+    import workloads as W
+    from scaled_dot_product_11_amd import sdpa_fwd
+    for wl in (W.config2(), W.config5(), W.config3(rank=4), W.config4(), W.config4(D=64),
+               W.config4(D=32)):
+        q, k, v, m = to_device(wl, "cuda")
+        out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            sdpa_fwd(q, k, v, out, lse, mask=m, is_causal=wl.is_causal, scale=wl.scale)
+        torch.cuda.synchronize()
+        print(wl.name, tuple(q.shape), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -590,10 +607,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
                     help="input type of the fwd and bwd passes (default bf16, the metric's)")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "varlen", "decode", "bias"),
+    ap.add_argument("--pass", dest="which",
+                    choices=("fwd", "bwd", "varlen", "decode", "bias", "counters"),
                     default="fwd",
                     help="fwd (default): the fused forward; bwd: its gradients; varlen: the "
-                         "forward over packed documents; decode: split keys, one query per head")
+                         "forward over packed documents; decode: split keys, one query per head; "
+                         "counters: three forward launches of each profiled workload, for "
+                         "counter passes (prints the workload names, no timing)")
     ap.add_argument("--head-dim", type=int, default=128, choices=(32, 64, 96, 128, 256),
                     help="fwd pass: head dim of the [1,32,8192,D] causal workload (default 128, "
                          "the metric's)")
@@ -622,6 +642,9 @@ def main():
         return
     if args.which == "bias":
         main_bias(args, props)
+        return
+    if args.which == "counters":
+        main_counters()
         return
 
     D = args.head_dim
