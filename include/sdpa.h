@@ -56,8 +56,7 @@ enum sdpa_status {
   SDPA_ERR_NULL = 1,     /* a required pointer is NULL (strides, or q/k/v/out when read) */
   SDPA_ERR_RANK = 2,     /* rank not 3 or 4, or rank 3 with B != 1                       */
   SDPA_ERR_SHAPE = 3,    /* negative size, or a size/extent beyond the supported maximum */
-  SDPA_ERR_HEAD_DIM = 4, /* D not a supported head dim (forward: 32, 64, 96, 128, 256;
-                            backward: 32, 64, 96, 128)                                 */
+  SDPA_ERR_HEAD_DIM = 4, /* D not a supported head dim (32, 64, 96, 128, 256)            */
   SDPA_ERR_DTYPE = 5,    /* dtype not an sdpa_dtype                                      */
   SDPA_ERR_STRIDE = 6,   /* innermost stride != 1, or a negative stride                  */
   SDPA_ERR_ALIGN = 7,    /* q/k/v/out base or row stride not 16-byte aligned, lse not 4  */
@@ -281,7 +280,7 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
                           const int64_t* strides, float scale, int causal, int dtype);
 
 /*
- * sdpa_bwd -- gradients dq, dk, dv of sdpa_fwd for an upstream gradient dout, bf16 or fp16.
+ * sdpa_bwd -- gradients dq, dk, dv of sdpa_fwd for an upstream gradient dout.
  *
  * The derivative of the forward above by the chain rule through its steps.  The pages
  * define no backward; it reuses the forward's exported lse, as the fused forward of
@@ -295,15 +294,19 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
  *   dS[i,j] = P[i,j] (dP[i,j] - delta[i])
  *   dq[i,:] = scale * sum_j dS[i,j] k[j,:],   dk[j,:] = scale * sum_i dS[i,j] q[i,:]
  *
- * P and dS are rounded to the input type (nearest-even) before their products (for dk,
- * dS is formed from the rounded P); every product accumulates in fp32, and dq, dk, dv
- * are rounded to the input type once at the end.  Deterministic: no atomics, every
+ * bf16 and fp16 at D <= 128 (tiled matrix-core kernels): P and dS are rounded to the input
+ * type (nearest-even) before their products (for dk, dS is formed from the rounded P);
+ * every product accumulates in fp32, and dq, dk, dv are rounded to the input type once at
+ * the end.  fp32 inputs (every D) and D = 256 (every dtype) take row-by-row kernels on the
+ * vector ALU: one wave per query row, then one per key row, every value and sum in fp32
+ * (P and dS not rounded), dq, dk, dv rounded to the input type at the end; correct for
+ * every shape, not tuned for speed.  Deterministic: no atomics, every
  * output element is written by exactly one lane.  A query row with no
  * visible key gets dq = 0 and contributes nothing to dk, dv; a key seen by no query gets
  * dk = dv = 0.
  *
  *   q, k, v, out, dout, dq, dk, dv
- *                 device pointers to the 16-bit dtype.  q, out, dout, dq are [B,H,Lq,D] / [N,Lq,D];
+ *                 device pointers to `dtype`.  q, out, dout, dq are [B,H,Lq,D] / [N,Lq,D];
  *                 k, v, dk, dv are [B,H,Lk,D] / [N,Lk,D]; any layout with unit innermost
  *                 stride.  Bases and non-innermost strides (in bytes) multiples of 16.
  *                 dq, dk, dv must not overlap each other or any input.  q/out/dout/dq
@@ -314,13 +317,13 @@ int sdpa_fwd_varlen_check(const void* q, const void* k, const void* v, const voi
  *   delta         device pointer to B*H*Lq contiguous floats of caller-owned scratch,
  *                 4-byte aligned; receives delta[i] above (fp32).  Required when
  *                 B*H*Lq > 0.
- *   rank, B..D    as in sdpa_fwd (D in {32, 64, 96, 128}); additionally (Lq + 64) times the row
+ *   rank, B..D    as in sdpa_fwd (D in {32, 64, 96, 128, 256}); additionally (Lq + 64) times the row
  *                 stride of q (and of dout) must stay below 2 GiB.
  *   strides       9*rank element strides, tensor-major: q, k, v, out, dout, dq, dk, dv,
  *                 mask, each in its own axis order as in sdpa_fwd.
  *   scale, is_causal, mask
  *                 exactly as passed to sdpa_fwd (all three causal modes).
- *   dtype         SDPA_BF16 or SDPA_F16 (anything else: SDPA_ERR_DTYPE).
+ *   dtype         SDPA_F32, SDPA_BF16 or SDPA_F16 (anything else: SDPA_ERR_DTYPE).
  *   stream        a hipStream_t (NULL = the null stream of the current device).
  *
  * Launches two kernels on `stream` (dq and delta first, then dk and dv); allocates,
@@ -383,7 +386,7 @@ int sdpa_bwd_bias_check(const void* q, const void* k, const void* v, const void*
  * sequences.  Same rounding and determinism as sdpa_bwd.
  *
  *   q, out, dout, dq
- *                 device [total_q, H, D] of `dtype` (bf16 or fp16); k, v, dk, dv device
+ *                 device [total_q, H, D] of `dtype` (fp32, bf16 or fp16); k, v, dk, dv device
  *                 [total_k, H, D].  Any token and head strides, unit dim stride; bases and
  *                 strides (bytes) multiples of 16.  Outputs must not overlap each other or
  *                 any input.  The query-side tensors may be NULL when total_q == 0, the
@@ -400,7 +403,7 @@ int sdpa_bwd_bias_check(const void* q, const void* k, const void* v, const void*
  *                 and total_k; they size the launches.  Rows of a longer sequence past them
  *                 are not written.
  *   total_q, total_k, H, D
- *                 sizes; D in {32, 64, 96, 128}; (total + 64) times the token stride of q,
+ *                 sizes; D in {32, 64, 96, 128, 256}; (total + 64) times the token stride of q,
  *                 dout, k and v (each with its own total) must stay below 2 GiB.
  *   strides       24 element strides: (token, head, dim) for q, k, v, out, dout, dq, dk, dv.
  *   scale, causal, dtype, stream

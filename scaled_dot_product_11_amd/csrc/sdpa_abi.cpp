@@ -58,6 +58,20 @@ int canon_strides(int rank, const int64_t* s, int64_t out[4]) {
 
 // The backward's checks of the sizes, head dim (its kernels take 32, 64, 96 and 128) and
 // scale.
+// The two backward launches (dq, then dk/dv) of `heads` heads with at most `rows` query and
+// `keys` key rows each fit HIP's grid limits: the tiled 16-bit kernels, or the row-by-row
+// kernels (fp32 inputs, D = 256) with one wave per row.
+bool bwd_grids_fit(int dtype, int64_t D, int64_t heads, int64_t rows, int64_t keys) {
+  if (heads == 0) return true;
+  const bool gen = sdpa::bwd_generic(dtype, D);
+  const int64_t bq = gen ? sdpa::kBwdGenRows : sdpa::kBwdBlockQ;
+  const int64_t bk = gen ? sdpa::kBwdGenRows : sdpa::kBwdBlockK;
+  const int64_t tq = (rows + bq - 1) / bq, tk = (keys + bk - 1) / bk;
+  return tq <= kMaxDim / heads && tk <= kMaxDim / heads &&
+         launch_fits(heads * tq, gen ? sdpa::kThreadsBwdGen : sdpa::kThreadsBwdQ) &&
+         launch_fits(heads * tk, gen ? sdpa::kThreadsBwdGen : sdpa::kThreadsBwdK);
+}
+
 int check_sizes(int rank, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D, float scale) {
   if (rank != 3 && rank != 4) return SDPA_ERR_RANK;
   if (rank == 3 && B != 1) return SDPA_ERR_RANK;
@@ -163,16 +177,12 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
                   int is_causal, const uint8_t* mask, int dtype, sdpa::BwdProblem* p) {
   int st = check_sizes(rank, B, H, Lq, Lk, D, scale);
   if (st != SDPA_OK) return st;
-  if (dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (is_causal < SDPA_CAUSAL_NONE || is_causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t bh = B * H;
-  const int64_t tq = (Lq + sdpa::kBwdBlockQ - 1) / sdpa::kBwdBlockQ;
-  const int64_t tk = (Lk + sdpa::kBwdBlockK - 1) / sdpa::kBwdBlockK;
-  if (bh != 0 && (tq > kMaxDim / bh || tk > kMaxDim / bh ||
-                  !launch_fits(bh * tq, sdpa::kThreadsBwdQ) ||
-                  !launch_fits(bh * tk, sdpa::kThreadsBwdK)))
-    return SDPA_ERR_SHAPE;  // grid sizes
+  if (!bwd_grids_fit(dtype, D, bh, Lq, Lk)) return SDPA_ERR_SHAPE;
+  const int64_t esize = dtype == SDPA_F32 ? 4 : 2;
   const bool rows = bh * Lq != 0;  // the dq kernel runs (and reads q, out, dout, lse)
   const bool keys = bh * Lk != 0;  // the dkdv kernel runs (and reads k, v, writes dk, dv)
 
@@ -201,7 +211,7 @@ int normalise_bwd(const void* q, const void* k, const void* v, const void* out,
     if (!(key_side ? keys : rows)) continue;
     if (!aligned(bases[t], 16)) return SDPA_ERR_ALIGN;
     for (int a = 0; a < 3; ++a)
-      if ((s4[t][a] * 2) % 16 != 0) return SDPA_ERR_ALIGN;
+      if ((s4[t][a] * esize) % 16 != 0) return SDPA_ERR_ALIGN;
   }
   if ((lse && !aligned(lse, 4)) || (delta && !aligned(delta, 4))) return SDPA_ERR_ALIGN;
   // Streamed tiles are addressed with 32-bit byte offsets from the head's base: K and V
@@ -286,17 +296,13 @@ int normalise_bwd_varlen(const void* q, const void* k, const void* v, const void
   if (max_seqlen_q > total_q || max_seqlen_k > total_k) return SDPA_ERR_SHAPE;
   if (H != 0 && total_q > kMaxDim / H) return SDPA_ERR_SHAPE;  // lse / delta [H, total_q]
   if (!sdpa::bwd_head_dim_ok(D)) return SDPA_ERR_HEAD_DIM;
-  if (dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
+  if (dtype != SDPA_F32 && dtype != SDPA_BF16 && dtype != SDPA_F16) return SDPA_ERR_DTYPE;
   if (!strides) return SDPA_ERR_NULL;
   if (!isfinite(scale)) return SDPA_ERR_SCALE;
   if (causal < SDPA_CAUSAL_NONE || causal > SDPA_CAUSAL_BOTTOM_RIGHT) return SDPA_ERR_CAUSAL;
   const int64_t heads = nseq * H;
-  const int64_t tq = (max_seqlen_q + sdpa::kBwdBlockQ - 1) / sdpa::kBwdBlockQ;
-  const int64_t tk = (max_seqlen_k + sdpa::kBwdBlockK - 1) / sdpa::kBwdBlockK;
-  if (heads != 0 && (tq > kMaxDim / heads || tk > kMaxDim / heads ||
-                     !launch_fits(heads * tq, sdpa::kThreadsBwdQ) ||
-                     !launch_fits(heads * tk, sdpa::kThreadsBwdK)))
-    return SDPA_ERR_SHAPE;  // grid sizes
+  if (!bwd_grids_fit(dtype, D, heads, max_seqlen_q, max_seqlen_k)) return SDPA_ERR_SHAPE;
+  const int64_t esize = dtype == SDPA_F32 ? 4 : 2;
   // the dq kernel runs when some sequence may have query rows, the dkdv kernel when some
   // may have keys; each reads the other side's rows too
   const bool rows = heads != 0 && max_seqlen_q != 0;
@@ -323,7 +329,7 @@ int normalise_bwd_varlen(const void* q, const void* k, const void* v, const void
     if (!bases[t]) return SDPA_ERR_NULL;
     if (!aligned(bases[t], 16)) return SDPA_ERR_ALIGN;
     for (int a = 1; a < 3; ++a)
-      if ((s4[t][a] * 2) % 16 != 0) return SDPA_ERR_ALIGN;
+      if ((s4[t][a] * esize) % 16 != 0) return SDPA_ERR_ALIGN;
   }
   if (any && total_q != 0 && (!lse || !delta)) return SDPA_ERR_NULL;
   if ((lse && !aligned(lse, 4)) || (delta && !aligned(delta, 4)) ||

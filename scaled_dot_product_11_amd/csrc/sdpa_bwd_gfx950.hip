@@ -948,6 +948,203 @@ void bwd_dkdv(BwdArgs a) {
     rows_to_global<D, RP>(ot, lane, kw, Lk, dvb, a.sdv[2]);
 }
 
+// ---------------------------------------------------------------------------------------
+// Row-by-row backward for fp32 inputs and for D = 256 (any input type): the formulas of the
+// two kernels above, one wave per query row (dq and delta), then one wave per key row (dk
+// and dv), on the vector ALU with every value and sum in fp32 (P and dS are not rounded).
+// For a run of 64 keys (queries) lane l first forms the score and dP of key (query) l
+// from the row's values, broadcast to the lanes one head dim at a time; the lanes then
+// switch to head dims l, l + 64, ... and add the run's contributions to the row's
+// gradients in key (query) order.  Deterministic; no workgroup barrier, so a wave past
+// its item's rows leaves at once.
+// ---------------------------------------------------------------------------------------
+constexpr int kGenDims = 4;  // head dims per lane (D <= 256)
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Score of (i, j) in natural-log units with the additive mask, -inf where (i, j) is hidden
+// by the boolean mask; position rules are the caller's.
+template <int MK>
+__device__ inline float gen_score(const BwdArgs& a, const BwdItem& it, int i, int j, float qk) {
+  float x = qk * a.scale;
+  if (MK == 1 && a.mask[it.m + int64_t(i) * a.sm[2] + j] == 0) x = -INFINITY;
+  if (MK == 2) x += a.bias[it.m + int64_t(i) * a.sm[2] + j];
+  return x;
+}
+
+__device__ inline float gen_prob(float x, float lse) {
+  return x > -INFINITY && lse > -INFINITY ? expf(x - lse) : 0.f;
+}
+
+template <typename E, bool CAUSAL, int MK, int MODE>
+__global__ __launch_bounds__(kThreadsBwdGen) void bwd_rows_gen(BwdArgs a, int D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = blockIdx.x / a.q_items;
+  const int i = int(blockIdx.x - bh * a.q_items) * kBwdGenRows + int(threadIdx.x >> 6);
+  const BwdItem it = bwd_item<MODE>(a, bh);
+  if (i >= it.Lq) return;
+  const E* q = static_cast<const E*>(a.q) + it.q + int64_t(i) * a.sq[2];
+  const E* o = static_cast<const E*>(a.out) + it.o + int64_t(i) * a.so[2];
+  const E* dO = static_cast<const E*>(a.dout) + it.dO + int64_t(i) * a.sdo[2];
+  const E* kb = static_cast<const E*>(a.k) + it.k;
+  const E* vb = static_cast<const E*>(a.v) + it.v;
+  float qv[kGenDims], dov[kGenDims], dqv[kGenDims];
+  float part = 0.f;
+#pragma unroll
+  for (int c = 0; c < kGenDims; ++c) {
+    const int d = lane + 64 * c;
+    const bool ok = d < D;
+    qv[c] = ok ? float(q[d]) : 0.f;
+    dov[c] = ok ? float(dO[d]) : 0.f;
+    part += ok ? dov[c] * float(o[d]) : 0.f;
+    dqv[c] = 0.f;
+  }
+  const float delta = wave_sum(part);
+  const float lse = a.lse[it.lse + i];
+  int kend = it.Lk;
+  if (CAUSAL) kend = max(0, min(kend, i + it.coff + 1));
+  for (int j0 = 0; j0 < kend; j0 += 64) {
+    const int j = j0 + lane;
+    const bool act = j < kend;
+    const E* kr = kb + int64_t(act ? j : j0) * a.sk[2];
+    const E* vr = vb + int64_t(act ? j : j0) * a.sv[2];
+    float qk = 0.f, dp = 0.f;
+#pragma unroll
+    for (int c = 0; c < kGenDims; ++c) {
+      if (64 * c >= D) break;
+      for (int e = 0; e < 64 && 64 * c + e < D; ++e) {
+        const int d = 64 * c + e;
+        qk += __shfl(qv[c], e) * float(kr[d]);
+        dp += __shfl(dov[c], e) * float(vr[d]);
+      }
+    }
+    const float p = act ? gen_prob(gen_score<MK>(a, it, i, j, qk), lse) : 0.f;
+    const float ds = p * (dp - delta);
+    const int n = min(64, kend - j0);
+    for (int e = 0; e < n; ++e) {
+      const float dse = __shfl(ds, e);
+      const E* kr2 = kb + int64_t(j0 + e) * a.sk[2];
+#pragma unroll
+      for (int c = 0; c < kGenDims; ++c) {
+        const int d = lane + 64 * c;
+        if (d < D) dqv[c] += dse * float(kr2[d]);
+      }
+    }
+  }
+  E* dq = static_cast<E*>(a.dq) + it.dq + int64_t(i) * a.sdq[2];
+#pragma unroll
+  for (int c = 0; c < kGenDims; ++c) {
+    const int d = lane + 64 * c;
+    if (d < D) dq[d] = static_cast<E>(dqv[c] * a.scale);
+  }
+  if (lane == 0) a.delta[it.lse + i] = delta;
+}
+
+template <typename E, bool CAUSAL, int MK, int MODE>
+__global__ __launch_bounds__(kThreadsBwdGen) void bwd_keys_gen(BwdArgs a, int D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = blockIdx.x / a.k_items;
+  const int j = int(blockIdx.x - bh * a.k_items) * kBwdGenRows + int(threadIdx.x >> 6);
+  const BwdItem it = bwd_item<MODE>(a, bh);
+  if (j >= it.Lk) return;
+  const E* kr = static_cast<const E*>(a.k) + it.k + int64_t(j) * a.sk[2];
+  const E* vr = static_cast<const E*>(a.v) + it.v + int64_t(j) * a.sv[2];
+  const E* qb = static_cast<const E*>(a.q) + it.q;
+  const E* db = static_cast<const E*>(a.dout) + it.dO;
+  float kv[kGenDims], vv[kGenDims], dkv[kGenDims], dvv[kGenDims];
+#pragma unroll
+  for (int c = 0; c < kGenDims; ++c) {
+    const int d = lane + 64 * c;
+    const bool ok = d < D;
+    kv[c] = ok ? float(kr[d]) : 0.f;
+    vv[c] = ok ? float(vr[d]) : 0.f;
+    dkv[c] = dvv[c] = 0.f;
+  }
+  // the queries that can see key j: i >= j - coff under a causal mask
+  const int istart = CAUSAL ? min(max(0, j - it.coff), it.Lq) : 0;
+  for (int i0 = istart; i0 < it.Lq; i0 += 64) {
+    const int i = i0 + lane;
+    const bool act = i < it.Lq;
+    const E* qr = qb + int64_t(act ? i : i0) * a.sq[2];
+    const E* dr = db + int64_t(act ? i : i0) * a.sdo[2];
+    float qk = 0.f, dp = 0.f;
+#pragma unroll
+    for (int c = 0; c < kGenDims; ++c) {
+      if (64 * c >= D) break;
+      for (int e = 0; e < 64 && 64 * c + e < D; ++e) {
+        const int d = 64 * c + e;
+        qk += __shfl(kv[c], e) * float(qr[d]);
+        dp += __shfl(vv[c], e) * float(dr[d]);
+      }
+    }
+    float p = 0.f, ds = 0.f;
+    if (act) {
+      p = gen_prob(gen_score<MK>(a, it, i, j, qk), a.lse[it.lse + i]);
+      ds = p * (dp - a.delta[it.lse + i]);
+    }
+    const int n = min(64, it.Lq - i0);
+    for (int e = 0; e < n; ++e) {
+      const float pe = __shfl(p, e), dse = __shfl(ds, e);
+      const E* q2 = qb + int64_t(i0 + e) * a.sq[2];
+      const E* d2 = db + int64_t(i0 + e) * a.sdo[2];
+#pragma unroll
+      for (int c = 0; c < kGenDims; ++c) {
+        const int d = lane + 64 * c;
+        if (d < D) {
+          dvv[c] += pe * float(d2[d]);
+          dkv[c] += dse * float(q2[d]);
+        }
+      }
+    }
+  }
+  E* dk = static_cast<E*>(a.dk) + it.dk + int64_t(j) * a.sdk[2];
+  E* dv = static_cast<E*>(a.dv) + it.dv + int64_t(j) * a.sdv[2];
+#pragma unroll
+  for (int c = 0; c < kGenDims; ++c) {
+    const int d = lane + 64 * c;
+    if (d < D) {
+      dk[d] = static_cast<E>(dkv[c] * a.scale);
+      dv[d] = static_cast<E>(dvv[c]);
+    }
+  }
+}
+
+template <typename E, bool CAUSAL, int MK, int MODE>
+hipError_t launch_gen_pair(const BwdArgs& a, int D, unsigned grid_q, unsigned grid_k,
+                           hipStream_t s) {
+  void* args[] = {const_cast<BwdArgs*>(&a), &D};
+  if (grid_q) {
+    const hipError_t e =
+        hipLaunchKernel(reinterpret_cast<const void*>(&bwd_rows_gen<E, CAUSAL, MK, MODE>),
+                        dim3(grid_q), dim3(kThreadsBwdGen), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  if (grid_k)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_keys_gen<E, CAUSAL, MK, MODE>),
+                           dim3(grid_k), dim3(kThreadsBwdGen), args, 0, s);
+  return hipSuccess;
+}
+
+template <typename E, bool CAUSAL>
+hipError_t launch_gen_c(const BwdArgs& a, bool varlen, int D, unsigned gq, unsigned gk,
+                        hipStream_t s) {
+  if (varlen) return launch_gen_pair<E, CAUSAL, 0, kBwdVarlen>(a, D, gq, gk, s);
+  if (a.mask) return launch_gen_pair<E, CAUSAL, 1, kBwdDense>(a, D, gq, gk, s);
+  if (a.bias) return launch_gen_pair<E, CAUSAL, 2, kBwdDense>(a, D, gq, gk, s);
+  return launch_gen_pair<E, CAUSAL, 0, kBwdDense>(a, D, gq, gk, s);
+}
+
+template <typename E>
+hipError_t launch_gen(const BwdArgs& a, bool causal, bool varlen, int D, unsigned gq,
+                      unsigned gk, hipStream_t s) {
+  return causal ? launch_gen_c<E, true>(a, varlen, D, gq, gk, s)
+                : launch_gen_c<E, false>(a, varlen, D, gq, gk, s);
+}
+
 template <typename E, int D, bool CAUSAL, int MK, int MODE>
 hipError_t launch_pair(const BwdArgs& a, unsigned grid_q, unsigned grid_k, hipStream_t s) {
   void* args[] = {const_cast<BwdArgs*>(&a)};
@@ -1015,8 +1212,11 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const int64_t qrows = p.varlen ? p.max_seqlen_q : p.Lq;
   const int64_t krows = p.varlen ? p.max_seqlen_k : p.Lk;
   a.bh_count = int32_t((p.varlen ? p.nseq : p.B) * p.H);
-  a.q_items = int32_t((qrows + kBwdBlockQ - 1) / kBwdBlockQ);
-  a.k_items = int32_t((krows + kBwdBlockK - 1) / kBwdBlockK);
+  const bool gen = bwd_generic(p.dtype, p.D);  // the row-by-row kernels
+  a.q_items = int32_t((qrows + (gen ? kBwdGenRows : kBwdBlockQ) - 1) /
+                      (gen ? kBwdGenRows : kBwdBlockQ));
+  a.k_items = int32_t((krows + (gen ? kBwdGenRows : kBwdBlockK) - 1) /
+                      (gen ? kBwdGenRows : kBwdBlockK));
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
   a.mask_vec8 = p.mask && (reinterpret_cast<uintptr_t>(p.mask) % 8 == 0) && p.sm[0] % 8 == 0 &&
@@ -1028,6 +1228,12 @@ hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream) {
   const unsigned gq = unsigned(int64_t(a.q_items) * a.bh_count);
   const unsigned gk = unsigned(int64_t(a.k_items) * a.bh_count);
   const bool causal = p.causal != 0;
+  if (gen) {
+    const int D = int(p.D);
+    if (p.dtype == 0) return launch_gen<float>(a, causal, p.varlen != 0, D, gq, gk, stream);
+    if (p.dtype == 2) return launch_gen<_Float16>(a, causal, p.varlen != 0, D, gq, gk, stream);
+    return launch_gen<__bf16>(a, causal, p.varlen != 0, D, gq, gk, stream);
+  }
   if (p.dtype == 2)
     switch (p.D) {
       case 32: return launch_bwd_d<_Float16, 32>(a, causal, p.varlen != 0, gq, gk, stream);

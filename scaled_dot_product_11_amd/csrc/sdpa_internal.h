@@ -23,7 +23,9 @@ constexpr int kBlockNF32 = 64;
 constexpr bool fwd_head_dim_ok(int64_t D) {
   return D == 32 || D == 64 || D == 96 || D == 128 || D == 256;
 }
-constexpr bool bwd_head_dim_ok(int64_t D) { return D == 32 || D == 64 || D == 96 || D == 128; }
+constexpr bool bwd_head_dim_ok(int64_t D) {
+  return D == 32 || D == 64 || D == 96 || D == 128 || D == 256;
+}
 // Phase groups of the 16-bit kernel at head dim D (2: paired waves alternate phases).
 constexpr int groups_16(int D) { return D <= 128 ? 2 : 1; }
 // Waves per SIMD of a 16-bit workgroup of G groups: two (one per group, or one from each of
@@ -189,6 +191,11 @@ constexpr int kThreadsBwdK = 512;
 constexpr int kBwdBlockQ = 256;
 constexpr int kBwdBlockK = 128;
 constexpr int kBwdStep = 64;
+// fp32 inputs and D = 256 take the row-by-row backward kernels: one wave per query row,
+// then one per key row, kBwdGenRows rows per workgroup.
+constexpr int kBwdGenRows = 4;
+constexpr int kThreadsBwdGen = 64 * kBwdGenRows;
+constexpr bool bwd_generic(int dtype, int64_t D) { return dtype == 0 || D == 256; }
 // LDS per workgroup of the two backward kernels.  dQ: two stages, each holding the K tile
 // in row-read layout (pitch k_pitch_bf16) and in transposed-read layout (pitch
 // v_pitch_bf16), and the V tile in row-read layout.
@@ -224,7 +231,7 @@ struct BwdProblem {
   int64_t sq[4], sk[4], sv[4], so[4], sdo[4], sdq[4], sdk[4], sdv[4], sm[4];
   float scale;
   int causal;
-  int dtype;  // 1 bf16, 2 fp16
+  int dtype;  // 0 fp32, 1 bf16, 2 fp16
   int varlen;
 };
 

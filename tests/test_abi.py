@@ -340,11 +340,13 @@ def test_bwd_check_valid_and_rank3():
 
 
 def test_bwd_check_errors():
-    assert bcheck(**bargs(dtype=sd.SDPA_F32)) == DTYPE  # the backward is 16-bit only
+    assert bcheck(**bargs(dtype=sd.SDPA_F32)) == OK  # fp32: the row-by-row kernels
+    assert bcheck(**bargs(dtype=7)) == DTYPE
     assert bcheck(**bargs(dtype=sd.SDPA_F16)) == OK
     assert bcheck(**bargs(D=96)) == OK
     assert bcheck(**bargs(D=32)) == OK
-    assert bcheck(**bargs(D=256)) == HEAD  # the forward takes 256, the backward does not
+    assert bcheck(**bargs(D=256)) == OK    # D = 256: the row-by-row kernels
+    assert bcheck(**bargs(D=256, dtype=sd.SDPA_F32)) == OK
     assert bcheck(**bargs(D=80)) == HEAD
     assert bcheck(**bargs(rank=5)) == RANK
     assert bcheck(**bargs(Lq=-1)) == SHAPE
@@ -382,9 +384,9 @@ def test_bwd_check_empty_sides():
 def test_bwd_rejects_before_any_device_call():
     import ctypes
     lib = sd.load_library()
-    a = bargs(D=256)
+    a = bargs(D=80)
     arr = (ctypes.c_int64 * 36)(*a["strides"])
-    st = lib.sdpa_bwd(*a["ptrs"], 4, 2, 3, 100, 90, 256, arr, 0.125, 1, None, 1, None)
+    st = lib.sdpa_bwd(*a["ptrs"], 4, 2, 3, 100, 90, 80, arr, 0.125, 1, None, 1, None)
     assert st == HEAD
     st = lib.sdpa_bwd(*([None] * 10), 4, 0, 3, 100, 90, 64, arr, 0.125, 1, None, 1, None)
     assert st == OK  # B == 0: nothing to do
@@ -597,8 +599,9 @@ def test_bwd_bias_check():
     assert bb(bias_ptr=None) == OK                   # no bias: sdpa_bwd's problem
     assert bb(bias_ptr=A + 4) == OK                  # fp32 bias: 4-byte alignment suffices
     assert bb(bias_ptr=A + 2) == ALIGN
-    assert bb(D=256) == HEAD
-    assert bb(dtype=sd.SDPA_F32) == DTYPE
+    assert bb(D=80) == HEAD
+    assert bb(D=256) == OK and bb(dtype=sd.SDPA_F32) == OK
+    assert bb(dtype=7) == DTYPE
     assert bb(is_causal=3) == CAUSAL_ERR
     a = bargs(mask=True)
     a.pop("mask_ptr")
@@ -631,8 +634,9 @@ def test_bwd_varlen_check():
     assert bvcheck(**bvargs()) == OK
     assert bvcheck(**bvargs(dtype=sd.SDPA_F16, D=128)) == OK
     assert bvcheck(**bvargs(D=96)) == OK and bvcheck(**bvargs(D=32)) == OK
-    assert bvcheck(**bvargs(D=256)) == HEAD
-    assert bvcheck(**bvargs(dtype=sd.SDPA_F32)) == DTYPE
+    assert bvcheck(**bvargs(D=80)) == HEAD
+    assert bvcheck(**bvargs(D=256)) == OK and bvcheck(**bvargs(dtype=sd.SDPA_F32)) == OK
+    assert bvcheck(**bvargs(dtype=7)) == DTYPE
     assert bvcheck(**bvargs(causal=3)) == CAUSAL_ERR
     assert bvcheck(**bvargs(nseq=-1)) == SHAPE
     assert bvcheck(**bvargs(max_q=101)) == SHAPE     # longer than every query token
@@ -673,15 +677,28 @@ def test_bwd_varlen_check():
 def test_bwd_bias_and_varlen_reject_before_any_device_call():
     import ctypes
     lib = sd.load_library()
-    a = bargs(D=256)
+    a = bargs(D=80)
     arr = (ctypes.c_int64 * 36)(*a["strides"])
-    assert lib.sdpa_bwd_bias(*a["ptrs"], 4, 2, 3, 100, 90, 256, arr, 0.125, 1, None, 1,
+    assert lib.sdpa_bwd_bias(*a["ptrs"], 4, 2, 3, 100, 90, 80, arr, 0.125, 1, None, 1,
                              None) == HEAD
     assert lib.sdpa_bwd_bias(*([None] * 10), 4, 0, 3, 100, 90, 64, arr, 0.125, 1, None, 1,
                              None) == OK  # B == 0: nothing to do
-    v = bvargs(D=256)
+    v = bvargs(D=80)
     varr = (ctypes.c_int64 * 24)(*v["strides"])
-    assert lib.sdpa_bwd_varlen(*v["ptrs"], 3, 50, 40, 100, 90, 4, 256, varr, 0.125, 2, 1,
+    assert lib.sdpa_bwd_varlen(*v["ptrs"], 3, 50, 40, 100, 90, 4, 80, varr, 0.125, 2, 1,
                                None) == HEAD
     assert lib.sdpa_bwd_varlen(*([None] * 12), 0, 0, 0, 0, 0, 4, 64, varr, 0.125, 2, 1,
                                None) == OK  # no sequences: nothing to do
+
+
+def test_bwd_grid_limits_of_the_row_by_row_kernels():
+    """fp32 and D = 256 launch one 256-thread workgroup per 4 rows: 65536 heads of 4096 rows
+    need 2^34 work-items, beyond HIP's 2^32, while the tiled 16-bit kernels fit."""
+    big = dict(B=1, H=65536, Lq=4096, Lk=4096, D=128)
+    assert bcheck(**bargs(**big)) == OK
+    assert bcheck(**bargs(dtype=sd.SDPA_F32, **big)) == SHAPE
+    assert bcheck(**bargs(dtype=sd.SDPA_F32, **dict(big, H=8192))) == OK  # 2^31
+    # packed: 16384 sequences x 4 heads, at most 4096 rows each
+    packed = dict(nseq=16384, max_q=4096, max_k=4096, total_q=4096, total_k=4096, H=4, D=128)
+    assert bvcheck(**bvargs(dtype=sd.SDPA_F32, **packed)) == SHAPE
+    assert bvcheck(**bvargs(**packed)) == OK

@@ -159,11 +159,11 @@ def test_bwd_invalid_arguments_raise():
     q, k, v, _ = rand_inputs(17, 1, 1, 8, 8, 64)
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     out, lse = sdpa_fwd(qd, kd, vd)
-    with pytest.raises(SdpaError, match="SDPA_ERR_DTYPE"):  # fp32 has no backward
-        f = [t.float() for t in (qd, kd, vd, out)]
+    with pytest.raises(SdpaError, match="SDPA_ERR_DTYPE"):  # fp64 has no kernel
+        f = [t.double() for t in (qd, kd, vd, out)]
         sdpa_bwd(*f[:3], f[3], f[3], lse)
     with pytest.raises(SdpaError, match="SDPA_ERR_HEAD_DIM"):
-        z = torch.zeros(1, 1, 8, 256, dtype=torch.bfloat16, device=DEV)
+        z = torch.zeros(1, 1, 8, 80, dtype=torch.bfloat16, device=DEV)
         sdpa_bwd(z, z, z, z, z, lse)
 
 
