@@ -138,3 +138,18 @@ def test_varlen_backward_is_two_kernels(profiler_sees_kernels):
     names = kernels_of(lambda: sdpa_bwd_varlen(q, k, v, out, dout, lse, cq, ck, 260, 300, dq,
                                                dk, dv, delta, is_causal=2))
     assert len(names) == 2 and len(ours(names)) == 2, names
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 256)],
+                         ids=["f32-64", "bf16-256"])
+def test_row_by_row_backward_is_two_kernels(profiler_sees_kernels, dtype, D):
+    """fp32 inputs and D = 256: the row-by-row kernels, one for dq and delta, one for dk, dv."""
+    q, k, v = small(dtype=dtype, D=D)
+    out, lse = sdpa_fwd(q, k, v, is_causal=True)
+    dout = torch.randn_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+    names = kernels_of(lambda: sdpa_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta,
+                                        is_causal=True))
+    assert len(names) == 2 and len(ours(names)) == 2, names
+    assert all("_gen" in n for n in names), names
