@@ -953,12 +953,32 @@ void bwd_dkdv(BwdArgs a) {
 // two kernels above, one wave per query row (dq and delta), then one wave per key row (dk
 // and dv), on the vector ALU with every value and sum in fp32 (P and dS are not rounded).
 // For a run of 64 keys (queries) lane l first forms the score and dP of key (query) l
-// from the row's values, broadcast to the lanes one head dim at a time; the lanes then
+// from the row's values, which the wave keeps in its own slot of LDS and reads back as
+// broadcasts, four head dims at a time; the lanes then
 // switch to head dims l, l + 64, ... and add the run's contributions to the row's
 // gradients in key (query) order.  Deterministic; no workgroup barrier, so a wave past
 // its item's rows leaves at once.
 // ---------------------------------------------------------------------------------------
 constexpr int kGenDims = 4;  // head dims per lane (D <= 256)
+
+// Four consecutive elements as floats (16-byte aligned for fp32, 8-byte for 16-bit types).
+template <typename E>
+__device__ inline f32x4 load4f(const E* p) {
+  if constexpr (sizeof(E) == 4) {
+    return *reinterpret_cast<const f32x4*>(p);
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    const auto h = [](uint32_t b) { return float(__builtin_bit_cast(E, uint16_t(b))); };
+    return f32x4{h(w[0] & 0xFFFFu), h(w[0] >> 16), h(w[1] & 0xFFFFu), h(w[1] >> 16)};
+  }
+}
+
+// Publishes a wave's LDS writes to its own later reads (no other wave reads them).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ inline float wave_sum(float x) {
 #pragma unroll
@@ -1005,6 +1025,19 @@ __global__ __launch_bounds__(kThreadsBwdGen) void bwd_rows_gen(BwdArgs a, int D)
   }
   const float delta = wave_sum(part);
   const float lse = a.lse[it.lse + i];
+  // the row's q and dout values in this wave's LDS slot, read back as broadcasts
+  __shared__ __attribute__((aligned(16))) float rows_lds[kBwdGenRows][2][64 * kGenDims];
+  float* const qs = rows_lds[threadIdx.x >> 6][0];
+  float* const dos = rows_lds[threadIdx.x >> 6][1];
+#pragma unroll
+  for (int c = 0; c < kGenDims; ++c) {
+    const int d = lane + 64 * c;
+    if (d < D) {
+      qs[d] = qv[c];
+      dos[d] = dov[c];
+    }
+  }
+  wave_lds_sync();
   int kend = it.Lk;
   if (CAUSAL) kend = max(0, min(kend, i + it.coff + 1));
   for (int j0 = 0; j0 < kend; j0 += 64) {
@@ -1013,13 +1046,14 @@ __global__ __launch_bounds__(kThreadsBwdGen) void bwd_rows_gen(BwdArgs a, int D)
     const E* kr = kb + int64_t(act ? j : j0) * a.sk[2];
     const E* vr = vb + int64_t(act ? j : j0) * a.sv[2];
     float qk = 0.f, dp = 0.f;
+    for (int d = 0; d < D; d += 4) {
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(qs + d);
+      const f32x4 o4 = *reinterpret_cast<const f32x4*>(dos + d);
+      const f32x4 k4 = load4f(kr + d), v4 = load4f(vr + d);
 #pragma unroll
-    for (int c = 0; c < kGenDims; ++c) {
-      if (64 * c >= D) break;
-      for (int e = 0; e < 64 && 64 * c + e < D; ++e) {
-        const int d = 64 * c + e;
-        qk += __shfl(qv[c], e) * float(kr[d]);
-        dp += __shfl(dov[c], e) * float(vr[d]);
+      for (int e = 0; e < 4; ++e) {
+        qk += q4[e] * k4[e];
+        dp += o4[e] * v4[e];
       }
     }
     const float p = act ? gen_prob(gen_score<MK>(a, it, i, j, qk), lse) : 0.f;
@@ -1064,6 +1098,19 @@ __global__ __launch_bounds__(kThreadsBwdGen) void bwd_keys_gen(BwdArgs a, int D)
     vv[c] = ok ? float(vr[d]) : 0.f;
     dkv[c] = dvv[c] = 0.f;
   }
+  // the key row's k and v values in this wave's LDS slot, read back as broadcasts
+  __shared__ __attribute__((aligned(16))) float rows_lds[kBwdGenRows][2][64 * kGenDims];
+  float* const ks = rows_lds[threadIdx.x >> 6][0];
+  float* const vs = rows_lds[threadIdx.x >> 6][1];
+#pragma unroll
+  for (int c = 0; c < kGenDims; ++c) {
+    const int d = lane + 64 * c;
+    if (d < D) {
+      ks[d] = kv[c];
+      vs[d] = vv[c];
+    }
+  }
+  wave_lds_sync();
   // the queries that can see key j: i >= j - coff under a causal mask
   const int istart = CAUSAL ? min(max(0, j - it.coff), it.Lq) : 0;
   for (int i0 = istart; i0 < it.Lq; i0 += 64) {
@@ -1072,13 +1119,14 @@ __global__ __launch_bounds__(kThreadsBwdGen) void bwd_keys_gen(BwdArgs a, int D)
     const E* qr = qb + int64_t(act ? i : i0) * a.sq[2];
     const E* dr = db + int64_t(act ? i : i0) * a.sdo[2];
     float qk = 0.f, dp = 0.f;
+    for (int d = 0; d < D; d += 4) {
+      const f32x4 k4 = *reinterpret_cast<const f32x4*>(ks + d);
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(vs + d);
+      const f32x4 q4 = load4f(qr + d), o4 = load4f(dr + d);
 #pragma unroll
-    for (int c = 0; c < kGenDims; ++c) {
-      if (64 * c >= D) break;
-      for (int e = 0; e < 64 && 64 * c + e < D; ++e) {
-        const int d = 64 * c + e;
-        qk += __shfl(kv[c], e) * float(qr[d]);
-        dp += __shfl(vv[c], e) * float(dr[d]);
+      for (int e = 0; e < 4; ++e) {
+        qk += k4[e] * q4[e];
+        dp += v4[e] * o4[e];
       }
     }
     float p = 0.f, ds = 0.f;
