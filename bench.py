@@ -65,8 +65,8 @@ TRAFFIC_BYTES = 544232 * 1024
 TRAFFIC_KERNEL_SHA256 = "9a0c4c6655ddfdbb"
 KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_fwd_gfx950.hip")
 # The same for one backward call (dq and dk/dv kernels together).
-BWD_TRAFFIC_BYTES = 1663773 * 1024
-BWD_TRAFFIC_KERNEL_SHA256 = "33e8bab179c0b526"
+BWD_TRAFFIC_BYTES = 1670917 * 1024
+BWD_TRAFFIC_KERNEL_SHA256 = "93054143fcb440f2"
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "scaled_dot_product_11_amd", "csrc", "sdpa_bwd_gfx950.hip")
 
 
